@@ -1,0 +1,334 @@
+"""Seeded synthetic inputs for dual-flow decode.
+
+This module is shared by the CPU oracle's tests, the GPU parity tests and the
+benchmark. It holds none of the method's arithmetic: it only draws random
+numbers, encodes the draws as bf16 bit patterns, and lays them out in the
+key/value cache format the library reads. Everything is deterministic in the
+seed: every (sequence, kv head, tensor) chunk has its own generator derived
+from ``[seed, tag, b, g]``, so any chunk can be regenerated on its own.
+
+Cache layout (one layer), shared by every consumer:
+
+* ``k_cache``: ``[num_blocks, num_kv_heads, block_size, head_dim]`` -- one key
+  row of ``head_dim`` contiguous elements per cached position.
+* ``v_cache``: ``[num_blocks, num_kv_heads, head_dim, block_size]`` -- values
+  are stored transposed inside a block, positions contiguous per dimension.
+* ``block_table``: int32 ``[batch, max_blocks_per_seq]``; logical block ``j``
+  of sequence ``b`` lives in physical block ``block_table[b, j]``; unused
+  entries hold -1. A "contiguous" cache is the special case of one block per
+  sequence whose size is the capacity.
+
+bf16 tensors are held as ``uint16`` bit patterns; fp32 tensors as ``float32``.
+Unused cache slots are filled with NaN so that any read of them shows up.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from dataclasses import dataclass, field
+from typing import Dict, Optional, Sequence, Tuple
+
+import numpy as np
+
+BF16_NAN_BITS = np.uint16(0x7FC0)
+
+# Tags separating the random streams of different tensors.
+_TAG = {"q1": 1, "q2": 2, "a": 3, "k": 4, "v": 5, "peak": 6, "len": 7, "perm": 8,
+        "x1": 11, "x2": 12, "wq": 13, "wk": 14, "wv": 15, "wo": 16, "wg": 17,
+        "wu": 18, "wd": 19, "b": 20, "c": 21}
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (round to nearest, ties to even); return bits.
+
+    Used only to encode random draws; NaN/Inf are never drawn.
+    """
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    rounding = np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    return ((u + rounding) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns to float32 (exact)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _rng(seed: int, tag: str, *idx: int) -> np.random.Generator:
+    return np.random.default_rng([int(seed), _TAG[tag], *[int(i) for i in idx]])
+
+
+def _normal(seed: int, tag: str, idx: Tuple[int, ...], shape, std: float = 1.0) -> np.ndarray:
+    x = _rng(seed, tag, *idx).standard_normal(shape, dtype=np.float32)
+    if std != 1.0:
+        x *= np.float32(std)
+    return x
+
+
+def _encode(x: np.ndarray, dtype: str) -> np.ndarray:
+    return f32_to_bf16_bits(x) if dtype == "bf16" else x.astype(np.float32)
+
+
+# --------------------------------------------------------------------------
+# Attention workloads
+# --------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class AttnConfig:
+    """One decode-attention workload: shapes, element type, lengths, paging."""
+
+    name: str
+    batch: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    dtype: str  # element type of Q1, Q2, K and V: "f32" or "bf16"
+    ctx_lens: Optional[Tuple[int, ...]] = None  # explicit per-sequence lengths
+    ctx_range: Optional[Tuple[int, int]] = None  # inclusive uniform range when drawn
+    block_size: int = 0  # 0: contiguous cache (one block per sequence)
+    capacity: int = 0  # contiguous capacity; 0: next power of two >= max length
+    shuffle_blocks: bool = False
+    peaky_fraction: float = 0.0  # fraction of key rows per (b, kv head) scaled
+    peaky_factor: float = 1.0
+    q_std: float = 1.0
+    kv_std: float = 1.0
+    a_std: float = 0.1
+
+    @property
+    def group(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+    def replace(self, **kw) -> "AttnConfig":
+        return dataclasses.replace(self, **kw)
+
+
+# The five decode workloads. C1-C4 are attention-only; C5 is the full layer.
+C1 = AttnConfig("c1", batch=1, num_q_heads=8, num_kv_heads=8, head_dim=64, dtype="f32",
+                ctx_lens=(512,))
+C2 = AttnConfig("c2", batch=16, num_q_heads=32, num_kv_heads=8, head_dim=128, dtype="bf16",
+                ctx_lens=(4096,) * 16)
+C3 = AttnConfig("c3", batch=64, num_q_heads=64, num_kv_heads=8, head_dim=128, dtype="bf16",
+                ctx_range=(1024, 8192), block_size=16, shuffle_blocks=True)
+C4 = AttnConfig("c4", batch=4, num_q_heads=32, num_kv_heads=8, head_dim=128, dtype="bf16",
+                ctx_lens=(131072,) * 4, peaky_fraction=0.01, peaky_factor=8.0)
+ATTN_CONFIGS = {"c1": C1, "c2": C2, "c3": C3, "c4": C4}
+SEEDS = {"c1": 1001, "c2": 1002, "c3": 1003, "c4": 1004, "c5": 1005}
+
+
+def draw_ctx_lens(cfg: AttnConfig, seed: int) -> np.ndarray:
+    if cfg.ctx_lens is not None:
+        lens = np.asarray(cfg.ctx_lens, dtype=np.int32)
+        if lens.shape != (cfg.batch,):
+            raise ValueError("ctx_lens must have one entry per sequence")
+        return lens
+    lo, hi = cfg.ctx_range
+    return _rng(seed, "len").integers(lo, hi + 1, size=cfg.batch).astype(np.int32)
+
+
+@dataclass
+class CacheLayout:
+    block_size: int
+    num_blocks: int
+    max_blocks_per_seq: int
+    block_table: np.ndarray  # int32 [batch, max_blocks_per_seq], -1 padded
+
+
+def plan_cache(batch: int, ctx_lens: np.ndarray, block_size: int, capacity: int,
+               shuffle: bool, seed: int, extra_slots: int = 0) -> CacheLayout:
+    """Physical block assignment. ``extra_slots`` reserves room past each length."""
+    need = ctx_lens.astype(np.int64) + extra_slots
+    if block_size == 0:
+        cap = capacity or (1 << int(math.ceil(math.log2(max(int(need.max()), 1)))))
+        if need.max() > cap:
+            raise ValueError("capacity smaller than a sequence")
+        table = np.arange(batch, dtype=np.int32).reshape(batch, 1)
+        return CacheLayout(cap, batch, 1, table)
+    nblk = (need + block_size - 1) // block_size
+    total = int(nblk.sum())
+    phys = _rng(seed, "perm").permutation(total).astype(np.int32) if shuffle \
+        else np.arange(total, dtype=np.int32)
+    mb = int(nblk.max())
+    table = np.full((batch, mb), -1, dtype=np.int32)
+    pos = 0
+    for b in range(batch):
+        n = int(nblk[b])
+        table[b, :n] = phys[pos:pos + n]
+        pos += n
+    return CacheLayout(block_size, total, mb, table)
+
+
+def kv_rows(cfg_seed: int, b: int, g: int, length: int, head_dim: int, dtype: str,
+            kv_std: float = 1.0, peaky_fraction: float = 0.0, peaky_factor: float = 1.0):
+    """Logical key and value rows of one (sequence, kv head): two [length, head_dim] arrays.
+
+    Returned encoded (bf16 bits or float32)."""
+    k = _normal(cfg_seed, "k", (b, g), (length, head_dim), kv_std)
+    if peaky_fraction > 0.0:
+        n_peak = int(round(peaky_fraction * length))
+        rows = _rng(cfg_seed, "peak", b, g).choice(length, size=n_peak, replace=False)
+        k[rows] *= np.float32(peaky_factor)
+    v = _normal(cfg_seed, "v", (b, g), (length, head_dim), kv_std)
+    return _encode(k, dtype), _encode(v, dtype)
+
+
+def empty_cache(layout: CacheLayout, num_kv_heads: int, head_dim: int, dtype: str):
+    shape_k = (layout.num_blocks, num_kv_heads, layout.block_size, head_dim)
+    shape_v = (layout.num_blocks, num_kv_heads, head_dim, layout.block_size)
+    if dtype == "bf16":
+        return (np.full(shape_k, BF16_NAN_BITS, dtype=np.uint16),
+                np.full(shape_v, BF16_NAN_BITS, dtype=np.uint16))
+    return (np.full(shape_k, np.nan, dtype=np.float32), np.full(shape_v, np.nan, dtype=np.float32))
+
+
+def store_rows(k_cache, v_cache, layout: CacheLayout, b: int, g: int, k_rows, v_rows, start: int = 0):
+    """Write logical rows [start, start+n) of (b, g) into the paged cache."""
+    bs = layout.block_size
+    n = k_rows.shape[0]
+    t = start
+    while t < start + n:
+        j, off = divmod(t, bs)
+        take = min(bs - off, start + n - t)
+        blk = int(layout.block_table[b, j])
+        k_cache[blk, g, off:off + take, :] = k_rows[t - start:t - start + take]
+        v_cache[blk, g, :, off:off + take] = v_rows[t - start:t - start + take].T
+        t += take
+
+
+@dataclass
+class AttnCase:
+    cfg: AttnConfig
+    seed: int
+    q1: np.ndarray
+    q2: np.ndarray
+    a: np.ndarray
+    k_cache: np.ndarray
+    v_cache: np.ndarray
+    block_table: np.ndarray
+    ctx_lens: np.ndarray
+    block_size: int
+    max_blocks_per_seq: int
+    extra: Dict[str, np.ndarray] = field(default_factory=dict)
+
+    @property
+    def max_ctx_len(self) -> int:
+        return int(self.ctx_lens.max())
+
+
+def make_attn_case(cfg: AttnConfig, seed: int, pad_nan: bool = True) -> AttnCase:
+    """All inputs of one decode-attention call for workload ``cfg``."""
+    lens = draw_ctx_lens(cfg, seed)
+    layout = plan_cache(cfg.batch, lens, cfg.block_size, cfg.capacity, cfg.shuffle_blocks, seed)
+    q1 = _encode(_normal(seed, "q1", (), (cfg.batch, cfg.num_q_heads, cfg.head_dim), cfg.q_std), cfg.dtype)
+    q2 = _encode(_normal(seed, "q2", (), (cfg.batch, cfg.num_q_heads, cfg.head_dim), cfg.q_std), cfg.dtype)
+    a = _normal(seed, "a", (), (cfg.num_q_heads, cfg.head_dim), cfg.a_std)
+    k_cache, v_cache = empty_cache(layout, cfg.num_kv_heads, cfg.head_dim, cfg.dtype)
+    if not pad_nan:
+        k_cache[...] = 0
+        v_cache[...] = 0
+    for b in range(cfg.batch):
+        for g in range(cfg.num_kv_heads):
+            kr, vr = kv_rows(seed, b, g, int(lens[b]), cfg.head_dim, cfg.dtype, cfg.kv_std,
+                             cfg.peaky_fraction, cfg.peaky_factor)
+            store_rows(k_cache, v_cache, layout, b, g, kr, vr)
+    return AttnCase(cfg, seed, q1, q2, a, k_cache, v_cache, layout.block_table, lens,
+                    layout.block_size, layout.max_blocks_per_seq)
+
+
+# --------------------------------------------------------------------------
+# Full-layer workload
+# --------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class LayerConfig:
+    """One dual-flow decoder layer at one decode step."""
+
+    name: str
+    batch: int
+    hidden: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    mlp: int
+    ctx: int  # cached positions before this step's append
+    block_size: int = 0  # 0: contiguous
+    capacity: int = 0
+    shuffle_blocks: bool = False
+    w_std: float = 0.02
+    x_std: float = 1.0
+    kv_std: float = 1.0
+    coupling_std: float = 0.1
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+    def replace(self, **kw) -> "LayerConfig":
+        return dataclasses.replace(self, **kw)
+
+
+C5 = LayerConfig("c5", batch=32, hidden=4096, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                 mlp=14336, ctx=4096, capacity=8192)
+
+
+@dataclass
+class LayerCase:
+    cfg: LayerConfig
+    seed: int
+    x1: np.ndarray  # float32 [B, hidden], values exactly representable in bf16
+    x2: np.ndarray
+    w: Dict[str, np.ndarray]  # bf16 bits, [out, in] row-major
+    a: np.ndarray  # float32 [Hq * D]
+    b: np.ndarray  # float32 [mlp]
+    c: np.ndarray  # float32 [hidden]
+    k_cache: np.ndarray
+    v_cache: np.ndarray
+    block_table: np.ndarray
+    ctx_lens: np.ndarray  # positions cached before the append
+    block_size: int
+    max_blocks_per_seq: int
+
+
+def weight_shapes(cfg: LayerConfig) -> Dict[str, Tuple[int, int]]:
+    qd, kd = cfg.num_q_heads * cfg.head_dim, cfg.num_kv_heads * cfg.head_dim
+    return {"wq": (qd, cfg.hidden), "wk": (kd, cfg.hidden), "wv": (kd, cfg.hidden),
+            "wo": (cfg.hidden, qd), "wg": (cfg.mlp, cfg.hidden), "wu": (cfg.mlp, cfg.hidden),
+            "wd": (cfg.hidden, cfg.mlp)}
+
+
+def make_layer_case(cfg: LayerConfig, seed: int, pad_nan: bool = True) -> LayerCase:
+    """All inputs of one dual-flow layer step for workload ``cfg``."""
+    lens = np.full(cfg.batch, cfg.ctx, dtype=np.int32)
+    layout = plan_cache(cfg.batch, lens, cfg.block_size, cfg.capacity, cfg.shuffle_blocks, seed,
+                        extra_slots=1)
+    x1 = bf16_bits_to_f32(f32_to_bf16_bits(_normal(seed, "x1", (), (cfg.batch, cfg.hidden), cfg.x_std)))
+    x2 = bf16_bits_to_f32(f32_to_bf16_bits(_normal(seed, "x2", (), (cfg.batch, cfg.hidden), cfg.x_std)))
+    w = {name: f32_to_bf16_bits(_normal(seed, name, (), shape, cfg.w_std))
+         for name, shape in weight_shapes(cfg).items()}
+    a = _normal(seed, "a", (), (cfg.num_q_heads * cfg.head_dim,), cfg.coupling_std)
+    bvec = _normal(seed, "b", (), (cfg.mlp,), cfg.coupling_std)
+    cvec = _normal(seed, "c", (), (cfg.hidden,), cfg.coupling_std)
+    k_cache, v_cache = empty_cache(layout, cfg.num_kv_heads, cfg.head_dim, "bf16")
+    if not pad_nan:
+        k_cache[...] = 0
+        v_cache[...] = 0
+    for bi in range(cfg.batch):
+        for g in range(cfg.num_kv_heads):
+            kr, vr = kv_rows(seed, bi, g, cfg.ctx, cfg.head_dim, "bf16", cfg.kv_std)
+            store_rows(k_cache, v_cache, layout, bi, g, kr, vr)
+    return LayerCase(cfg, seed, x1, x2, w, a, bvec, cvec, k_cache, v_cache, layout.block_table,
+                     lens, layout.block_size, layout.max_blocks_per_seq)
+
+
+def permute_blocks(k_cache, v_cache, block_table, seed: int):
+    """Same logical cache under a different physical block order (a layout-only change)."""
+    nb = k_cache.shape[0]
+    perm = np.random.default_rng([int(seed), 99]).permutation(nb)  # new position of old block i
+    k2 = np.empty_like(k_cache)
+    v2 = np.empty_like(v_cache)
+    k2[perm] = k_cache
+    v2[perm] = v_cache
+    t2 = np.where(block_table >= 0, perm[np.maximum(block_table, 0)], -1).astype(np.int32)
+    return k2, v2, t2

@@ -1,0 +1,249 @@
+#!/usr/bin/env python3
+"""Dual-flow decode-attention benchmark on one MI355X.
+
+One step = one dual-flow decode-attention call of the whole batch: the split
+kernel (both flows' scores, online softmax and weighted values from one read
+of every cached key and value; query coupling in its prologue) and the
+log-sum-exp combine -- the two launches dfa_decode_attn makes, issued here as
+dfa_decode_attn_partials + dfa_combine so that HIP events can bracket the split
+kernel alone. Inputs are resident in HBM before timing; four copies of the
+cache are rotated between steps so that no step finds the cache in the 256 MB
+last-level cache.
+
+Prints one JSON line. `value` is tokens per second counting both flows (two
+per sequence per step). Also reported: achieved HBM bandwidth of the step and
+of the split kernel against the 8 TB/s peak, the measured stream-read ceiling,
+the auxiliary flow's increment over a one-flow run of the same kernel, and the
+CPU oracle's rate on a bounded sample (context only).
+
+    python bench.py [--steps K] [--warmup W] [--config c2|c3|c4]
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "dual-flow decode attn: tokens/s (both flows) + achieved HBM GB/s vs peak"
+HBM_PEAK_GBPS = 8000.0
+KERNEL_SOURCES = ["dual_flow_shared_decode_amd/csrc/attn_bf16.hip", "dual_flow_shared_decode_amd/csrc/attn_common.h"]
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "attn_bf16_c2_counters.txt")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(config_name: str):
+    """HBM bytes per split-kernel launch from the committed counter summary, or None
+    when there is none for this workload or the kernel source changed since."""
+    if config_name != "c2" or not os.path.exists(COUNTERS_FILE):
+        return None
+    vals = {}
+    with open(COUNTERS_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def algorithmic_bytes(case, num_flows):
+    """Bytes the method must move for one call: every cached key and value once, the
+    queries (and a), the outputs. Split kernel alone: the same without the outputs."""
+    cfg = case.cfg
+    esz = 2 if cfg.dtype == "bf16" else 4
+    qsz = 2 if cfg.qtype == "bf16" else 4
+    kv = int(case.ctx_lens.astype("int64").sum()) * cfg.num_kv_heads * cfg.head_dim * esz * 2
+    rows = cfg.batch * cfg.num_q_heads * cfg.head_dim
+    q = rows * qsz * num_flows + (cfg.num_q_heads * cfg.head_dim * 4 if num_flows == 2 else 0)
+    out = rows * 4 * num_flows
+    return kv + q + out, kv + q
+
+
+def cpu_baseline(case, budget_s: float):
+    """The float64 oracle, as it stands, on (sequence, kv head) pairs of the same
+    workload until the time budget is spent; rate scaled to tokens/s of both flows."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import attention as A
+    cfg = case.cfg
+    pairs = [(b, g) for b in range(cfg.batch) for g in range(cfg.num_kv_heads)]
+    t0 = time.perf_counter()
+    done = 0
+    for pair in pairs:
+        A.decode_attention(case.q1, case.q2, case.a, case.k_cache, case.v_cache, case.block_table,
+                           case.ctx_lens, num_kv_heads=cfg.num_kv_heads, scale=cfg.scale,
+                           block_size=case.block_size, num_flows=2, q_dtype=cfg.qtype, kv_dtype=cfg.dtype,
+                           pairs=[pair])
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    blas = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+    seqs = done / cfg.num_kv_heads
+    return {"value": 2.0 * seqs / dt, "unit": "tokens/s (both flows)", "cores": int(max(blas) if blas else 1),
+            "kind": "oracle",
+            "sample": f"{done} of {len(pairs)} (sequence, kv head) pairs of {cfg.name} "
+                      f"({int(case.ctx_lens.max())} positions each), both flows, float64 numpy, {dt:.1f} s",
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="c2", choices=["c2", "c3", "c4"])
+    ap.add_argument("--split", type=int, default=0, help="positions per split (0: library choice)")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="time the steps only (for profiler runs)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU (asked for --gpus {args.gpus}, WORLD_SIZE {world}); this "
+              "library runs on a single GPU and sharding across GPUs is not part of it", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import dual_flow_shared_decode_amd as dfa
+    import workloads as W
+    from workloads.device import upload_attn_case
+
+    torch.cuda.set_device(0)
+    cfg = W.ATTN_CONFIGS[args.config]
+    log(f"generating {cfg.name} inputs")
+    case = W.make_attn_case(cfg, W.SEEDS[cfg.name], pad_nan=False)
+    t = upload_attn_case(case)
+    kv_set_bytes = (case.k_cache.nbytes + case.v_cache.nbytes)
+    nsets = max(1, min(4, math.ceil((1 << 30) / kv_set_bytes)))
+    sets = [(t["k_cache"], t["v_cache"])] + [(t["k_cache"].clone(), t["v_cache"].clone()) for _ in range(nsets - 1)]
+    log(f"{nsets} cache copies of {kv_set_bytes / 2**20:.0f} MiB rotated between steps")
+
+    def make_desc(flows):
+        return dfa.AttnDesc(batch=cfg.batch, num_q_heads=cfg.num_q_heads, num_kv_heads=cfg.num_kv_heads,
+                            head_dim=cfg.head_dim, block_size=case.block_size,
+                            max_blocks_per_seq=case.max_blocks_per_seq, num_blocks=case.k_cache.shape[0],
+                            max_ctx_len=case.max_ctx_len, num_flows=flows, split_len=args.split,
+                            scale=cfg.scale, q_dtype=dfa.DFA_BF16, kv_dtype=dfa.DFA_BF16)
+
+    stream = torch.cuda.current_stream()
+    o1 = torch.empty((cfg.batch, cfg.num_q_heads, cfg.head_dim), dtype=torch.float32, device="cuda")
+    o2 = torch.empty_like(o1)
+
+    def runner(flows):
+        d = make_desc(flows)
+        ws = torch.empty(max(dfa.dfa_decode_attn_workspace_size(d) // 4, 4), dtype=torch.float32, device="cuda")
+        q2 = t["q2"] if flows == 2 else None
+        a = t["a"] if flows == 2 else None
+        out2 = o2 if flows == 2 else None
+
+        def step(i, ev=None):
+            k, v = sets[i % nsets]
+            if ev is not None:
+                ev[0].record(stream)
+            dfa.dfa_decode_attn_partials(d, t["q1"], q2, a, k, v, t["block_table"], t["ctx_lens"], ws, stream)
+            if ev is not None:
+                ev[1].record(stream)
+            dfa.dfa_combine(d, t["ctx_lens"], ws, o1, out2, stream)
+        return d, step
+
+    def timed(step, steps, warmup):
+        for i in range(warmup):
+            step(i)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        start.record(stream)
+        for i in range(steps):
+            step(warmup + i, evs[i])
+        end.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        ms = start.elapsed_time(end) / steps
+        kern = [a.elapsed_time(b) for a, b in evs]
+        return ms, float(np.mean(kern)), float(np.median(kern)), wall
+
+    d2, step2 = runner(2)
+    log(f"split length {dfa.dfa_decode_attn_split_len(d2)}, {dfa.dfa_decode_attn_num_splits(d2)} splits; timing")
+    ms, kern_ms, kern_med, wall = timed(step2, args.steps, args.warmup)
+    step_bytes, kern_bytes = algorithmic_bytes(case, 2)
+    step_gbps = step_bytes / (ms * 1e-3) / 1e9
+    kern_gbps = kern_bytes / (kern_ms * 1e-3) / 1e9
+    flow_tokens = 2 * cfg.batch / (ms * 1e-3)
+    log(f"{ms * 1e3:.1f} us/step ({wall:.3f} s wall for {args.steps} steps); split kernel {kern_ms * 1e3:.1f} us "
+        f"(median {kern_med * 1e3:.1f}); {step_gbps:.0f} GB/s step, {kern_gbps:.0f} GB/s split kernel")
+
+    rec = {"metric": METRIC, "value": flow_tokens, "unit": "tokens/s (both flows)", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": f"{cfg.name}: dual-flow decode attention, batch {cfg.batch}, "
+                                  f"{cfg.num_q_heads} query / {cfg.num_kv_heads} kv heads, head_dim {cfg.head_dim}, "
+                                  f"context {int(case.ctx_lens.min())}-{int(case.ctx_lens.max())}, bf16 cache, "
+                                  f"{'paged ' + str(case.block_size) if cfg.block_size else 'contiguous'}",
+                      "batch": cfg.batch, "num_q_heads": cfg.num_q_heads, "num_kv_heads": cfg.num_kv_heads,
+                      "head_dim": cfg.head_dim, "ctx_total": int(case.ctx_lens.sum()), "num_flows": 2,
+                      "split_len": dfa.dfa_decode_attn_split_len(d2),
+                      "num_splits": dfa.dfa_decode_attn_num_splits(d2), "cache_copies": nsets},
+           "accumulate": "f32",
+           "seq_tokens_per_s": cfg.batch / (ms * 1e-3),
+           "achieved_gbps": step_gbps, "hbm_peak_gbps": HBM_PEAK_GBPS, "frac_of_peak": step_gbps / HBM_PEAK_GBPS,
+           "algorithmic_bytes_per_step": step_bytes,
+           "roofline": {"bound": "hbm", "kernel": "attn_bf16_kernel (split stage)", "achieved": kern_gbps,
+                        "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": kern_gbps / HBM_PEAK_GBPS,
+                        "traffic": measured_traffic(cfg.name), "algorithmic_bytes_per_launch": kern_bytes,
+                        "avg_launch_us": kern_ms * 1e3}}
+
+    if not args.no_extras:
+        d1, step1 = runner(1)
+        ms1, kern1, _, _ = timed(step1, args.steps, args.warmup)
+        rec["ms_per_step_one_flow"] = ms1
+        rec["aux_increment"] = ms / ms1 - 1.0
+        rec["aux_increment_split_kernel"] = kern_ms / kern1 - 1.0
+        log(f"one flow: {ms1 * 1e3:.1f} us/step, split kernel {kern1 * 1e3:.1f} us -> aux increment "
+            f"{100 * rec['aux_increment']:.1f}%")
+        buf = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
+        sink = torch.empty(dfa.dfa_stream_read_sink_bytes() // 4, dtype=torch.int32, device="cuda")
+        for _ in range(3):
+            dfa.dfa_stream_read(buf, sink, stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(10):
+            dfa.dfa_stream_read(buf, sink, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ceil_gbps = buf.numel() * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        rec["stream_read_gbps"] = ceil_gbps
+        rec["frac_of_stream_read"] = kern_gbps / ceil_gbps
+        del buf
+        log(f"stream-read ceiling {ceil_gbps:.0f} GB/s")
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        rec["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

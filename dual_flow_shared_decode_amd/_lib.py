@@ -1,0 +1,151 @@
+"""ctypes binding of libdfa (include/dfa.h): argument marshalling only.
+
+Each function takes torch tensors resident on the GPU (or None where the C
+entry point accepts NULL), passes their device addresses and the current HIP
+stream to the C function of the same name, and raises ``DfaError`` on a
+non-zero status. Every step of the computation runs in the library's kernels;
+there is no fallback: if libdfa.so is missing, loading fails loudly.
+"""
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libdfa.so")
+
+DFA_F32, DFA_BF16 = 0, 1
+STATUS = {0: "DFA_OK", 1: "DFA_ERR_NULL", 2: "DFA_ERR_SHAPE", 3: "DFA_ERR_DTYPE",
+          4: "DFA_ERR_WORKSPACE", 5: "DFA_ERR_UNSUPPORTED", 6: "DFA_ERR_ALIGNMENT", 7: "DFA_ERR_HIP"}
+
+# Every symbol include/dfa.h declares.
+EXPORTS = ["dfa_decode_attn_split_len", "dfa_decode_attn_num_splits", "dfa_decode_attn_workspace_size",
+           "dfa_decode_attn", "dfa_decode_attn_partials", "dfa_combine", "dfa_status_string",
+           "dfa_last_error", "dfa_version", "dfa_stream_read", "dfa_stream_read_sink_bytes"]
+
+
+class DfaError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+
+
+class AttnDesc(ctypes.Structure):
+    """Mirror of dfa_attn_desc."""
+
+    _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
+                ("num_blocks", ctypes.c_int32), ("max_ctx_len", ctypes.c_int32),
+                ("num_flows", ctypes.c_int32), ("split_len", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("q_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32)]
+
+
+_lib = None
+_P = ctypes.c_void_p
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (loaded once). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m dual_flow_shared_decode_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        D = ctypes.POINTER(AttnDesc)
+        sig = {
+            "dfa_decode_attn_split_len": (ctypes.c_int32, [D]),
+            "dfa_decode_attn_num_splits": (ctypes.c_int32, [D]),
+            "dfa_decode_attn_workspace_size": (ctypes.c_size_t, [D]),
+            "dfa_decode_attn": (ctypes.c_int, [D, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P, _P, _P]),
+            "dfa_decode_attn_partials": (ctypes.c_int, [D, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+            "dfa_combine": (ctypes.c_int, [D, _P, _P, ctypes.c_size_t, _P, _P, _P]),
+            "dfa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+            "dfa_last_error": (ctypes.c_char_p, []),
+            "dfa_version": (ctypes.c_int32, []),
+            "dfa_stream_read": (ctypes.c_int, [_P, ctypes.c_size_t, _P, _P]),
+            "dfa_stream_read_sink_bytes": (ctypes.c_size_t, []),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _ptr(t):
+    """Device address of a GPU tensor, or None (NULL)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("libdfa takes GPU tensors")
+    if not t.is_contiguous():
+        raise ValueError("libdfa takes contiguous tensors")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _check(status: int):
+    if status != 0:
+        raise DfaError(status, lib().dfa_last_error().decode())
+
+
+def dfa_decode_attn_split_len(desc: AttnDesc) -> int:
+    v = lib().dfa_decode_attn_split_len(ctypes.byref(desc))
+    if v <= 0:
+        raise DfaError(-v, lib().dfa_last_error().decode())
+    return v
+
+
+def dfa_decode_attn_num_splits(desc: AttnDesc) -> int:
+    v = lib().dfa_decode_attn_num_splits(ctypes.byref(desc))
+    if v <= 0:
+        raise DfaError(-v, lib().dfa_last_error().decode())
+    return v
+
+
+def dfa_decode_attn_workspace_size(desc: AttnDesc) -> int:
+    return int(lib().dfa_decode_attn_workspace_size(ctypes.byref(desc)))
+
+
+def dfa_decode_attn(desc, q1, q2, a, k_cache, v_cache, block_table, ctx_lens, workspace, o1, o2,
+                    stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().dfa_decode_attn(ctypes.byref(desc), _ptr(q1), _ptr(q2), _ptr(a), _ptr(k_cache),
+                                 _ptr(v_cache), _ptr(block_table), _ptr(ctx_lens), _ptr(workspace),
+                                 ws_bytes, _ptr(o1), _ptr(o2), _stream(stream)))
+
+
+def dfa_decode_attn_partials(desc, q1, q2, a, k_cache, v_cache, block_table, ctx_lens, workspace,
+                             stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().dfa_decode_attn_partials(ctypes.byref(desc), _ptr(q1), _ptr(q2), _ptr(a), _ptr(k_cache),
+                                          _ptr(v_cache), _ptr(block_table), _ptr(ctx_lens),
+                                          _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def dfa_combine(desc, ctx_lens, workspace, o1, o2, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().dfa_combine(ctypes.byref(desc), _ptr(ctx_lens), _ptr(workspace), ws_bytes, _ptr(o1),
+                             _ptr(o2), _stream(stream)))
+
+
+def dfa_stream_read(buf, sink, stream=None):
+    _check(lib().dfa_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream)))
+
+
+def dfa_stream_read_sink_bytes() -> int:
+    return int(lib().dfa_stream_read_sink_bytes())
+
+
+def dfa_status_string(status: int) -> str:
+    return lib().dfa_status_string(status).decode()
+
+
+def dfa_version() -> int:
+    return int(lib().dfa_version())

@@ -1,0 +1,292 @@
+// Split-K decode attention over a bf16 KV cache, both flows from one read of
+// every key and value (asymmetric shared-KV attention: "Resumo Técnico:
+// Dual-Flow Transformers", section "Mecanismos Chave"; the shared cache read
+// once for both flows: section "Custos de Inferência vs. Treinamento").
+//
+// Workgroup = (split s, kv head g, sequence b), 4 waves. The query rows of the
+// workgroup are the G query heads of kv head g times the flows: row r is flow
+// r / G, head g*G + r % G. Waves take 32-position chunks of the split in turn
+// and each keeps its own online-softmax state; a merge in LDS ends the
+// workgroup.
+//
+// Both products run on v_mfma_f32_16x16x32_bf16 (A: 16x32, B: 32x16, C: 16x16):
+//   scores  S^T[key][row] = K[key][:] . Q[row][:]     (A = keys, B = queries)
+//   output  O^T[dim][row] += V^T[dim][key] . P[row][key]^T (A = values, B = weights)
+// Lane l of a wave owns column n = l % 16 and k-group l / 16 of each operand;
+// result element (m = 4*(l/16) + i, n = l % 16) is in lane l, register i.
+//
+// Operands that are not exact bf16 (the scaled, coupled queries and the
+// softmax weights) are split as x = hi + lo with hi = bf16(x) and
+// lo = bf16(x - hi), so each product keeps about 16 significant bits. With at
+// most 8 query rows (PACKED) the hi parts fill columns 0-7 and the lo parts
+// columns 8-15 of one MFMA and a DPP row rotation by 8 adds the halves; with
+// 16 rows the lo parts take a second MFMA into the same accumulator.
+//
+// Keys come straight from global memory into MFMA operand registers: lane
+// (n, grp) reads 16 bytes of key row kappa(n) at dims 32*st + 8*grp, so one
+// load instruction covers 16 rows x 64 contiguous bytes. Within a 32-position
+// chunk the two score blocks map operand row n to positions
+// 8*(n/4) + n%4 (block 0) and that + 4 (block 1); their result registers then
+// hold, in lane group grp, exactly the 8 positions 8*grp .. 8*grp+7 whose
+// transposed values the same lanes load for the PV product (16 bytes: eight
+// consecutive positions of one dimension). Loads of chunk c+4 are issued before
+// the math of chunk c.
+#include <hip/hip_runtime.h>
+
+#include "attn_common.h"
+#include "dfa_internal.h"
+
+namespace dfa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float dpp_ror8(float x) {
+  // lane i of each 16-lane row receives lane (i + 8) % 16
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false));
+}
+
+__device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int D>
+struct Chunk {
+  bf16x8 k0[D / 32];  // key rows of score block 0, one 8-dim slice per k-step
+  bf16x8 k1[D / 32];  // score block 1
+  bf16x8 v[D / 16];   // eight consecutive positions of dim 16*db + n
+};
+
+template <int D>
+__device__ __forceinline__ void load_chunk(const AttnParams& p, const uint16_t* __restrict__ kc,
+                                           const uint16_t* __restrict__ vc, const int* tbl, int jb0,
+                                           int t0, int end, int n, int grp, Chunk<D>& ch) {
+  const int bs_mask = (1 << p.bs_log2) - 1;
+  const int kk = 8 * (n >> 2) + (n & 3);
+  const int ta = min(t0 + kk, end - 1);
+  const int tb = min(t0 + kk + 4, end - 1);
+  const int tv = min(t0 + 8 * grp, (end - 1) & ~7);
+  const uint16_t* ka = kc + (size_t)tbl[(ta >> p.bs_log2) - jb0] * p.blk_stride + (size_t)(ta & bs_mask) * D + 8 * grp;
+  const uint16_t* kb = kc + (size_t)tbl[(tb >> p.bs_log2) - jb0] * p.blk_stride + (size_t)(tb & bs_mask) * D + 8 * grp;
+  const uint16_t* va = vc + (size_t)tbl[(tv >> p.bs_log2) - jb0] * p.blk_stride + (tv & bs_mask) + ((size_t)n << p.bs_log2);
+#pragma unroll
+  for (int st = 0; st < D / 32; ++st) {
+    ch.k0[st] = *(const bf16x8*)(ka + 32 * st);
+    ch.k1[st] = *(const bf16x8*)(kb + 32 * st);
+  }
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db) ch.v[db] = *(const bf16x8*)(va + ((size_t)(16 * db) << p.bs_log2));
+}
+
+template <int D, int NRP>
+__global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnParams p) {
+  constexpr int KS = D / 32;
+  constexpr int DB = D / 16;
+  constexpr bool PACKED = (NRP == 8);
+  __shared__ int tbl[kMaxTableSlice];
+  __shared__ float sm[kWaves * NRP];
+  __shared__ float sl[kWaves * NRP];
+  __shared__ __attribute__((aligned(16))) float so[kWaves * NRP * D];
+
+  const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  SplitRange r;
+  if (!split_range<D>(p, b, g, s, r)) return;
+  const int jb0 = stage_table(p, b, r, tbl);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, grp = lane >> 4;
+  const int row = PACKED ? (n & 7) : n;
+  const int nr = p.flows * p.group;
+
+  // ---- query operands: scaled (and for flow 2 coupled) rows, split hi/lo ----
+  bf16x8 qa[KS], qb[KS];
+  {
+    float x[KS][8];
+    if (row < nr) {
+      const int f = row / p.group, h = g * p.group + (row - f * p.group);
+      const size_t qoff = ((size_t)b * p.hq + h) * D;
+#pragma unroll
+      for (int st = 0; st < KS; ++st) {
+        const int d0 = 32 * st + 8 * grp;
+        float v1[8], v2[8];
+        if (p.q_f32) {
+          const float4* q = (const float4*)((const float*)p.q1 + qoff + d0);
+          float4 u0 = q[0], u1 = q[1];
+          v1[0] = u0.x; v1[1] = u0.y; v1[2] = u0.z; v1[3] = u0.w;
+          v1[4] = u1.x; v1[5] = u1.y; v1[6] = u1.z; v1[7] = u1.w;
+        } else {
+          bf16x8 u = *(const bf16x8*)((const uint16_t*)p.q1 + qoff + d0);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v1[j] = (float)u[j];
+        }
+        if (f == 1) {
+          if (p.q_f32) {
+            const float4* q = (const float4*)((const float*)p.q2 + qoff + d0);
+            float4 u0 = q[0], u1 = q[1];
+            v2[0] = u0.x; v2[1] = u0.y; v2[2] = u0.z; v2[3] = u0.w;
+            v2[4] = u1.x; v2[5] = u1.y; v2[6] = u1.z; v2[7] = u1.w;
+          } else {
+            bf16x8 u = *(const bf16x8*)((const uint16_t*)p.q2 + qoff + d0);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v2[j] = (float)u[j];
+          }
+          const float4* av = (const float4*)(p.a + (size_t)h * D + d0);
+          float4 a0 = av[0], a1 = av[1];
+          const float aa[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+          for (int j = 0; j < 8; ++j) x[st][j] = fmaf(aa[j], v1[j], v2[j]) * p.qscale;
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) x[st][j] = v1[j] * p.qscale;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int st = 0; st < KS; ++st)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[st][j] = 0.f;
+    }
+#pragma unroll
+    for (int st = 0; st < KS; ++st) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const __bf16 hi = (__bf16)x[st][j];
+        const __bf16 lo = (__bf16)(x[st][j] - (float)hi);
+        if (PACKED) {
+          qa[st][j] = (n < 8) ? hi : lo;
+        } else {
+          qa[st][j] = hi;
+          qb[st][j] = lo;
+        }
+      }
+    }
+  }
+
+  // ---- stream the split's positions in 32-position chunks ----
+  const int bs = 1 << p.bs_log2;
+  const uint16_t* __restrict__ kc = (const uint16_t*)p.k + (size_t)g * bs * D;
+  const uint16_t* __restrict__ vc = (const uint16_t*)p.v + (size_t)g * D * bs;
+  const int nchunks = (r.end - r.start + 31) >> 5;
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 oacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  Chunk<D> nxt;
+  int c = wave;
+  if (c < nchunks) load_chunk<D>(p, kc, vc, tbl, jb0, r.start + 32 * c, r.end, n, grp, nxt);
+  for (; c < nchunks; c += kWaves) {
+    Chunk<D> cur = nxt;
+    if (c + kWaves < nchunks)
+      load_chunk<D>(p, kc, vc, tbl, jb0, r.start + 32 * (c + kWaves), r.end, n, grp, nxt);
+    const int t0 = r.start + 32 * c;
+
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < KS; ++st) {
+      s0 = mfma(cur.k0[st], qa[st], s0);
+      s1 = mfma(cur.k1[st], qa[st], s1);
+    }
+    if (!PACKED) {
+#pragma unroll
+      for (int st = 0; st < KS; ++st) {
+        s0 = mfma(cur.k0[st], qb[st], s0);
+        s1 = mfma(cur.k1[st], qb[st], s1);
+      }
+    }
+    float sc[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sc[i] = s0[i];
+      sc[4 + i] = s1[i];
+    }
+    if (PACKED) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sc[j] += dpp_ror8(sc[j]);
+    }
+    if (t0 + 32 > r.end) {  // tail chunk: mask positions past the split, zero unused values
+      const int tv = min(t0 + 8 * grp, (r.end - 1) & ~7);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (t0 + 8 * grp + j >= r.end) sc[j] = -INFINITY;
+        if (tv + j >= r.end) {
+#pragma unroll
+          for (int db = 0; db < DB; ++db) cur.v[db][j] = (__bf16)0.f;
+        }
+      }
+    }
+    float cmax = sc[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) cmax = fmaxf(cmax, sc[j]);
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+    const float m_new = fmaxf(m_run, cmax);
+    const float alpha = fast_exp2(m_run - m_new);
+    float pv[8], psum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      pv[j] = fast_exp2(sc[j] - m_new);
+      psum += pv[j];
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+    bf16x8 pa, pb;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const __bf16 hi = (__bf16)pv[j];
+      const __bf16 lo = (__bf16)(pv[j] - (float)hi);
+      if (PACKED) {
+        pa[j] = (n < 8) ? hi : lo;
+      } else {
+        pa[j] = hi;
+        pb[j] = lo;
+      }
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[db] = mfma(cur.v[db], pa, oacc[db]);
+    if (!PACKED) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] = mfma(cur.v[db], pb, oacc[db]);
+    }
+  }
+
+  // ---- wave state to LDS, then merge the waves ----
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  if (PACKED) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) oacc[db][i] += dpp_ror8(oacc[db][i]);
+  }
+  if ((!PACKED || n < 8) && row < nr) {
+    float* dst = so + (wave * NRP + row) * D + 4 * grp;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) *(f32x4*)(dst + 16 * db) = oacc[db];
+    if (grp == 0) {
+      sm[wave * NRP + row] = m_run;
+      sl[wave * NRP + row] = l_run;
+    }
+  }
+  __syncthreads();
+  merge_waves<D, NRP>(p, b, g, s, sm, sl, so);
+}
+
+hipError_t launch_attn_bf16(const AttnParams& p, int head_dim, int rows_padded, hipStream_t stream) {
+  const dim3 grid(p.n_splits, p.hkv, p.batch), block(kThreads);
+  if (head_dim == 128 && rows_padded == 8)
+    hipLaunchKernelGGL((attn_bf16_kernel<128, 8>), grid, block, 0, stream, p);
+  else if (head_dim == 128 && rows_padded == 16)
+    hipLaunchKernelGGL((attn_bf16_kernel<128, 16>), grid, block, 0, stream, p);
+  else if (head_dim == 64 && rows_padded == 8)
+    hipLaunchKernelGGL((attn_bf16_kernel<64, 8>), grid, block, 0, stream, p);
+  else if (head_dim == 64 && rows_padded == 16)
+    hipLaunchKernelGGL((attn_bf16_kernel<64, 16>), grid, block, 0, stream, p);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace dfa

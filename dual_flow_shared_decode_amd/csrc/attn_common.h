@@ -1,0 +1,107 @@
+// Device helpers shared by the attention kernels: split bounds, block-table
+// staging, wave reductions, and the cross-wave merge that ends every
+// workgroup (written as a normalised output or as a split record).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "dfa_internal.h"
+
+namespace dfa {
+
+// 2^x on the hardware exponential unit. Inputs below -126 give 0 or a value
+// far below the precision of any sum it joins; -inf gives exactly 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
+// Positions [start, end) handled by workgroup (split s, sequence b); returns
+// false when the workgroup has nothing to do. Writes zero outputs for an empty
+// sequence in direct mode (split 0 only).
+struct SplitRange {
+  int start, end, len;
+};
+
+template <int D>
+__device__ __forceinline__ bool split_range(const AttnParams& p, int b, int g, int s, SplitRange& r) {
+  int len = p.ctx[b];
+  len = len < 0 ? 0 : (len > p.max_ctx ? p.max_ctx : len);
+  r.len = len;
+  r.start = s * p.split_len;
+  r.end = min(r.start + p.split_len, len);
+  if (len == 0) {
+    if (p.direct && s == 0) {
+      const int nr = p.flows * p.group;
+      for (int idx = threadIdx.x; idx < nr * D; idx += kThreads) {
+        const int row = idx / D, d = idx - row * D;
+        const int f = row / p.group, h = g * p.group + (row - f * p.group);
+        float* out = f ? p.o2 : p.o1;
+        out[((size_t)b * p.hq + h) * D + d] = 0.f;
+      }
+    }
+    return false;
+  }
+  return r.start < len;
+}
+
+// Stages the physical block ids of the split's positions into LDS, clamped to
+// [0, num_blocks) so that no cache access can leave the cache tensors.
+__device__ __forceinline__ int stage_table(const AttnParams& p, int b, const SplitRange& r, int* tbl) {
+  const int jb0 = r.start >> p.bs_log2;
+  const int jb1 = (r.end - 1) >> p.bs_log2;
+  const int32_t* row = p.table + (size_t)b * p.max_blocks;
+  for (int j = threadIdx.x; j <= jb1 - jb0; j += kThreads) {
+    int blk = row[jb0 + j];
+    blk = blk < 0 ? 0 : (blk >= p.num_blocks ? p.num_blocks - 1 : blk);
+    tbl[j] = blk;
+  }
+  return jb0;
+}
+
+// Cross-wave merge. Each wave w left, for each of its rows, the running max
+// sm[w*NRP+row], sum sl[w*NRP+row] and unnormalised output so[(w*NRP+row)*D+d]
+// (all in base-2 units). Writes either the normalised output (direct) or the
+// split record (m, l, O) of each row.
+template <int D, int NRP>
+__device__ __forceinline__ void merge_waves(const AttnParams& p, int b, int g, int s,
+                                            const float* sm, const float* sl, const float* so) {
+  const int nr = p.flows * p.group;
+  for (int idx = threadIdx.x; idx < nr * D; idx += kThreads) {
+    const int row = idx / D, d = idx - row * D;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, sm[w * NRP + row]);
+    float o = 0.f, l = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float e = fast_exp2(sm[w * NRP + row] - mx);
+      o += e * so[(w * NRP + row) * D + d];
+      l += e * sl[w * NRP + row];
+    }
+    const int f = row / p.group, h = g * p.group + (row - f * p.group);
+    if (p.direct) {
+      float* out = f ? p.o2 : p.o1;
+      out[((size_t)b * p.hq + h) * D + d] = o / l;
+    } else {
+      float* rec = p.part + ((((size_t)b * p.hq + h) * p.flows + f) * p.n_splits + s) * (D + kRecPad);
+      rec[d] = o;
+      if (d == 0) {
+        rec[D] = mx;
+        rec[D + 1] = l;
+      }
+    }
+  }
+}
+
+}  // namespace dfa

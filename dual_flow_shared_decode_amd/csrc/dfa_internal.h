@@ -1,0 +1,51 @@
+// Internal interface between the host-side ABI (abi.cpp) and the kernel
+// launchers (*.hip). Plain structs passed by value to the kernels.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace dfa {
+
+constexpr int kWaves = 4;          // waves per attention workgroup
+constexpr int kThreads = 64 * kWaves;
+constexpr int kMaxRows = 16;       // query rows (heads x flows) served per workgroup
+constexpr int kRecPad = 4;         // partial record = head_dim + kRecPad floats
+constexpr int kMaxTableSlice = 1024;  // block-table entries staged per split
+
+struct AttnParams {
+  const void* q1;
+  const void* q2;
+  const float* a;
+  const void* k;
+  const void* v;
+  const int32_t* table;
+  const int32_t* ctx;
+  float* part;   // split records (split mode)
+  float* o1;     // outputs (direct mode)
+  float* o2;
+  int32_t batch, hq, hkv, group, flows;
+  int32_t bs_log2, max_blocks, num_blocks, max_ctx;
+  int32_t split_len, n_splits;
+  int64_t blk_stride;  // elements per physical block: hkv * block_size * head_dim
+  float qscale;        // scale * log2(e): scores come out in base-2 units
+  int32_t direct;      // 1: one split per sequence; normalise and write o1/o2
+  int32_t q_f32;       // Q element type is float32 (else bf16)
+};
+
+struct CombineParams {
+  const float* part;
+  const int32_t* ctx;
+  float* o1;
+  float* o2;
+  int32_t batch, hq, flows, split_len, n_splits, max_ctx;
+};
+
+// Launchers return the launch status (hipGetLastError after the launch).
+hipError_t launch_attn_bf16(const AttnParams& p, int head_dim, int rows_padded, hipStream_t s);
+hipError_t launch_attn_f32(const AttnParams& p, int head_dim, hipStream_t s);
+hipError_t launch_combine(const CombineParams& p, int head_dim, hipStream_t s);
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s);
+size_t stream_read_threads();
+
+}  // namespace dfa

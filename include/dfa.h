@@ -1,0 +1,184 @@
+/*
+ * dfa.h -- C ABI of libdfa: the decode step of a Dual-Flow Transformer on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * A Dual-Flow layer runs two residual flows over shared weights and one
+ * persistent key/value cache. The primary flow writes the cache; the
+ * auxiliary flow couples its query to the primary query through a learned
+ * vector a, attends the primary keys and values, and never writes the cache.
+ * Sources: "Resumo Técnico: Dual-Flow Transformers" (gist.science, pt),
+ * sections "Arquitetura Central" (flows, shared matrices, the cache is written
+ * by the primary flow only), "Mecanismos Chave" (asymmetric shared-KV
+ * attention; coupling vectors a, b, c at the query, MLP-intermediate and
+ * MLP-output levels, primary to auxiliary only) and "Custos de Inferência vs.
+ * Treinamento" (decode does about twice the arithmetic while reading the same
+ * cache and the same unique weights).
+ *
+ * The pages give the coupling vectors but not their formulas; this library
+ * computes q2' = q2 + a * q1, z2' = z2 + b * z1 and m2' = m2 + c * m1
+ * (elementwise; z = SwiGLU product, m = MLP output).
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers (hipMalloc'd or equivalent) and
+ *    must be 16-byte aligned. The caller owns every buffer; the library
+ *    allocates nothing, keeps no pointer after returning, and holds no global
+ *    state besides a per-thread error message, so calls are thread-safe.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Work is enqueued asynchronously; results are valid once the stream has
+ *    been synchronised. Calls on one stream execute in order.
+ *  - Arguments are validated on the host before anything is enqueued; an
+ *    invalid call returns a non-zero dfa_status and has no side effects.
+ *    Device-resident sizes (ctx_lens, block_table) cannot be validated on the
+ *    host: they are the caller's contract. The kernels clamp them so that no
+ *    access leaves the buffers the descriptor describes: a length is clamped
+ *    to [0, max_ctx_len], a block id to [0, num_blocks).
+ *  - No C++ exception crosses this interface.
+ *
+ * Layouts (row-major, innermost last):
+ *  - Q1, Q2, O1, O2:   [batch, num_q_heads, head_dim]
+ *  - a:                [num_q_heads * head_dim] float32
+ *  - K cache:          [num_blocks, num_kv_heads, block_size, head_dim]
+ *  - V cache:          [num_blocks, num_kv_heads, head_dim, block_size]
+ *                      (values transposed inside a block: positions contiguous)
+ *  - block_table:      int32 [batch, max_blocks_per_seq]; position t of
+ *                      sequence b is slot t % block_size of physical block
+ *                      block_table[b][t / block_size]. A contiguous cache is
+ *                      one block per sequence (block_size = capacity).
+ *  - ctx_lens:         int32 [batch], cached positions attended (>= 1)
+ *  - query head h reads kv head h / (num_q_heads / num_kv_heads).
+ */
+#ifndef DFA_H
+#define DFA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__) || defined(__clang__)
+#define DFA_API __attribute__((visibility("default")))
+#else
+#define DFA_API
+#endif
+
+typedef enum dfa_status {
+  DFA_OK = 0,
+  DFA_ERR_NULL = 1,        /* a required pointer is NULL */
+  DFA_ERR_SHAPE = 2,       /* a size is out of range or sizes are inconsistent */
+  DFA_ERR_DTYPE = 3,       /* unsupported element-type combination */
+  DFA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required */
+  DFA_ERR_UNSUPPORTED = 5, /* well-formed request with no kernel in this build */
+  DFA_ERR_ALIGNMENT = 6,   /* a device pointer is not 16-byte aligned */
+  DFA_ERR_HIP = 7          /* the HIP runtime reported an error */
+} dfa_status;
+
+typedef enum dfa_dtype { DFA_F32 = 0, DFA_BF16 = 1 } dfa_dtype;
+
+/* Shape and policy of one decode-attention call (one layer). */
+typedef struct dfa_attn_desc {
+  int32_t batch;              /* sequences, >= 1 */
+  int32_t num_q_heads;        /* Hq, multiple of num_kv_heads */
+  int32_t num_kv_heads;       /* Hkv >= 1 */
+  int32_t head_dim;           /* D: 64 or 128 */
+  int32_t block_size;         /* positions per cache block: power of two >= 16 */
+  int32_t max_blocks_per_seq; /* columns of block_table */
+  int32_t num_blocks;         /* physical blocks in each cache tensor */
+  int32_t max_ctx_len;        /* upper bound of ctx_lens; <= max_blocks_per_seq * block_size */
+  int32_t num_flows;          /* 1 = primary only, 2 = primary and auxiliary */
+  int32_t split_len;          /* positions per split (multiple of 32), 0 = library choice */
+  float scale;                /* softmax scale applied to q.k (1/sqrt(D) in a standard layer) */
+  dfa_dtype q_dtype;          /* element type of Q1 and Q2 */
+  dfa_dtype kv_dtype;         /* element type of the K and V caches */
+} dfa_attn_desc;
+
+/*
+ * Split plan. A sequence's positions are cut into splits of split_len
+ * positions, processed independently and merged by a log-sum-exp combine.
+ * Returns the split length the library will use for `desc` (> 0), or
+ * -(dfa_status) if `desc` is invalid.
+ */
+DFA_API int32_t dfa_decode_attn_split_len(const dfa_attn_desc* desc);
+
+/* Number of split slots per sequence: ceil(max_ctx_len / split_len); <= 0 on error. */
+DFA_API int32_t dfa_decode_attn_num_splits(const dfa_attn_desc* desc);
+
+/*
+ * Workspace bytes needed by dfa_decode_attn (when it runs more than one
+ * split) and by dfa_decode_attn_partials / dfa_combine: one partial record per
+ * (sequence, query head, flow, split). 0 if `desc` is invalid.
+ */
+DFA_API size_t dfa_decode_attn_workspace_size(const dfa_attn_desc* desc);
+
+/*
+ * Dual-flow decode attention (asymmetric shared-KV attention, "Mecanismos
+ * Chave"). For every sequence b, query head h and flow f:
+ *     q^1 = Q1[b,h],  q^2 = Q2[b,h] + a[h] * Q1[b,h]
+ *     O_f[b,h] = sum_t softmax_t(scale * <q^f, K_t>) V_t,  t in [0, ctx_lens[b])
+ * Both flows are served from one read of every cached key and value. The
+ * caches are read only (the auxiliary flow never writes KV).
+ *  q1, q2:   Q1, Q2 of type desc->q_dtype. q2 and a are ignored (may be NULL)
+ *            when num_flows == 1.
+ *  k_cache, v_cache: type desc->kv_dtype, layouts above. Never written.
+ *  workspace: device scratch of workspace_bytes; required (>= the size from
+ *            dfa_decode_attn_workspace_size) when more than one split runs,
+ *            else may be NULL. Contents on return are unspecified.
+ *  o1, o2:   float32 outputs; o2 ignored (may be NULL) when num_flows == 1.
+ */
+DFA_API dfa_status dfa_decode_attn(const dfa_attn_desc* desc, const void* q1, const void* q2,
+                           const float* a, const void* k_cache, const void* v_cache,
+                           const int32_t* block_table, const int32_t* ctx_lens,
+                           void* workspace, size_t workspace_bytes, float* o1, float* o2,
+                           void* stream);
+
+/*
+ * The split stage alone: writes one partial record per (b, h, f, split) to
+ * `workspace` and no output. Record (b, h, f, s) starts at float index
+ *     (((b * num_q_heads + h) * num_flows + f) * num_splits + s) * (head_dim + 4)
+ * and holds head_dim floats of unnormalised output sum_t 2^(u_t - m) V_t, then
+ * m = max_t u_t and l = sum_t 2^(u_t - m), with u_t = scale * log2(e) * <q, K_t>
+ * over the split's positions, then two unused floats. Splits past the end of
+ * a sequence are not written. With dfa_combine this is the same computation
+ * as dfa_decode_attn; the records also let a caller merge splits computed
+ * elsewhere (for example other devices holding other positions).
+ */
+DFA_API dfa_status dfa_decode_attn_partials(const dfa_attn_desc* desc, const void* q1, const void* q2,
+                                    const float* a, const void* k_cache, const void* v_cache,
+                                    const int32_t* block_table, const int32_t* ctx_lens,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Log-sum-exp combine of the partial records in `workspace` (layout above)
+ * into the normalised outputs: with M = max_s m_s over the
+ * ceil(ctx_lens[b] / split_len) splits of sequence b,
+ *     O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
+ * A sequence with ctx_lens[b] <= 0 gets zero outputs.
+ */
+DFA_API dfa_status dfa_combine(const dfa_attn_desc* desc, const int32_t* ctx_lens, const void* workspace,
+                       size_t workspace_bytes, float* o1, float* o2, void* stream);
+
+/* Short fixed description of a status code. Never NULL. */
+DFA_API const char* dfa_status_string(dfa_status status);
+
+/* Detail of the last failure reported on the calling thread ("" if none). */
+DFA_API const char* dfa_last_error(void);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+DFA_API int32_t dfa_version(void);
+
+/*
+ * Measurement helper (not part of the method): reads `bytes` bytes at `buf`
+ * with coalesced 16-byte loads on `stream`, the bandwidth ceiling that the
+ * streaming kernels are compared to. `sink` must hold 4 bytes per launched
+ * thread (dfa_stream_read_sink_bytes()); it is written only with a value that
+ * keeps the loads live. bytes must be a multiple of 16.
+ */
+DFA_API dfa_status dfa_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+DFA_API size_t dfa_stream_read_sink_bytes(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DFA_H */

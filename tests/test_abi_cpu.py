@@ -1,0 +1,132 @@
+"""The C ABI on the host: the library loads, exports what include/dfa.h declares,
+plans splits, and rejects invalid calls before enqueuing anything.
+
+None of these calls reaches a kernel launch: every call with device pointers
+here fails host-side validation (the pointers are never dereferenced).
+"""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import dual_flow_shared_decode_amd as dfa
+from dual_flow_shared_decode_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000  # an aligned, never-dereferenced stand-in for a device address
+
+
+def c2_desc(**kw):
+    d = dict(batch=16, num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=4096,
+             max_blocks_per_seq=1, num_blocks=16, max_ctx_len=4096, num_flows=2, split_len=0,
+             scale=1 / math.sqrt(128), q_dtype=dfa.DFA_BF16, kv_dtype=dfa.DFA_BF16)
+    d.update(kw)
+    return dfa.AttnDesc(**d)
+
+
+def test_header_declarations_are_exported():
+    with open(os.path.join(ROOT, "include", "dfa.h")) as f:
+        header = f.read()
+    declared = set(re.findall(r"DFA_API\s+[\w\s\*]+?\b(dfa_\w+)\s*\(", header))
+    assert declared == set(_lib.EXPORTS)
+    L = dfa.lib()
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_status_strings_and_version():
+    for code in range(8):
+        assert dfa.dfa_status_string(code)
+    assert dfa.dfa_version() >= 100
+
+
+def test_split_plan_and_workspace_size():
+    d = c2_desc()
+    split = dfa.dfa_decode_attn_split_len(d)
+    ns = dfa.dfa_decode_attn_num_splits(d)
+    assert split % 32 == 0 and ns == -(-4096 // split)
+    assert dfa.dfa_decode_attn_workspace_size(d) == 16 * 32 * 2 * ns * (128 + 4) * 4
+    d1 = c2_desc(split_len=4096)
+    assert dfa.dfa_decode_attn_num_splits(d1) == 1
+    assert dfa.dfa_decode_attn_split_len(c2_desc(split_len=96)) == 96
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(batch=0), "DFA_ERR_SHAPE"),
+    (dict(num_q_heads=30), "DFA_ERR_SHAPE"),
+    (dict(num_flows=3), "DFA_ERR_SHAPE"),
+    (dict(head_dim=96), "DFA_ERR_UNSUPPORTED"),
+    (dict(num_q_heads=72), "DFA_ERR_UNSUPPORTED"),  # 9 heads per kv head x 2 flows > 16 rows
+    (dict(block_size=48), "DFA_ERR_SHAPE"),
+    (dict(block_size=8, max_blocks_per_seq=512), "DFA_ERR_SHAPE"),
+    (dict(max_ctx_len=0), "DFA_ERR_SHAPE"),
+    (dict(max_ctx_len=4097), "DFA_ERR_SHAPE"),  # beyond max_blocks_per_seq * block_size
+    (dict(split_len=100), "DFA_ERR_SHAPE"),
+    (dict(scale=float("nan")), "DFA_ERR_SHAPE"),
+    (dict(q_dtype=dfa.DFA_BF16, kv_dtype=dfa.DFA_F32), "DFA_ERR_DTYPE"),
+    (dict(kv_dtype=7), "DFA_ERR_DTYPE"),
+    (dict(block_size=16, max_blocks_per_seq=256, split_len=16384 + 32), "DFA_ERR_UNSUPPORTED"),
+])
+def test_invalid_descriptors(change, status):
+    d = c2_desc(**change)
+    v = _lib.lib().dfa_decode_attn_split_len(ctypes.byref(d))
+    assert v < 0 and _lib.STATUS[-v] == status
+    assert dfa.dfa_decode_attn_workspace_size(d) == 0
+    with pytest.raises(dfa.DfaError) as e:
+        _call_attn(d)
+    assert _lib.STATUS[e.value.status] == status
+    assert _lib.lib().dfa_last_error().decode()
+
+
+def _call_attn(d, **ptrs):
+    p = dict(q1=FAKE, q2=FAKE, a=FAKE, k=FAKE, v=FAKE, table=FAKE, ctx=FAKE, ws=FAKE, ws_bytes=0,
+             o1=FAKE, o2=FAKE)
+    p.update(ptrs)
+    st = _lib.lib().dfa_decode_attn(ctypes.byref(d), p["q1"], p["q2"], p["a"], p["k"], p["v"], p["table"],
+                                    p["ctx"], p["ws"], p["ws_bytes"], p["o1"], p["o2"], None)
+    _lib._check(st)
+
+
+@pytest.mark.parametrize("missing", ["q1", "k", "v", "table", "ctx", "o1", "q2", "a", "o2"])
+def test_null_pointers(missing):
+    with pytest.raises(dfa.DfaError) as e:
+        _call_attn(c2_desc(), **{missing: None})
+    assert _lib.STATUS[e.value.status] == "DFA_ERR_NULL"
+
+
+def test_single_flow_accepts_null_aux_pointers_until_the_workspace_check():
+    with pytest.raises(dfa.DfaError) as e:
+        _call_attn(c2_desc(num_flows=1), q2=None, a=None, o2=None, ws=None)
+    assert _lib.STATUS[e.value.status] == "DFA_ERR_WORKSPACE"
+
+
+def test_workspace_and_alignment_errors():
+    d = c2_desc()
+    need = dfa.dfa_decode_attn_workspace_size(d)
+    with pytest.raises(dfa.DfaError) as e:
+        _call_attn(d, ws=None)
+    assert _lib.STATUS[e.value.status] == "DFA_ERR_WORKSPACE"
+    with pytest.raises(dfa.DfaError) as e:
+        _call_attn(d, ws_bytes=need - 4)
+    assert _lib.STATUS[e.value.status] == "DFA_ERR_WORKSPACE"
+    for name in ("q1", "k", "ws", "o1", "a"):
+        with pytest.raises(dfa.DfaError) as e:
+            _call_attn(d, ws_bytes=need - 4, **{name: FAKE + 4})
+        assert _lib.STATUS[e.value.status] == "DFA_ERR_ALIGNMENT", name
+    with pytest.raises(dfa.DfaError) as e:
+        _lib._check(_lib.lib().dfa_combine(ctypes.byref(d), FAKE, FAKE, need - 4, FAKE, FAKE, None))
+    assert _lib.STATUS[e.value.status] == "DFA_ERR_WORKSPACE"
+    with pytest.raises(dfa.DfaError) as e:
+        _lib._check(_lib.lib().dfa_decode_attn_partials(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                                        FAKE, None, 0, None))
+    assert _lib.STATUS[e.value.status] == "DFA_ERR_WORKSPACE"
+
+
+def test_stream_read_validation():
+    with pytest.raises(dfa.DfaError):
+        _lib._check(_lib.lib().dfa_stream_read(FAKE, 100, FAKE, None))
+    with pytest.raises(dfa.DfaError):
+        _lib._check(_lib.lib().dfa_stream_read(None, 1024, FAKE, None))
+    assert dfa.dfa_stream_read_sink_bytes() > 0

@@ -92,6 +92,11 @@ class AttnConfig:
     q_std: float = 1.0
     kv_std: float = 1.0
     a_std: float = 0.1
+    q_dtype: Optional[str] = None  # element type of Q1, Q2 when it differs from the cache's
+
+    @property
+    def qtype(self) -> str:
+        return self.q_dtype or self.dtype
 
     @property
     def group(self) -> int:
@@ -186,15 +191,13 @@ def empty_cache(layout: CacheLayout, num_kv_heads: int, head_dim: int, dtype: st
 def store_rows(k_cache, v_cache, layout: CacheLayout, b: int, g: int, k_rows, v_rows, start: int = 0):
     """Write logical rows [start, start+n) of (b, g) into the paged cache."""
     bs = layout.block_size
-    n = k_rows.shape[0]
-    t = start
-    while t < start + n:
-        j, off = divmod(t, bs)
-        take = min(bs - off, start + n - t)
-        blk = int(layout.block_table[b, j])
-        k_cache[blk, g, off:off + take, :] = k_rows[t - start:t - start + take]
-        v_cache[blk, g, :, off:off + take] = v_rows[t - start:t - start + take].T
-        t += take
+    pos = np.arange(start, start + k_rows.shape[0])
+    blk = layout.block_table[b, pos // bs].astype(np.int64)
+    if np.any(blk < 0):
+        raise ValueError("position outside the allocated blocks")
+    slot = pos % bs
+    k_cache[blk, g, slot, :] = k_rows
+    v_cache[blk, g, :, slot] = v_rows
 
 
 @dataclass
@@ -221,8 +224,8 @@ def make_attn_case(cfg: AttnConfig, seed: int, pad_nan: bool = True) -> AttnCase
     """All inputs of one decode-attention call for workload ``cfg``."""
     lens = draw_ctx_lens(cfg, seed)
     layout = plan_cache(cfg.batch, lens, cfg.block_size, cfg.capacity, cfg.shuffle_blocks, seed)
-    q1 = _encode(_normal(seed, "q1", (), (cfg.batch, cfg.num_q_heads, cfg.head_dim), cfg.q_std), cfg.dtype)
-    q2 = _encode(_normal(seed, "q2", (), (cfg.batch, cfg.num_q_heads, cfg.head_dim), cfg.q_std), cfg.dtype)
+    q1 = _encode(_normal(seed, "q1", (), (cfg.batch, cfg.num_q_heads, cfg.head_dim), cfg.q_std), cfg.qtype)
+    q2 = _encode(_normal(seed, "q2", (), (cfg.batch, cfg.num_q_heads, cfg.head_dim), cfg.q_std), cfg.qtype)
     a = _normal(seed, "a", (), (cfg.num_q_heads, cfg.head_dim), cfg.a_std)
     k_cache, v_cache = empty_cache(layout, cfg.num_kv_heads, cfg.head_dim, cfg.dtype)
     if not pad_nan:

@@ -56,7 +56,8 @@ __device__ __forceinline__ bool split_range(const AttnParams& p, int b, int g, i
 }
 
 // Stages the physical block ids of the split's positions into LDS, clamped to
-// [0, num_blocks) so that no cache access can leave the cache tensors.
+// [0, num_blocks) so that no cache access can leave the cache tensors. Ends
+// with a workgroup barrier: the entries are read by every wave.
 __device__ __forceinline__ int stage_table(const AttnParams& p, int b, const SplitRange& r, int* tbl) {
   const int jb0 = r.start >> p.bs_log2;
   const int jb1 = (r.end - 1) >> p.bs_log2;
@@ -66,6 +67,7 @@ __device__ __forceinline__ int stage_table(const AttnParams& p, int b, const Spl
     blk = blk < 0 ? 0 : (blk >= p.num_blocks ? p.num_blocks - 1 : blk);
     tbl[j] = blk;
   }
+  __syncthreads();  // every wave reads entries other waves wrote
   return jb0;
 }
 

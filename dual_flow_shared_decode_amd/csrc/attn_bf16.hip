@@ -9,11 +9,20 @@
 // and each keeps its own online-softmax state; a merge in LDS ends the
 // workgroup.
 //
-// Both products run on v_mfma_f32_16x16x32_bf16 (A: 16x32, B: 32x16, C: 16x16):
-//   scores  S^T[key][row] = K[key][:] . Q[row][:]     (A = keys, B = queries)
-//   output  O^T[dim][row] += V^T[dim][key] . P[row][key]^T (A = values, B = weights)
-// Lane l of a wave owns column n = l % 16 and k-group l / 16 of each operand;
-// result element (m = 4*(l/16) + i, n = l % 16) is in lane l, register i.
+// Cache layout (see include/dfa.h): keys [block][kv head][D/8][position][8],
+// values [block][kv head][position/16][D][16]. A chunk is 32 positions = two
+// 16-position tiles; every load of a tile reads whole 128-byte lines
+// (keys: 4 runs of 256 B, values: 512 B), so the cache is streamed with
+// non-temporal loads: each byte is read once and need not stay in L2.
+//
+// Per tile, on the matrix cores (lane l owns column n = l % 16 and k-group
+// grp = l / 16 of each operand; result (m = 4*grp + i, n) is lane l, register i):
+//   scores   S^T[pos][row] = K[pos][:] . Q[row][:]   v_mfma_f32_16x16x32_bf16,
+//            A = keys (lane: position n, dims 32*st + 8*grp ..+7), B = queries
+//   output   O^T[dim][row] += V^T[dim][pos] . P^T     v_mfma_f32_16x16x16_bf16,
+//            A = values (lane: dim 16*db + n, positions 4*grp ..+3), B = weights
+// The score result of a tile (lane: row n, positions 4*grp + i) is exactly the
+// weight operand the output product needs, so no data moves between lanes.
 //
 // Operands that are not exact bf16 (the scaled, coupled queries and the
 // softmax weights) are split as x = hi + lo with hi = bf16(x) and
@@ -21,16 +30,6 @@
 // most 8 query rows (PACKED) the hi parts fill columns 0-7 and the lo parts
 // columns 8-15 of one MFMA and a DPP row rotation by 8 adds the halves; with
 // 16 rows the lo parts take a second MFMA into the same accumulator.
-//
-// Keys come straight from global memory into MFMA operand registers: lane
-// (n, grp) reads 16 bytes of key row kappa(n) at dims 32*st + 8*grp, so one
-// load instruction covers 16 rows x 64 contiguous bytes. Within a 32-position
-// chunk the two score blocks map operand row n to positions
-// 8*(n/4) + n%4 (block 0) and that + 4 (block 1); their result registers then
-// hold, in lane group grp, exactly the 8 positions 8*grp .. 8*grp+7 whose
-// transposed values the same lanes load for the PV product (16 bytes: eight
-// consecutive positions of one dimension). Loads of chunk c+4 are issued before
-// the math of chunk c.
 #include <hip/hip_runtime.h>
 
 #include "attn_common.h"
@@ -39,6 +38,8 @@
 namespace dfa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float dpp_ror8(float x) {
@@ -50,32 +51,40 @@ __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f3
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+__device__ __forceinline__ f32x4 mfma16(const bf16x4& a, const bf16x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
 template <int D>
 struct Chunk {
-  bf16x8 k0[D / 32];  // key rows of score block 0, one 8-dim slice per k-step
-  bf16x8 k1[D / 32];  // score block 1
-  bf16x8 v[D / 16];   // eight consecutive positions of dim 16*db + n
+  bf16x8 k[2][D / 32];  // per tile: keys of position n, one 8-dim group per k-step
+  bf16x4 v[2][D / 16];  // per tile: four positions 4*grp.. of dim 16*db + n
 };
+
+// First position of tile u of the chunk at t0, moved back onto the last tile
+// that holds a position of the split when it lies past the end (its scores are
+// masked; reading it keeps every address inside an allocated block).
+__device__ __forceinline__ int tile_start(int t0, int u, int end) { return min(t0 + 16 * u, (end - 1) & ~15); }
 
 template <int D>
 __device__ __forceinline__ void load_chunk(const AttnParams& p, const uint16_t* __restrict__ kc,
                                            const uint16_t* __restrict__ vc, const int* tbl, int jb0,
                                            int t0, int end, int n, int grp, Chunk<D>& ch) {
   const int bs_mask = (1 << p.bs_log2) - 1;
-  const int kk = 8 * (n >> 2) + (n & 3);
-  const int ta = min(t0 + kk, end - 1);
-  const int tb = min(t0 + kk + 4, end - 1);
-  const int tv = min(t0 + 8 * grp, (end - 1) & ~7);
-  const uint16_t* ka = kc + (size_t)tbl[(ta >> p.bs_log2) - jb0] * p.blk_stride + (size_t)(ta & bs_mask) * D + 8 * grp;
-  const uint16_t* kb = kc + (size_t)tbl[(tb >> p.bs_log2) - jb0] * p.blk_stride + (size_t)(tb & bs_mask) * D + 8 * grp;
-  const uint16_t* va = vc + (size_t)tbl[(tv >> p.bs_log2) - jb0] * p.blk_stride + (tv & bs_mask) + ((size_t)n << p.bs_log2);
 #pragma unroll
-  for (int st = 0; st < D / 32; ++st) {
-    ch.k0[st] = *(const bf16x8*)(ka + 32 * st);
-    ch.k1[st] = *(const bf16x8*)(kb + 32 * st);
+  for (int u = 0; u < 2; ++u) {
+    const int tt = tile_start(t0, u, end);
+    const size_t blk = (size_t)tbl[(tt >> p.bs_log2) - jb0] * p.blk_stride;
+    const int pos = tt & bs_mask;
+    const uint16_t* ka = kc + blk + ((size_t)grp << (p.bs_log2 + 3)) + (pos + n) * 8;
+    const uint16_t* va = vc + blk + (size_t)(pos >> 4) * (D * 16) + n * 16 + 4 * grp;
+#pragma unroll
+    for (int st = 0; st < D / 32; ++st)
+      ch.k[u][st] = __builtin_nontemporal_load((const bf16x8*)(ka + ((size_t)(4 * st) << (p.bs_log2 + 3))));
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db)
+      ch.v[u][db] = __builtin_nontemporal_load((const bf16x4*)(va + 16 * 16 * db));
   }
-#pragma unroll
-  for (int db = 0; db < D / 16; ++db) ch.v[db] = *(const bf16x8*)(va + ((size_t)(16 * db) << p.bs_log2));
 }
 
 template <int D, int NRP>
@@ -180,39 +189,45 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnParams p) {
     if (c + kWaves < nchunks)
       load_chunk<D>(p, kc, vc, tbl, jb0, r.start + 32 * (c + kWaves), r.end, n, grp, nxt);
     const int t0 = r.start + 32 * c;
-
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    f32x4 sv[2];
 #pragma unroll
-    for (int st = 0; st < KS; ++st) {
-      s0 = mfma(cur.k0[st], qa[st], s0);
-      s1 = mfma(cur.k1[st], qa[st], s1);
-    }
-    if (!PACKED) {
+    for (int u = 0; u < 2; ++u) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int st = 0; st < KS; ++st) {
-        s0 = mfma(cur.k0[st], qb[st], s0);
-        s1 = mfma(cur.k1[st], qb[st], s1);
+      for (int st = 0; st < KS; ++st) acc = mfma(cur.k[u][st], qa[st], acc);
+      if (!PACKED) {
+#pragma unroll
+        for (int st = 0; st < KS; ++st) acc = mfma(cur.k[u][st], qb[st], acc);
       }
+      sv[u] = acc;
     }
-    float sc[8];
+    float sc[8];  // sc[4*u + i]: row n, position t0 + 16*u + 4*grp + i
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sc[i] = s0[i];
-      sc[4 + i] = s1[i];
-    }
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[4 * u + i] = sv[u][i];
     if (PACKED) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) sc[j] += dpp_ror8(sc[j]);
     }
-    if (t0 + 32 > r.end) {  // tail chunk: mask positions past the split, zero unused values
-      const int tv = min(t0 + 8 * grp, (r.end - 1) & ~7);
+    if (t0 + 32 > r.end) {  // tail chunk (wave-uniform): mask positions past the split, zero unused values
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (t0 + 8 * grp + j >= r.end) sc[j] = -INFINITY;
-        if (tv + j >= r.end) {
+      for (int u = 0; u < 2; ++u) {
+        const int tv = tile_start(t0, u, r.end) + 4 * grp;  // positions of this lane's values
+        uint32_t keep[2];
 #pragma unroll
-          for (int db = 0; db < DB; ++db) cur.v[db][j] = (__bf16)0.f;
+        for (int h = 0; h < 2; ++h)
+          keep[h] = (tv + 2 * h < r.end ? 0x0000FFFFu : 0u) | (tv + 2 * h + 1 < r.end ? 0xFFFF0000u : 0u);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          u32x2 w = __builtin_bit_cast(u32x2, cur.v[u][db]);
+          w[0] &= keep[0];
+          w[1] &= keep[1];
+          cur.v[u][db] = __builtin_bit_cast(bf16x4, w);
         }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          sc[4 * u + i] = (t0 + 16 * u + 4 * grp + i < r.end) ? sc[4 * u + i] : -INFINITY;
       }
     }
     float cmax = sc[0];
@@ -232,23 +247,27 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnParams p) {
     m_run = m_new;
 #pragma unroll
     for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-    bf16x8 pa, pb;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const __bf16 hi = (__bf16)pv[j];
-      const __bf16 lo = (__bf16)(pv[j] - (float)hi);
-      if (PACKED) {
-        pa[j] = (n < 8) ? hi : lo;
-      } else {
-        pa[j] = hi;
-        pb[j] = lo;
+    for (int u = 0; u < 2; ++u) {
+      bf16x4 pa, pb;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float x = pv[4 * u + i];
+        const __bf16 hi = (__bf16)x;
+        const __bf16 lo = (__bf16)(x - (float)hi);
+        if (PACKED) {
+          pa[i] = (n < 8) ? hi : lo;
+        } else {
+          pa[i] = hi;
+          pb[i] = lo;
+        }
       }
-    }
 #pragma unroll
-    for (int db = 0; db < DB; ++db) oacc[db] = mfma(cur.v[db], pa, oacc[db]);
-    if (!PACKED) {
+      for (int db = 0; db < DB; ++db) oacc[db] = mfma16(cur.v[u][db], pa, oacc[db]);
+      if (!PACKED) {
 #pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[db] = mfma(cur.v[db], pb, oacc[db]);
+        for (int db = 0; db < DB; ++db) oacc[db] = mfma16(cur.v[u][db], pb, oacc[db]);
+      }
     }
   }
 

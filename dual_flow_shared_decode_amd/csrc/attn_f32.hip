@@ -8,8 +8,9 @@
 // flow 2 coupled) query rows sit in LDS. Each wave takes 64-position chunks:
 // lane t scores position t0 + t against every row; the row max and sum are
 // wave reductions; for the weighted value sum, lane owns dims lane + 64*j and
-// reads the transposed values of each position while the weight of position t
-// is broadcast from lane t.
+// reads the values of each position while the weight of position t is
+// broadcast from lane t. Cache layout as in include/dfa.h (keys in 8-dim
+// groups, values transposed in 16-position tiles), here with float elements.
 #include <hip/hip_runtime.h>
 
 #include "attn_common.h"
@@ -59,12 +60,13 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnParams p) {
     const int t0 = r.start + 64 * c;
     const int t = t0 + lane;
     const int tc = min(t, r.end - 1);
-    const float4* kr = (const float4*)(kc + (size_t)tbl[(tc >> p.bs_log2) - jb0] * p.blk_stride + (size_t)(tc & bs_mask) * D);
+    // key of position tc: dims 8j..8j+7 are 8 contiguous floats in group j
+    const float* kr = kc + (size_t)tbl[(tc >> p.bs_log2) - jb0] * p.blk_stride + (size_t)(tc & bs_mask) * 8;
     float sc[kMaxRows];
 #pragma unroll
     for (int i = 0; i < kMaxRows; ++i) sc[i] = 0.f;
     for (int d4 = 0; d4 < D / 4; ++d4) {
-      const float4 kv = kr[d4];
+      const float4 kv = *(const float4*)(kr + ((size_t)(d4 >> 1) << (p.bs_log2 + 3)) + 4 * (d4 & 1));
 #pragma unroll
       for (int i = 0; i < kMaxRows; ++i) {
         if (i < nr) {
@@ -90,10 +92,11 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnParams p) {
     const int cnt = min(64, r.end - t0);
     for (int tt = 0; tt < cnt; ++tt) {
       const int key = t0 + tt;
-      const float* vr = vc + (size_t)tbl[(key >> p.bs_log2) - jb0] * p.blk_stride + (key & bs_mask);
+      const int pos = key & bs_mask;  // value of (dim d, pos) is at tile pos/16, row d, column pos%16
+      const float* vr = vc + (size_t)tbl[(key >> p.bs_log2) - jb0] * p.blk_stride + (size_t)(pos >> 4) * (D * 16) + (pos & 15);
       float v[DJ];
 #pragma unroll
-      for (int j = 0; j < DJ; ++j) v[j] = vr[(size_t)(lane + 64 * j) * bs];
+      for (int j = 0; j < DJ; ++j) v[j] = vr[(lane + 64 * j) * 16];
 #pragma unroll
       for (int i = 0; i < kMaxRows; ++i) {
         if (i < nr) {

@@ -37,9 +37,12 @@
  * Layouts (row-major, innermost last):
  *  - Q1, Q2, O1, O2:   [batch, num_q_heads, head_dim]
  *  - a:                [num_q_heads * head_dim] float32
- *  - K cache:          [num_blocks, num_kv_heads, block_size, head_dim]
- *  - V cache:          [num_blocks, num_kv_heads, head_dim, block_size]
- *                      (values transposed inside a block: positions contiguous)
+ *  - K cache:          [num_blocks, num_kv_heads, head_dim / 8, block_size, 8]
+ *                      (keys in groups of 8 dimensions; within a group the
+ *                      block's positions are contiguous, 8 elements each)
+ *  - V cache:          [num_blocks, num_kv_heads, block_size / 16, head_dim, 16]
+ *                      (values transposed inside tiles of 16 positions: for a
+ *                      tile and a dimension, the 16 positions are contiguous)
  *  - block_table:      int32 [batch, max_blocks_per_seq]; position t of
  *                      sequence b is slot t % block_size of physical block
  *                      block_table[b][t / block_size]. A contiguous cache is

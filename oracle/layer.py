@@ -61,8 +61,9 @@ def append_kv(k_cache, v_cache, block_table, ctx_lens, k_bits, v_bits, block_siz
         blk = int(block_table[b, pos // block_size])
         if blk < 0:
             raise ValueError("no cache block for the appended position")
-        k_new[blk, :, pos % block_size, :] = k_bits[b]
-        v_new[blk, :, :, pos % block_size] = v_bits[b]
+        slot = pos % block_size
+        k_new[blk, :, :, slot, :] = k_bits[b].reshape(k_bits.shape[1], -1, 8)
+        v_new[blk, :, slot // 16, :, slot % 16] = v_bits[b]
     return k_new, v_new
 
 

@@ -20,11 +20,11 @@ from oracle import brute as BR
 TINY = [
     # (config, seed): GQA paged + shuffled bf16 with ragged lengths; MHA contiguous f32
     (W.AttnConfig("tiny_gqa", batch=2, num_q_heads=4, num_kv_heads=2, head_dim=8, dtype="bf16",
-                  ctx_lens=(5, 33), block_size=4, shuffle_blocks=True), 11),
-    (W.AttnConfig("tiny_mha", batch=1, num_q_heads=2, num_kv_heads=2, head_dim=6, dtype="f32",
+                  ctx_lens=(5, 50), block_size=16, shuffle_blocks=True), 11),
+    (W.AttnConfig("tiny_mha", batch=1, num_q_heads=2, num_kv_heads=2, head_dim=16, dtype="f32",
                   ctx_lens=(9,)), 12),
-    (W.AttnConfig("tiny_g4", batch=2, num_q_heads=4, num_kv_heads=1, head_dim=4, dtype="bf16",
-                  ctx_lens=(1, 17), block_size=8, shuffle_blocks=True, peaky_fraction=0.2,
+    (W.AttnConfig("tiny_g4", batch=2, num_q_heads=4, num_kv_heads=1, head_dim=8, dtype="bf16",
+                  ctx_lens=(1, 35), block_size=16, shuffle_blocks=True, peaky_fraction=0.2,
                   peaky_factor=8.0), 13),
 ]
 
@@ -82,23 +82,24 @@ def pin_library_sdpa():
 
 
 def _single(keys, values, q, scale=1.0):
-    """Oracle on one sequence, one head, one flow, contiguous f32 cache."""
+    """Oracle on one sequence, one head, one flow, one f32 cache block."""
     keys = np.asarray(keys, dtype=np.float32)
     values = np.asarray(values, dtype=np.float32)
     n, d = keys.shape
-    k_cache = keys[None, None]  # [1, 1, n, d]
-    v_cache = values.T[None, None]  # [1, 1, d, n]
+    layout = W.plan_cache(1, np.array([n]), 0, 0, False, 0)
+    k_cache, v_cache = W.empty_cache(layout, 1, d, "f32")
+    W.store_rows(k_cache, v_cache, layout, 0, 0, keys, values)
     q = np.asarray(q, dtype=np.float32)[None, None]
     out = A.decode_attention(q, q, np.zeros((1, d), np.float32), k_cache, v_cache,
-                             np.zeros((1, 1), np.int32), np.array([n]), num_kv_heads=1, scale=scale,
-                             block_size=n, num_flows=2, q_dtype="f32", kv_dtype="f32",
+                             layout.block_table, np.array([n]), num_kv_heads=1, scale=scale,
+                             block_size=layout.block_size, num_flows=2, q_dtype="f32", kv_dtype="f32",
                              return_weights=True)
     return out["o1"][0, 0], out["w"][(0, 0, 1)]
 
 
 def pin_closed_forms():
     rng = np.random.default_rng(5)
-    d = 6
+    d = 8
     # one cached position: the output is that position's value
     v = rng.standard_normal((1, d)).astype(np.float32)
     o, _ = _single(rng.standard_normal((1, d)), v, rng.standard_normal(d))
@@ -156,13 +157,14 @@ def pin_block_order():
 
 def pin_key_shift():
     """Adding one vector to every key shifts all scores of a row equally: outputs unchanged."""
-    cfg = W.AttnConfig("shift", batch=1, num_q_heads=2, num_kv_heads=1, head_dim=8, dtype="f32",
+    cfg = W.AttnConfig("shift", batch=1, num_q_heads=2, num_kv_heads=1, head_dim=16, dtype="f32",
                        ctx_lens=(12,))
     case = W.make_attn_case(cfg, 4)
     case.k_cache = case.k_cache.astype(np.float64)  # the shift below is exact in float64
     case.v_cache = case.v_cache.astype(np.float64)
     ref = run_oracle(case, kv_dtype="f64")
-    case.k_cache = case.k_cache + 0.25 * np.arange(8, dtype=np.float64)
+    shift = 0.25 * np.arange(16, dtype=np.float64).reshape(2, 1, 8)  # dim 8*j+e lives at [.., j, :, e]
+    case.k_cache = case.k_cache + shift
     got = run_oracle(case, kv_dtype="f64")
     assert np.allclose(ref["o1"], got["o1"], rtol=0, atol=1e-12)
     assert np.allclose(ref["o2"], got["o2"], rtol=0, atol=1e-12)

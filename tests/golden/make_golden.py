@@ -18,9 +18,9 @@ from oracle import attention as A  # noqa: E402
 from oracle import layer as LY  # noqa: E402
 
 ATTN = W.AttnConfig("golden_attn", batch=2, num_q_heads=4, num_kv_heads=2, head_dim=8, dtype="bf16",
-                    ctx_lens=(3, 21), block_size=4, shuffle_blocks=True)
-LAYER = W.C5.replace(batch=1, hidden=8, num_q_heads=2, num_kv_heads=1, head_dim=4, mlp=12, ctx=3,
-                     capacity=4)
+                    ctx_lens=(3, 21), block_size=16, shuffle_blocks=True)
+LAYER = W.C5.replace(batch=1, hidden=8, num_q_heads=2, num_kv_heads=1, head_dim=8, mlp=12, ctx=3,
+                     capacity=16)
 SEED = 7
 
 
@@ -35,7 +35,7 @@ def build():
                              head_dim=LAYER.head_dim, scale=LAYER.scale, block_size=lc.block_size)
     return {
         "attention": {"config": ATTN.name, "seed": SEED, "o1": att["o1"].tolist(), "o2": att["o2"].tolist()},
-        "layer": {"config": "c5 at hidden 8, heads 2/1, head_dim 4, mlp 12, ctx 3", "seed": SEED,
+        "layer": {"config": "c5 at hidden 8, heads 2/1, head_dim 8, mlp 12, ctx 3", "seed": SEED,
                   "out1": lay["out1"].tolist(), "out2": lay["out2"].tolist(),
                   "k1_bits": lay["k1_bits"].astype(int).tolist(), "v1_bits": lay["v1_bits"].astype(int).tolist()},
     }

@@ -136,7 +136,7 @@ def test_one_position_returns_its_value():
     case = W.make_attn_case(cfg, 2011)
     say("case length-1 context")
     o1, o2 = run_attn(case)
-    v = W.bf16_bits_to_f32(case.v_cache[:, :, :, 0])  # [B, Hkv, D]
+    v = W.bf16_bits_to_f32(case.v_cache[:, :, 0, :, 0])  # position 0 of each sequence: [B, Hkv, D]
     expect = np.repeat(v, cfg.group, axis=1)
     assert np.array_equal(o1, expect) and np.array_equal(o2, expect)
 
@@ -144,7 +144,7 @@ def test_one_position_returns_its_value():
 def test_constant_values_return_that_value():
     case = W.make_attn_case(W.C2.replace(batch=2, ctx_lens=(777, 2048), capacity=2048), 2012)
     vconst = W.f32_to_bf16_bits(np.linspace(-2, 2, 128, dtype=np.float32))
-    case.v_cache[...] = vconst[None, None, :, None]
+    case.v_cache[...] = vconst[None, None, None, :, None]  # every position holds vconst
     say("case constant values")
     o1, o2 = run_attn(case, split_len=256)
     expect = W.bf16_bits_to_f32(vconst)[None, None, :]

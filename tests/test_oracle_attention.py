@@ -16,13 +16,13 @@ def test_oracle_rejects_bad_inputs():
     import workloads as W
     case = W.make_attn_case(cfg, seed)
     bad = case.block_table.copy()
-    bad[1, 3] = -1  # a block the context needs
+    bad[1, 2] = -1  # a block the context needs
     with pytest.raises(ValueError):
         A.decode_attention(case.q1, case.q2, case.a, case.k_cache, case.v_cache, bad, case.ctx_lens,
-                           num_kv_heads=2, scale=cfg.scale, block_size=4)
+                           num_kv_heads=2, scale=cfg.scale, block_size=16)
     with pytest.raises(ValueError):
         A.decode_attention(case.q1, case.q2, case.a, case.k_cache, case.v_cache, case.block_table,
-                           np.array([0, 3]), num_kv_heads=2, scale=cfg.scale, block_size=4)
+                           np.array([0, 3]), num_kv_heads=2, scale=cfg.scale, block_size=16)
 
 
 def test_pairs_subset_matches_full():
@@ -46,16 +46,17 @@ def _unnormalised(s):
 
 
 def _values_untransposed(v_cache, table_row, length, g, block_size, dtype):
-    """Reads the transposed value block as if it were [block, D]."""
+    """Reads each transposed value tile as if it were [16 positions, D]."""
     blocks = A.block_rows(table_row, length, block_size)
-    return A.to_f64(v_cache[blocks, g].reshape(-1, v_cache.shape[-2])[:length], dtype)
+    return A.to_f64(v_cache[blocks, g].reshape(-1, v_cache.shape[3])[:length], dtype)
+
+
+_GATHER_KEYS = A.gather_keys
 
 
 def _keys_rotated(k_cache, table_row, length, g, block_size, dtype):
     """Position t paired with the key of position t - 1."""
-    blocks = A.block_rows(table_row, length, block_size)
-    k = k_cache[blocks, g].reshape(-1, k_cache.shape[-1])[:length]
-    return A.to_f64(np.roll(k, 1, axis=0), dtype)
+    return np.roll(_GATHER_KEYS(k_cache, table_row, length, g, block_size, dtype), 1, axis=0)
 
 
 def _ignore_table(table_row, length, block_size):

@@ -7,8 +7,8 @@ import workloads as W
 from oracle import brute as BR
 from oracle import layer as LY
 
-TINY = W.C5.replace(batch=2, hidden=16, num_q_heads=4, num_kv_heads=2, head_dim=4, mlp=24, ctx=6,
-                    block_size=4, shuffle_blocks=True)
+TINY = W.C5.replace(batch=2, hidden=16, num_q_heads=2, num_kv_heads=1, head_dim=8, mlp=24, ctx=20,
+                    block_size=16, shuffle_blocks=True)
 
 
 def run(case, **over):
@@ -21,7 +21,7 @@ def run(case, **over):
                               head_dim=cfg.head_dim, scale=cfg.scale, block_size=case.block_size)
 
 
-@pytest.mark.parametrize("cfg", [TINY, TINY.replace(block_size=0, capacity=8, ctx=7, num_kv_heads=4)])
+@pytest.mark.parametrize("cfg", [TINY, TINY.replace(block_size=0, capacity=16, ctx=7, num_kv_heads=2)])
 def test_brute_force(cfg):
     case = W.make_layer_case(cfg, 21)
     got = run(case)
@@ -71,16 +71,16 @@ def test_append_writes_only_the_new_primary_slot():
     case = W.make_layer_case(TINY, 25)
     got = run(case)
     bs = case.block_size
-    changed_k = np.argwhere(np.any(got["k_cache"] != case.k_cache, axis=-1))
+    changed_k = np.argwhere(np.any(got["k_cache"] != case.k_cache, axis=(2, 4)))  # [blk, g, slot]
     expect = sorted((int(case.block_table[b, case.ctx_lens[b] // bs]), g, int(case.ctx_lens[b] % bs))
                     for b in range(TINY.batch) for g in range(TINY.num_kv_heads))
     assert sorted(map(tuple, changed_k.tolist())) == expect
     for b in range(TINY.batch):
         blk, slot = case.block_table[b, case.ctx_lens[b] // bs], case.ctx_lens[b] % bs
-        assert np.array_equal(got["k_cache"][blk, :, slot, :], got["k1_bits"][b])
-        assert np.array_equal(got["v_cache"][blk, :, :, slot], got["v1_bits"][b])
-    changed_v = np.argwhere(np.any(got["v_cache"] != case.v_cache, axis=2))  # [blk, g, slot]
-    assert sorted(map(tuple, changed_v.tolist())) == expect
+        assert np.array_equal(got["k_cache"][blk, :, :, slot, :].reshape(TINY.num_kv_heads, -1), got["k1_bits"][b])
+        assert np.array_equal(got["v_cache"][blk, :, slot // 16, :, slot % 16], got["v1_bits"][b])
+    changed_v = np.argwhere(np.any(got["v_cache"] != case.v_cache, axis=3))  # [blk, g, tile, s]
+    assert sorted((int(i), int(g), int(t) * 16 + int(s)) for i, g, t, s in changed_v) == expect
 
 
 def _brute_disagrees(cfg=TINY, seed=26):

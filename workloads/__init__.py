@@ -9,10 +9,13 @@ from ``[seed, tag, b, g]``, so any chunk can be regenerated on its own.
 
 Cache layout (one layer), shared by every consumer:
 
-* ``k_cache``: ``[num_blocks, num_kv_heads, block_size, head_dim]`` -- one key
-  row of ``head_dim`` contiguous elements per cached position.
-* ``v_cache``: ``[num_blocks, num_kv_heads, head_dim, block_size]`` -- values
-  are stored transposed inside a block, positions contiguous per dimension.
+* ``k_cache``: ``[num_blocks, num_kv_heads, head_dim // 8, block_size, 8]`` --
+  keys in groups of 8 dimensions; within a group, the block's positions are
+  contiguous (8 elements each).
+* ``v_cache``: ``[num_blocks, num_kv_heads, block_size // 16, head_dim, 16]`` --
+  values transposed inside tiles of 16 positions: for each tile and dimension,
+  the 16 positions are contiguous.
+* ``block_size`` is a multiple of 16 and ``head_dim`` a multiple of 8.
 * ``block_table``: int32 ``[batch, max_blocks_per_seq]``; logical block ``j``
   of sequence ``b`` lives in physical block ``block_table[b, j]``; unused
   entries hold -1. A "contiguous" cache is the special case of one block per
@@ -85,7 +88,7 @@ class AttnConfig:
     ctx_lens: Optional[Tuple[int, ...]] = None  # explicit per-sequence lengths
     ctx_range: Optional[Tuple[int, int]] = None  # inclusive uniform range when drawn
     block_size: int = 0  # 0: contiguous cache (one block per sequence)
-    capacity: int = 0  # contiguous capacity; 0: next power of two >= max length
+    capacity: int = 0  # contiguous capacity; 0: next power of two >= max length (at least 16)
     shuffle_blocks: bool = False
     peaky_fraction: float = 0.0  # fraction of key rows per (b, kv head) scaled
     peaky_factor: float = 1.0
@@ -146,7 +149,7 @@ def plan_cache(batch: int, ctx_lens: np.ndarray, block_size: int, capacity: int,
     """Physical block assignment. ``extra_slots`` reserves room past each length."""
     need = ctx_lens.astype(np.int64) + extra_slots
     if block_size == 0:
-        cap = capacity or (1 << int(math.ceil(math.log2(max(int(need.max()), 1)))))
+        cap = capacity or max(16, 1 << int(math.ceil(math.log2(max(int(need.max()), 1)))))
         if need.max() > cap:
             raise ValueError("capacity smaller than a sequence")
         table = np.arange(batch, dtype=np.int32).reshape(batch, 1)
@@ -180,8 +183,11 @@ def kv_rows(cfg_seed: int, b: int, g: int, length: int, head_dim: int, dtype: st
 
 
 def empty_cache(layout: CacheLayout, num_kv_heads: int, head_dim: int, dtype: str):
-    shape_k = (layout.num_blocks, num_kv_heads, layout.block_size, head_dim)
-    shape_v = (layout.num_blocks, num_kv_heads, head_dim, layout.block_size)
+    bs = layout.block_size
+    if bs % 16 or head_dim % 8:
+        raise ValueError("block_size must be a multiple of 16 and head_dim of 8")
+    shape_k = (layout.num_blocks, num_kv_heads, head_dim // 8, bs, 8)
+    shape_v = (layout.num_blocks, num_kv_heads, bs // 16, head_dim, 16)
     if dtype == "bf16":
         return (np.full(shape_k, BF16_NAN_BITS, dtype=np.uint16),
                 np.full(shape_v, BF16_NAN_BITS, dtype=np.uint16))
@@ -196,8 +202,9 @@ def store_rows(k_cache, v_cache, layout: CacheLayout, b: int, g: int, k_rows, v_
     if np.any(blk < 0):
         raise ValueError("position outside the allocated blocks")
     slot = pos % bs
-    k_cache[blk, g, slot, :] = k_rows
-    v_cache[blk, g, :, slot] = v_rows
+    n, d = k_rows.shape
+    k_cache[blk, g, :, slot, :] = k_rows.reshape(n, d // 8, 8)
+    v_cache[blk, g, slot // 16, :, slot % 16] = v_rows
 
 
 @dataclass

@@ -1,12 +1,12 @@
 """Dual-flow shared-KV decode on AMD Instinct MI355X (gfx950).
 
 The computation lives in libdfa.so (C ABI in include/dfa.h, HIP kernels under
-csrc/). This package is its ctypes binding (``_lib``, the same names as the C
-entry points) plus ``host``, small helpers that turn host-side workload
-descriptions into descriptors and device tensors. PyTorch serves only for
-device memory and streams.
+csrc/, built by ``build``). This package is its ctypes binding (``_lib``: the
+same names as the C entry points, argument marshalling only). PyTorch serves
+only for device memory, streams and events.
 """
-from ._lib import (DFA_BF16, DFA_F32, AttnDesc, DfaError, dfa_combine, dfa_decode_attn,  # noqa: F401
-                   dfa_decode_attn_num_splits, dfa_decode_attn_partials, dfa_decode_attn_split_len,
+from ._lib import (DFA_BF16, DFA_F32, AttnDesc, DfaError, KernelEvents, dfa_combine,  # noqa: F401
+                   dfa_decode_attn, dfa_decode_attn_num_splits, dfa_decode_attn_partials,
+                   dfa_decode_attn_split_len, dfa_decode_attn_timed,
                    dfa_decode_attn_workspace_size, dfa_status_string, dfa_stream_read,
                    dfa_stream_read_sink_bytes, dfa_version, lib)

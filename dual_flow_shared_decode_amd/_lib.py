@@ -18,8 +18,8 @@ STATUS = {0: "DFA_OK", 1: "DFA_ERR_NULL", 2: "DFA_ERR_SHAPE", 3: "DFA_ERR_DTYPE"
 
 # Every symbol include/dfa.h declares.
 EXPORTS = ["dfa_decode_attn_split_len", "dfa_decode_attn_num_splits", "dfa_decode_attn_workspace_size",
-           "dfa_decode_attn", "dfa_decode_attn_partials", "dfa_combine", "dfa_status_string",
-           "dfa_last_error", "dfa_version", "dfa_stream_read", "dfa_stream_read_sink_bytes"]
+           "dfa_decode_attn", "dfa_decode_attn_timed", "dfa_decode_attn_partials", "dfa_combine",
+           "dfa_status_string", "dfa_last_error", "dfa_version", "dfa_stream_read", "dfa_stream_read_sink_bytes"]
 
 
 class DfaError(RuntimeError):
@@ -39,6 +39,12 @@ class AttnDesc(ctypes.Structure):
                 ("scale", ctypes.c_float), ("q_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32)]
 
 
+class KernelEvents(ctypes.Structure):
+    """Mirror of dfa_kernel_events (hipEvent_t handles)."""
+
+    _fields_ = [("start", ctypes.c_void_p), ("stop", ctypes.c_void_p)]
+
+
 _lib = None
 _P = ctypes.c_void_p
 
@@ -56,6 +62,8 @@ def lib() -> ctypes.CDLL:
             "dfa_decode_attn_num_splits": (ctypes.c_int32, [D]),
             "dfa_decode_attn_workspace_size": (ctypes.c_size_t, [D]),
             "dfa_decode_attn": (ctypes.c_int, [D, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P, _P, _P]),
+            "dfa_decode_attn_timed": (ctypes.c_int, [D, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P, _P, _P,
+                                                     ctypes.POINTER(KernelEvents)]),
             "dfa_decode_attn_partials": (ctypes.c_int, [D, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
             "dfa_combine": (ctypes.c_int, [D, _P, _P, ctypes.c_size_t, _P, _P, _P]),
             "dfa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -119,6 +127,25 @@ def dfa_decode_attn(desc, q1, q2, a, k_cache, v_cache, block_table, ctx_lens, wo
     _check(lib().dfa_decode_attn(ctypes.byref(desc), _ptr(q1), _ptr(q2), _ptr(a), _ptr(k_cache),
                                  _ptr(v_cache), _ptr(block_table), _ptr(ctx_lens), _ptr(workspace),
                                  ws_bytes, _ptr(o1), _ptr(o2), _stream(stream)))
+
+
+def _event_handle(ev):
+    """Raw hipEvent_t of a torch.cuda.Event (created on its first record)."""
+    if ev is None:
+        return None
+    if not ev.cuda_event:
+        raise ValueError("record the event once before passing it, so that it exists")
+    return ev.cuda_event
+
+
+def dfa_decode_attn_timed(desc, q1, q2, a, k_cache, v_cache, block_table, ctx_lens, workspace, o1, o2,
+                          stream=None, start=None, stop=None):
+    """dfa_decode_attn with torch.cuda.Event `start`/`stop` recorded around its attention kernel."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ev = KernelEvents(_event_handle(start), _event_handle(stop))
+    _check(lib().dfa_decode_attn_timed(ctypes.byref(desc), _ptr(q1), _ptr(q2), _ptr(a), _ptr(k_cache),
+                                       _ptr(v_cache), _ptr(block_table), _ptr(ctx_lens), _ptr(workspace),
+                                       ws_bytes, _ptr(o1), _ptr(o2), _stream(stream), ctypes.byref(ev)))
 
 
 def dfa_decode_attn_partials(desc, q1, q2, a, k_cache, v_cache, block_table, ctx_lens, workspace,

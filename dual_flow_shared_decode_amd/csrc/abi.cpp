@@ -27,16 +27,18 @@ int log2i(int64_t x) {
   return r;
 }
 
-// Positions per split chosen by the library: enough workgroups to fill the
-// chip (about 1024 (split, kv head, sequence) workgroups, 4 per CU) while
-// keeping each split long enough to amortise the query load and the merge.
+// Positions per split chosen by the library (measured on MI355X, 256 CUs): a
+// single split per sequence when there are at least 128 (sequence, kv head)
+// pairs -- one workgroup per pair then streams at full rate, and the combine
+// launch would cost more than the extra parallelism gains; otherwise splits of
+// at least 2048 positions, enough of them for about 512 workgroups.
 int64_t auto_split_len(const dfa_attn_desc* d) {
   const int64_t pairs = int64_t(d->batch) * d->num_kv_heads;
-  const int64_t target_wg = 1024;
-  const int64_t want = std::max<int64_t>(1, (target_wg + pairs - 1) / pairs);
+  if (pairs >= 128) return (int64_t(d->max_ctx_len) + 31) / 32 * 32;
+  const int64_t want = (512 + pairs - 1) / pairs;
   int64_t len = (int64_t(d->max_ctx_len) + want - 1) / want;
   len = (len + 127) / 128 * 128;
-  return std::max<int64_t>(len, 256);
+  return std::max<int64_t>(len, 2048);
 }
 
 dfa_status validate_attn(const dfa_attn_desc* d, int32_t* split_out) {
@@ -81,6 +83,7 @@ int32_t num_splits(const dfa_attn_desc* d, int32_t split) {
   return int32_t((int64_t(d->max_ctx_len) + split - 1) / split);
 }
 
+// Workspace = one partial record per (sequence, query head, flow, split).
 size_t workspace_bytes(const dfa_attn_desc* d, int32_t split) {
   return size_t(d->batch) * d->num_q_heads * d->num_flows * size_t(num_splits(d, split)) *
          (d->head_dim + dfa::kRecPad) * sizeof(float);
@@ -126,13 +129,19 @@ dfa::AttnParams make_params(const dfa_attn_desc* d, int32_t split, const void* q
   return p;
 }
 
-dfa_status launch_split_stage(const dfa_attn_desc* d, const dfa::AttnParams& p, hipStream_t st) {
+dfa_status launch_split_stage(const dfa_attn_desc* d, const dfa::AttnParams& p, hipStream_t st,
+                              const dfa_kernel_events* events) {
+  dfa::KernelEvents ev;
+  if (events) {
+    ev.start = static_cast<hipEvent_t>(events->start);
+    ev.stop = static_cast<hipEvent_t>(events->stop);
+  }
   hipError_t e;
   if (d->kv_dtype == DFA_F32) {
-    e = dfa::launch_attn_f32(p, d->head_dim, st);
+    e = dfa::launch_attn_f32(p, d->head_dim, st, ev);
   } else {
     const int rows = (d->num_q_heads / d->num_kv_heads) * d->num_flows;
-    e = dfa::launch_attn_bf16(p, d->head_dim, rows <= 8 ? 8 : 16, st);
+    e = dfa::launch_attn_bf16(p, d->head_dim, rows <= 8 ? 8 : 16, st, ev);
   }
   if (e != hipSuccess) return fail(DFA_ERR_HIP, std::string("attention launch: ") + hipGetErrorString(e));
   return DFA_OK;
@@ -185,10 +194,10 @@ size_t dfa_decode_attn_workspace_size(const dfa_attn_desc* desc) {
   return workspace_bytes(desc, split);
 }
 
-dfa_status dfa_decode_attn(const dfa_attn_desc* desc, const void* q1, const void* q2, const float* a,
-                           const void* k_cache, const void* v_cache, const int32_t* block_table,
-                           const int32_t* ctx_lens, void* workspace, size_t ws_bytes, float* o1,
-                           float* o2, void* stream) {
+dfa_status dfa_decode_attn_timed(const dfa_attn_desc* desc, const void* q1, const void* q2, const float* a,
+                                 const void* k_cache, const void* v_cache, const int32_t* block_table,
+                                 const int32_t* ctx_lens, void* workspace, size_t ws_bytes, float* o1,
+                                 float* o2, void* stream, const dfa_kernel_events* events) {
   try {
     int32_t split = 0;
     dfa_status st = validate_attn(desc, &split);
@@ -209,15 +218,23 @@ dfa_status dfa_decode_attn(const dfa_attn_desc* desc, const void* q1, const void
       p.direct = 1;
       p.o1 = o1;
       p.o2 = desc->num_flows == 2 ? o2 : nullptr;
-      return launch_split_stage(desc, p, hs);
+      return launch_split_stage(desc, p, hs, events);
     }
     p.part = static_cast<float*>(workspace);
-    st = launch_split_stage(desc, p, hs);
+    st = launch_split_stage(desc, p, hs, events);
     if (st != DFA_OK) return st;
     return launch_combine_stage(desc, split, ctx_lens, workspace, o1, o2, hs);
   } catch (...) {
     return fail(DFA_ERR_HIP, "unexpected host exception");
   }
+}
+
+dfa_status dfa_decode_attn(const dfa_attn_desc* desc, const void* q1, const void* q2, const float* a,
+                           const void* k_cache, const void* v_cache, const int32_t* block_table,
+                           const int32_t* ctx_lens, void* workspace, size_t ws_bytes, float* o1,
+                           float* o2, void* stream) {
+  return dfa_decode_attn_timed(desc, q1, q2, a, k_cache, v_cache, block_table, ctx_lens, workspace, ws_bytes,
+                               o1, o2, stream, nullptr);
 }
 
 dfa_status dfa_decode_attn_partials(const dfa_attn_desc* desc, const void* q1, const void* q2,
@@ -234,7 +251,7 @@ dfa_status dfa_decode_attn_partials(const dfa_attn_desc* desc, const void* q1, c
     if (st != DFA_OK) return st;
     dfa::AttnParams p = make_params(desc, split, q1, q2, a, k_cache, v_cache, block_table, ctx_lens);
     p.part = static_cast<float*>(workspace);
-    return launch_split_stage(desc, p, static_cast<hipStream_t>(stream));
+    return launch_split_stage(desc, p, static_cast<hipStream_t>(stream), nullptr);
   } catch (...) {
     return fail(DFA_ERR_HIP, "unexpected host exception");
   }

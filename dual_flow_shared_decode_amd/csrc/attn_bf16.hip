@@ -34,6 +34,7 @@
 
 #include "attn_common.h"
 #include "dfa_internal.h"
+#include "launch.h"
 
 namespace dfa {
 
@@ -293,19 +294,14 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnParams p) {
   merge_waves<D, NRP>(p, b, g, s, sm, sl, so);
 }
 
-hipError_t launch_attn_bf16(const AttnParams& p, int head_dim, int rows_padded, hipStream_t stream) {
+hipError_t launch_attn_bf16(const AttnParams& p, int head_dim, int rows_padded, hipStream_t stream,
+                            const KernelEvents& ev) {
   const dim3 grid(p.n_splits, p.hkv, p.batch), block(kThreads);
-  if (head_dim == 128 && rows_padded == 8)
-    hipLaunchKernelGGL((attn_bf16_kernel<128, 8>), grid, block, 0, stream, p);
-  else if (head_dim == 128 && rows_padded == 16)
-    hipLaunchKernelGGL((attn_bf16_kernel<128, 16>), grid, block, 0, stream, p);
-  else if (head_dim == 64 && rows_padded == 8)
-    hipLaunchKernelGGL((attn_bf16_kernel<64, 8>), grid, block, 0, stream, p);
-  else if (head_dim == 64 && rows_padded == 16)
-    hipLaunchKernelGGL((attn_bf16_kernel<64, 16>), grid, block, 0, stream, p);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+  if (head_dim == 128 && rows_padded == 8) return launch_kernel(attn_bf16_kernel<128, 8>, grid, block, stream, ev, p);
+  if (head_dim == 128 && rows_padded == 16) return launch_kernel(attn_bf16_kernel<128, 16>, grid, block, stream, ev, p);
+  if (head_dim == 64 && rows_padded == 8) return launch_kernel(attn_bf16_kernel<64, 8>, grid, block, stream, ev, p);
+  if (head_dim == 64 && rows_padded == 16) return launch_kernel(attn_bf16_kernel<64, 16>, grid, block, stream, ev, p);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace dfa

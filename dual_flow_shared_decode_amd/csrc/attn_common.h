@@ -73,12 +73,13 @@ __device__ __forceinline__ int stage_table(const AttnParams& p, int b, const Spl
 
 // Cross-wave merge. Each wave w left, for each of its rows, the running max
 // sm[w*NRP+row], sum sl[w*NRP+row] and unnormalised output so[(w*NRP+row)*D+d]
-// (all in base-2 units). Writes either the normalised output (direct) or the
-// split record (m, l, O) of each row.
+// (all in base-2 units). Writes the normalised output in direct mode (one
+// split per sequence), otherwise the split record (O, m, l) of each row.
 template <int D, int NRP>
 __device__ __forceinline__ void merge_waves(const AttnParams& p, int b, int g, int s,
                                             const float* sm, const float* sl, const float* so) {
   const int nr = p.flows * p.group;
+  const bool to_out = p.direct;
   for (int idx = threadIdx.x; idx < nr * D; idx += kThreads) {
     const int row = idx / D, d = idx - row * D;
     float mx = -INFINITY;
@@ -92,7 +93,7 @@ __device__ __forceinline__ void merge_waves(const AttnParams& p, int b, int g, i
       l += e * sl[w * NRP + row];
     }
     const int f = row / p.group, h = g * p.group + (row - f * p.group);
-    if (p.direct) {
+    if (to_out) {
       float* out = f ? p.o2 : p.o1;
       out[((size_t)b * p.hq + h) * D + d] = o / l;
     } else {

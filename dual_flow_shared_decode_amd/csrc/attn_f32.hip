@@ -15,6 +15,7 @@
 
 #include "attn_common.h"
 #include "dfa_internal.h"
+#include "launch.h"
 
 namespace dfa {
 
@@ -122,15 +123,11 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnParams p) {
   merge_waves<D, kMaxRows>(p, b, g, s, sm, sl, so);
 }
 
-hipError_t launch_attn_f32(const AttnParams& p, int head_dim, hipStream_t stream) {
+hipError_t launch_attn_f32(const AttnParams& p, int head_dim, hipStream_t stream, const KernelEvents& ev) {
   const dim3 grid(p.n_splits, p.hkv, p.batch), block(kThreads);
-  if (head_dim == 64)
-    hipLaunchKernelGGL((attn_f32_kernel<64>), grid, block, 0, stream, p);
-  else if (head_dim == 128)
-    hipLaunchKernelGGL((attn_f32_kernel<128>), grid, block, 0, stream, p);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+  if (head_dim == 64) return launch_kernel(attn_f32_kernel<64>, grid, block, stream, ev, p);
+  if (head_dim == 128) return launch_kernel(attn_f32_kernel<128>, grid, block, stream, ev, p);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace dfa

@@ -21,8 +21,8 @@ struct AttnParams {
   const void* v;
   const int32_t* table;
   const int32_t* ctx;
-  float* part;   // split records (split mode)
-  float* o1;     // outputs (direct mode)
+  float* part;  // split records (split mode)
+  float* o1;    // outputs (direct mode)
   float* o2;
   int32_t batch, hq, hkv, group, flows;
   int32_t bs_log2, max_blocks, num_blocks, max_ctx;
@@ -41,9 +41,16 @@ struct CombineParams {
   int32_t batch, hq, flows, split_len, n_splits, max_ctx;
 };
 
+// Optional events recorded by the runtime at the start and end of a kernel's
+// own dispatch (no extra commands on the stream).
+struct KernelEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
 // Launchers return the launch status (hipGetLastError after the launch).
-hipError_t launch_attn_bf16(const AttnParams& p, int head_dim, int rows_padded, hipStream_t s);
-hipError_t launch_attn_f32(const AttnParams& p, int head_dim, hipStream_t s);
+hipError_t launch_attn_bf16(const AttnParams& p, int head_dim, int rows_padded, hipStream_t s, const KernelEvents& ev);
+hipError_t launch_attn_f32(const AttnParams& p, int head_dim, hipStream_t s, const KernelEvents& ev);
 hipError_t launch_combine(const CombineParams& p, int head_dim, hipStream_t s);
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s);
 size_t stream_read_threads();

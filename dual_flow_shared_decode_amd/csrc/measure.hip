@@ -1,6 +1,7 @@
-// Bandwidth ceiling probe: a plain read of a buffer with coalesced 16-byte
-// loads, each workgroup streaming one contiguous range. Not part of the
-// method; the attention kernels' achieved bandwidth is compared to it.
+// Bandwidth ceiling probe: a read of a buffer with coalesced, non-temporal
+// 16-byte loads (the cache policy the attention kernels stream with), each
+// workgroup streaming one contiguous range. Not part of the method; the
+// attention kernels' achieved bandwidth is compared to it.
 #include <hip/hip_runtime.h>
 
 #include "dfa_internal.h"
@@ -24,7 +25,7 @@ __global__ __launch_bounds__(kReadThreads) void stream_read_kernel(const u32x4* 
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const size_t j = i + (size_t)u * kReadThreads;
-      v[u] = j < stop ? buf[j] : u32x4{0u, 0u, 0u, 0u};
+      v[u] = j < stop ? __builtin_nontemporal_load(buf + j) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;

@@ -110,7 +110,8 @@ DFA_API int32_t dfa_decode_attn_num_splits(const dfa_attn_desc* desc);
 /*
  * Workspace bytes needed by dfa_decode_attn (when it runs more than one
  * split) and by dfa_decode_attn_partials / dfa_combine: one partial record per
- * (sequence, query head, flow, split). 0 if `desc` is invalid.
+ * (sequence, query head, flow, split). 0 if `desc` is invalid. Calls that
+ * share a workspace must not overlap in time.
  */
 DFA_API size_t dfa_decode_attn_workspace_size(const dfa_attn_desc* desc);
 
@@ -120,7 +121,9 @@ DFA_API size_t dfa_decode_attn_workspace_size(const dfa_attn_desc* desc);
  *     q^1 = Q1[b,h],  q^2 = Q2[b,h] + a[h] * Q1[b,h]
  *     O_f[b,h] = sum_t softmax_t(scale * <q^f, K_t>) V_t,  t in [0, ctx_lens[b])
  * Both flows are served from one read of every cached key and value. The
- * caches are read only (the auxiliary flow never writes KV).
+ * caches are read only (the auxiliary flow never writes KV). With one split
+ * per sequence this is one kernel; with more, the split kernel is followed by
+ * the log-sum-exp combine of dfa_combine on the same stream.
  *  q1, q2:   Q1, Q2 of type desc->q_dtype. q2 and a are ignored (may be NULL)
  *            when num_flows == 1.
  *  k_cache, v_cache: type desc->kv_dtype, layouts above. Never written.
@@ -134,6 +137,24 @@ DFA_API dfa_status dfa_decode_attn(const dfa_attn_desc* desc, const void* q1, co
                            const int32_t* block_table, const int32_t* ctx_lens,
                            void* workspace, size_t workspace_bytes, float* o1, float* o2,
                            void* stream);
+
+/*
+ * Optional events for measuring the attention kernel itself: hipEvent_t
+ * handles (passed as void*) that the runtime records when the attention
+ * kernel's dispatch starts and ends, adding no command to the stream. NULL
+ * members are not recorded. The combine kernel, if any, is not covered.
+ */
+typedef struct dfa_kernel_events {
+  void* start;
+  void* stop;
+} dfa_kernel_events;
+
+/* dfa_decode_attn with dfa_kernel_events around its attention kernel (events may be NULL). */
+DFA_API dfa_status dfa_decode_attn_timed(const dfa_attn_desc* desc, const void* q1, const void* q2,
+                                         const float* a, const void* k_cache, const void* v_cache,
+                                         const int32_t* block_table, const int32_t* ctx_lens,
+                                         void* workspace, size_t workspace_bytes, float* o1, float* o2,
+                                         void* stream, const dfa_kernel_events* events);
 
 /*
  * The split stage alone: writes one partial record per (b, h, f, split) to
@@ -172,8 +193,8 @@ DFA_API int32_t dfa_version(void);
 
 /*
  * Measurement helper (not part of the method): reads `bytes` bytes at `buf`
- * with coalesced 16-byte loads on `stream`, the bandwidth ceiling that the
- * streaming kernels are compared to. `sink` must hold 4 bytes per launched
+ * with coalesced, non-temporal 16-byte loads on `stream`, the bandwidth
+ * ceiling that the streaming kernels are compared to. `sink` must hold 4 bytes per launched
  * thread (dfa_stream_read_sink_bytes()); it is written only with a value that
  * keeps the loads live. bytes must be a multiple of 16.
  */

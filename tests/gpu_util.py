@@ -37,7 +37,7 @@ def run_attn(case, num_flows=2, split_len=0, tensors=None, desc=None):
     t = tensors or upload_attn_case(case)
     d = desc or desc_for(case, num_flows, split_len)
     ws_bytes = dfa.dfa_decode_attn_workspace_size(d)
-    ws = torch.empty(max(ws_bytes // 4, 4), dtype=torch.float32, device="cuda")
+    ws = torch.zeros(max(ws_bytes // 4, 4), dtype=torch.float32, device="cuda")
     B, H, D = case.cfg.batch, case.cfg.num_q_heads, case.cfg.head_dim
     o1 = torch.full((B, H, D), float("nan"), device="cuda")
     o2 = torch.full((B, H, D), float("nan"), device="cuda") if num_flows == 2 else None

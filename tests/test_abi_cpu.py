@@ -48,6 +48,10 @@ def test_split_plan_and_workspace_size():
     ns = dfa.dfa_decode_attn_num_splits(d)
     assert split % 32 == 0 and ns == -(-4096 // split)
     assert dfa.dfa_decode_attn_workspace_size(d) == 16 * 32 * 2 * ns * (128 + 4) * 4
+    # 128 (sequence, kv head) pairs: one split each; 32 pairs of 131072: splits of >= 2048 positions
+    assert ns == 1
+    d4 = c2_desc(batch=4, block_size=131072, max_ctx_len=131072)
+    assert dfa.dfa_decode_attn_split_len(d4) >= 2048 and dfa.dfa_decode_attn_num_splits(d4) >= 8
     d1 = c2_desc(split_len=4096)
     assert dfa.dfa_decode_attn_num_splits(d1) == 1
     assert dfa.dfa_decode_attn_split_len(c2_desc(split_len=96)) == 96
@@ -97,13 +101,13 @@ def test_null_pointers(missing):
 
 
 def test_single_flow_accepts_null_aux_pointers_until_the_workspace_check():
-    with pytest.raises(dfa.DfaError) as e:
-        _call_attn(c2_desc(num_flows=1), q2=None, a=None, o2=None, ws=None)
+    with pytest.raises(dfa.DfaError) as e:  # split_len 512: several splits, so a workspace is needed
+        _call_attn(c2_desc(num_flows=1, split_len=512), q2=None, a=None, o2=None, ws=None)
     assert _lib.STATUS[e.value.status] == "DFA_ERR_WORKSPACE"
 
 
 def test_workspace_and_alignment_errors():
-    d = c2_desc()
+    d = c2_desc(split_len=512)  # several splits, so a workspace is needed
     need = dfa.dfa_decode_attn_workspace_size(d)
     with pytest.raises(dfa.DfaError) as e:
         _call_attn(d, ws=None)

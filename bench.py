@@ -36,7 +36,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "dual-flow decode attn: tokens/s (both flows) + achieved HBM GB/s vs peak"
 HBM_PEAK_GBPS = 8000.0
-KERNEL_SOURCES = ["dual_flow_shared_decode_amd/csrc/attn_bf16.hip", "dual_flow_shared_decode_amd/csrc/attn_common.h"]
+KERNEL_SOURCES = ["dual_flow_shared_decode_amd/csrc/" + f
+                  for f in ("attn_bf16.hip", "attn_common.h", "dfa_internal.h", "launch.h")]
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "attn_bf16_c2_counters.txt")
 
 
@@ -124,6 +125,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="time the steps only (for profiler runs)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="after timing, copy a MIB-MiB buffer once (a known-size reference for HBM counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -221,6 +224,15 @@ def main():
                         "traffic": measured_traffic(cfg.name), "algorithmic_bytes_per_launch": kern_bytes,
                         "avg_launch_us": kern_ms * 1e3}}
 
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        rec["copy_calibration_bytes"] = n
+        del src, dst
     if not args.no_extras:
         d1, step1 = runner(1)
         ms1, kern1, _ = timed(step1, args.steps, args.warmup)

@@ -19,7 +19,11 @@ STATUS = {0: "DFA_OK", 1: "DFA_ERR_NULL", 2: "DFA_ERR_SHAPE", 3: "DFA_ERR_DTYPE"
 # Every symbol include/dfa.h declares.
 EXPORTS = ["dfa_decode_attn_split_len", "dfa_decode_attn_num_splits", "dfa_decode_attn_workspace_size",
            "dfa_decode_attn", "dfa_decode_attn_timed", "dfa_decode_attn_partials", "dfa_combine",
+           "dfa_dual_gemv_workspace_size", "dfa_dual_gemv", "dfa_pack_weight",
+           "dfa_decode_layer_workspace_size", "dfa_decode_layer",
            "dfa_status_string", "dfa_last_error", "dfa_version", "dfa_stream_read", "dfa_stream_read_sink_bytes"]
+
+DFA_EPI_NONE, DFA_EPI_RESIDUAL, DFA_EPI_SWIGLU, DFA_EPI_RESIDUAL_COUPLED, DFA_EPI_KV_APPEND = range(5)
 
 
 class DfaError(RuntimeError):
@@ -37,6 +41,37 @@ class AttnDesc(ctypes.Structure):
                 ("num_blocks", ctypes.c_int32), ("max_ctx_len", ctypes.c_int32),
                 ("num_flows", ctypes.c_int32), ("split_len", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("q_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32)]
+
+
+class GemvDesc(ctypes.Structure):
+    """Mirror of dfa_gemv_desc."""
+
+    _fields_ = [("batch", ctypes.c_int32), ("n", ctypes.c_int32), ("k", ctypes.c_int32),
+                ("num_flows", ctypes.c_int32), ("epilogue", ctypes.c_int32), ("x_exact_bf16", ctypes.c_int32),
+                ("k_split", ctypes.c_int32)]
+
+
+class KvTarget(ctypes.Structure):
+    """Mirror of dfa_kv_target."""
+
+    _fields_ = [("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
+                ("ctx_lens", ctypes.c_void_p), ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
+                ("num_blocks", ctypes.c_int32)]
+
+
+class LayerDesc(ctypes.Structure):
+    """Mirror of dfa_layer_desc."""
+
+    _fields_ = [(f, ctypes.c_int32) for f in ("batch", "hidden", "num_q_heads", "num_kv_heads", "head_dim", "mlp",
+                                              "block_size", "max_blocks_per_seq", "num_blocks", "max_ctx_len")] + \
+               [("scale", ctypes.c_float), ("x_exact_bf16", ctypes.c_int32)]
+
+
+class LayerWeights(ctypes.Structure):
+    """Mirror of dfa_layer_weights."""
+
+    _fields_ = [(f, ctypes.c_void_p) for f in ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down", "a", "b", "c")]
 
 
 class KernelEvents(ctypes.Structure):
@@ -66,6 +101,13 @@ def lib() -> ctypes.CDLL:
                                                      ctypes.POINTER(KernelEvents)]),
             "dfa_decode_attn_partials": (ctypes.c_int, [D, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
             "dfa_combine": (ctypes.c_int, [D, _P, _P, ctypes.c_size_t, _P, _P, _P]),
+            "dfa_dual_gemv_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(GemvDesc)]),
+            "dfa_dual_gemv": (ctypes.c_int, [ctypes.POINTER(GemvDesc), _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                             ctypes.POINTER(KvTarget), _P, ctypes.c_size_t, _P]),
+            "dfa_pack_weight": (ctypes.c_int, [_P, _P, ctypes.c_int32, ctypes.c_int32, _P]),
+            "dfa_decode_layer_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(LayerDesc)]),
+            "dfa_decode_layer": (ctypes.c_int, [ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerWeights), _P, _P, _P,
+                                                _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
             "dfa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
             "dfa_last_error": (ctypes.c_char_p, []),
             "dfa_version": (ctypes.c_int32, []),
@@ -160,6 +202,45 @@ def dfa_combine(desc, ctx_lens, workspace, o1, o2, stream=None):
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().dfa_combine(ctypes.byref(desc), _ptr(ctx_lens), _ptr(workspace), ws_bytes, _ptr(o1),
                              _ptr(o2), _stream(stream)))
+
+
+def dfa_dual_gemv_workspace_size(desc: GemvDesc) -> int:
+    return int(lib().dfa_dual_gemv_workspace_size(ctypes.byref(desc)))
+
+
+def kv_target(k_cache, v_cache, block_table, ctx_lens, num_kv_heads, head_dim, block_size,
+              max_blocks_per_seq, num_blocks) -> KvTarget:
+    return KvTarget(_ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(ctx_lens), num_kv_heads, head_dim,
+                    block_size, max_blocks_per_seq, num_blocks)
+
+
+def dfa_dual_gemv(desc, w, w2, x1, x2, couple, res1, res2, y1, y2, kv, workspace, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().dfa_dual_gemv(ctypes.byref(desc), _ptr(w), _ptr(w2), _ptr(x1), _ptr(x2), _ptr(couple),
+                               _ptr(res1), _ptr(res2), _ptr(y1), _ptr(y2),
+                               ctypes.byref(kv) if kv is not None else None, _ptr(workspace), ws_bytes,
+                               _stream(stream)))
+
+
+def dfa_pack_weight(w, w_tiled, n, k, stream=None):
+    _check(lib().dfa_pack_weight(_ptr(w), _ptr(w_tiled), n, k, _stream(stream)))
+
+
+def dfa_decode_layer_workspace_size(desc: LayerDesc) -> int:
+    return int(lib().dfa_decode_layer_workspace_size(ctypes.byref(desc)))
+
+
+def layer_weights(wq, wk, wv, wo, w_gate, w_up, w_down, a, b, c) -> LayerWeights:
+    """Device addresses of packed weights and coupling vectors (tensors or None)."""
+    return LayerWeights(*[_ptr(t) for t in (wq, wk, wv, wo, w_gate, w_up, w_down, a, b, c)])
+
+
+def dfa_decode_layer(desc, weights, x1, x2, k_cache, v_cache, block_table, ctx_lens, out1, out2, workspace,
+                     stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().dfa_decode_layer(ctypes.byref(desc), ctypes.byref(weights), _ptr(x1), _ptr(x2), _ptr(k_cache),
+                                  _ptr(v_cache), _ptr(block_table), _ptr(ctx_lens), _ptr(out1), _ptr(out2),
+                                  _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def dfa_stream_read(buf, sink, stream=None):

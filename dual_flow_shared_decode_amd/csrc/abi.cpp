@@ -3,6 +3,7 @@
 // an invalid call returns a status and enqueues nothing.
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <string>
@@ -147,9 +148,10 @@ dfa_status launch_split_stage(const dfa_attn_desc* d, const dfa::AttnParams& p, 
   return DFA_OK;
 }
 
-dfa_status launch_combine_stage(const dfa_attn_desc* d, int32_t split, const int32_t* ctx,
+dfa_status launch_combine_stage(const dfa_attn_desc* d, int32_t split, const int32_t* ctx, int32_t ctx_add,
                                 const void* ws, float* o1, float* o2, hipStream_t st) {
   dfa::CombineParams c{};
+  c.ctx_add = ctx_add;
   c.part = static_cast<const float*>(ws);
   c.ctx = ctx;
   c.o1 = o1;
@@ -172,9 +174,281 @@ dfa_status check_workspace(const dfa_attn_desc* d, int32_t split, const void* ws
   return DFA_OK;
 }
 
+dfa_status attn_impl(const dfa_attn_desc* desc, const void* q1, const void* q2, const float* a, const void* k_cache,
+                     const void* v_cache, const int32_t* block_table, const int32_t* ctx_lens, int32_t ctx_add,
+                     void* workspace, size_t ws_bytes, float* o1, float* o2, hipStream_t hs,
+                     const dfa_kernel_events* events) {
+  int32_t split = 0;
+  dfa_status st = validate_attn(desc, &split);
+  if (st != DFA_OK) return st;
+  st = check_tensors(desc, q1, q2, a, k_cache, v_cache, block_table, ctx_lens);
+  if (st != DFA_OK) return st;
+  if (!o1 || (desc->num_flows == 2 && !o2)) return fail(DFA_ERR_NULL, "o1 (and o2 with two flows) are required");
+  if (!aligned16(o1) || (desc->num_flows == 2 && !aligned16(o2)))
+    return fail(DFA_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
+  const int32_t ns = num_splits(desc, split);
+  if (ns > 1) {
+    st = check_workspace(desc, split, workspace, ws_bytes);
+    if (st != DFA_OK) return st;
+  }
+  dfa::AttnParams p = make_params(desc, split, q1, q2, a, k_cache, v_cache, block_table, ctx_lens);
+  p.ctx_add = ctx_add;
+  if (ns == 1) {
+    p.direct = 1;
+    p.o1 = o1;
+    p.o2 = desc->num_flows == 2 ? o2 : nullptr;
+    return launch_split_stage(desc, p, hs, events);
+  }
+  p.part = static_cast<float*>(workspace);
+  st = launch_split_stage(desc, p, hs, events);
+  if (st != DFA_OK) return st;
+  return launch_combine_stage(desc, split, ctx_lens, ctx_add, workspace, o1, o2, hs);
+}
+
+// ------------------------------------------------------------------ dual GEMV
+struct GemvPlan {
+  int32_t cbf, m_pad, k_split, k_range, mats;
+};
+
+dfa_status validate_gemv(const dfa_gemv_desc* d, GemvPlan* plan) {
+  if (!d) return fail(DFA_ERR_NULL, "desc is NULL");
+  if (d->num_flows != 1 && d->num_flows != 2) return fail(DFA_ERR_SHAPE, "num_flows must be 1 or 2");
+  if (d->batch < 1 || d->batch * d->num_flows > 64)
+    return fail(DFA_ERR_UNSUPPORTED, "batch must be in [1, 32] with two flows, [1, 64] with one");
+  if (d->n < 128 || d->n % 128 != 0) return fail(DFA_ERR_SHAPE, "n must be a positive multiple of 128");
+  if (d->k < 128 || d->k % 128 != 0) return fail(DFA_ERR_SHAPE, "k must be a positive multiple of 128");
+  if (d->epilogue < DFA_EPI_NONE || d->epilogue > DFA_EPI_KV_APPEND) return fail(DFA_ERR_SHAPE, "unknown epilogue");
+  if (d->epilogue == DFA_EPI_KV_APPEND && d->num_flows != 1)
+    return fail(DFA_ERR_SHAPE, "the KV append is the primary flow's alone (num_flows 1)");
+  if (d->k_split < 0) return fail(DFA_ERR_SHAPE, "k_split must be >= 0");
+  GemvPlan pl;
+  pl.cbf = (d->batch + 15) / 16;  // 16-row activation blocks per flow; kernels exist for 1, 2, 4 blocks in all
+  if (d->num_flows * pl.cbf > 4) return fail(DFA_ERR_UNSUPPORTED, "too many activation rows");
+  if (pl.cbf == 3) pl.cbf = 4;    // one flow, 33..48 rows: padded to 64
+  pl.m_pad = d->num_flows * pl.cbf * 16;
+  const int64_t chunks = d->k / int64_t(dfa::gemv_chunk());
+  const int64_t row_groups = d->n / int64_t(dfa::gemv_rows_per_workgroup());
+  int64_t ks = d->k_split > 0 ? d->k_split : std::max<int64_t>(1, (512 + row_groups - 1) / row_groups);
+  ks = std::min<int64_t>(ks, chunks);
+  const int64_t chunks_per = (chunks + ks - 1) / ks;
+  pl.k_range = int32_t(chunks_per * dfa::gemv_chunk());
+  pl.k_split = int32_t((chunks + chunks_per - 1) / chunks_per);
+  pl.mats = (d->epilogue == DFA_EPI_SWIGLU || d->epilogue == DFA_EPI_KV_APPEND) ? 2 : 1;
+  if (plan) *plan = pl;
+  return DFA_OK;
+}
+
+size_t gemv_workspace(const dfa_gemv_desc* d, const GemvPlan& pl) {
+  return size_t(pl.k_split) * pl.mats * pl.m_pad * size_t(d->n) * sizeof(float);
+}
+
+dfa_status gemv_impl(const dfa_gemv_desc* d, const uint16_t* w, const uint16_t* w2, const float* x1,
+                     const float* x2, const float* couple, const float* res1, const float* res2, float* y1,
+                     float* y2, const dfa_kv_target* kv, void* workspace, size_t ws_bytes, hipStream_t hs) {
+  {
+    GemvPlan pl;
+    dfa_status st = validate_gemv(d, &pl);
+    if (st != DFA_OK) return st;
+    const bool two = d->num_flows == 2;
+    const bool pair = pl.mats == 2;
+    const bool kvapp = d->epilogue == DFA_EPI_KV_APPEND;
+    const bool resid = d->epilogue == DFA_EPI_RESIDUAL || d->epilogue == DFA_EPI_RESIDUAL_COUPLED;
+    if (!w || !x1 || (two && !x2) || (pair && !w2)) return fail(DFA_ERR_NULL, "w, x1 (x2 with two flows, w2 for SwiGLU / KV append) are required");
+    if (!kvapp && (!y1 || (two && !y2))) return fail(DFA_ERR_NULL, "y1 (and y2 with two flows) are required");
+    if (resid && (!res1 || (two && !res2))) return fail(DFA_ERR_NULL, "residual inputs are required");
+    if (kvapp && (!kv || !kv->k_cache || !kv->v_cache || !kv->block_table || !kv->ctx_lens))
+      return fail(DFA_ERR_NULL, "the KV append needs a complete dfa_kv_target");
+    const void* ptrs[] = {w, w2, x1, x2, couple, res1, res2, y1, y2, workspace};
+    for (const void* q : ptrs)
+      if (q && !aligned16(q)) return fail(DFA_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
+    if (!workspace) return fail(DFA_ERR_WORKSPACE, "workspace is required");
+    if (ws_bytes < gemv_workspace(d, pl)) return fail(DFA_ERR_WORKSPACE, "workspace smaller than dfa_dual_gemv_workspace_size()");
+    dfa::GemvParams p{};
+    if (kvapp) {
+      if (kv->num_kv_heads < 1 || kv->head_dim < 8 || kv->head_dim % 8 != 0 ||
+          int64_t(kv->num_kv_heads) * kv->head_dim != d->n)
+        return fail(DFA_ERR_SHAPE, "KV append: n must equal num_kv_heads * head_dim (head_dim multiple of 8)");
+      if (!is_pow2(kv->block_size) || kv->block_size < 16 || kv->max_blocks_per_seq < 1 || kv->num_blocks < 1)
+        return fail(DFA_ERR_SHAPE, "KV append: block_size power of two >= 16, positive table sizes");
+      if (!aligned16(kv->k_cache) || !aligned16(kv->v_cache) || !aligned16(kv->block_table) || !aligned16(kv->ctx_lens))
+        return fail(DFA_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
+      p.kv_k = static_cast<uint16_t*>(kv->k_cache);
+      p.kv_v = static_cast<uint16_t*>(kv->v_cache);
+      p.kv_table = kv->block_table;
+      p.kv_ctx = kv->ctx_lens;
+      p.kv_hkv = kv->num_kv_heads;
+      p.kv_head_dim = kv->head_dim;
+      p.kv_bs_log2 = log2i(kv->block_size);
+      p.kv_max_blocks = kv->max_blocks_per_seq;
+      p.kv_num_blocks = kv->num_blocks;
+    }
+    p.w = w;
+    p.w2 = pair ? w2 : nullptr;
+    p.x1 = x1;
+    p.x2 = two ? x2 : nullptr;
+    p.couple = two ? couple : nullptr;
+    p.res1 = res1;
+    p.res2 = two ? res2 : nullptr;
+    p.y1 = y1;
+    p.y2 = two || kvapp ? y2 : nullptr;
+    p.part = static_cast<float*>(workspace);
+    p.batch = d->batch;
+    p.n = d->n;
+    p.k = d->k;
+    p.flows = d->num_flows;
+    p.cbf = pl.cbf;
+    p.m_pad = pl.m_pad;
+    p.k_split = pl.k_split;
+    p.k_range = pl.k_range;
+    p.pair = pair;
+    p.x_exact = d->x_exact_bf16 != 0;
+    p.epilogue = d->epilogue;
+    hipError_t e = dfa::launch_gemv(p, hs);
+    if (e != hipSuccess) return fail(DFA_ERR_HIP, std::string("gemv launch: ") + hipGetErrorString(e));
+    e = dfa::launch_gemv_finalize(p, hs);
+    if (e != hipSuccess) return fail(DFA_ERR_HIP, std::string("gemv epilogue launch: ") + hipGetErrorString(e));
+    return DFA_OK;
+  }
+}
+
+// ------------------------------------------------------------------ decode layer
+struct LayerPlan {
+  dfa_attn_desc attn;
+  dfa_gemv_desc q, kv, o, mlp_in, mlp_out;
+  size_t off_q, off_o, off_h, off_z, off_attn, off_gemv, total;
+};
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+dfa_status plan_layer(const dfa_layer_desc* d, LayerPlan* lp) {
+  if (!d) return fail(DFA_ERR_NULL, "desc is NULL");
+  if (d->num_kv_heads < 1 || d->num_q_heads % d->num_kv_heads != 0)
+    return fail(DFA_ERR_SHAPE, "num_q_heads must be a positive multiple of num_kv_heads");
+  LayerPlan p{};
+  p.attn = dfa_attn_desc{d->batch, d->num_q_heads, d->num_kv_heads, d->head_dim, d->block_size,
+                         d->max_blocks_per_seq, d->num_blocks, d->max_ctx_len, 2, 0, d->scale, DFA_F32, DFA_BF16};
+  const int32_t qd = d->num_q_heads * d->head_dim, kd = d->num_kv_heads * d->head_dim;
+  p.q = dfa_gemv_desc{d->batch, qd, d->hidden, 2, DFA_EPI_NONE, d->x_exact_bf16, 0};
+  p.kv = dfa_gemv_desc{d->batch, kd, d->hidden, 1, DFA_EPI_KV_APPEND, d->x_exact_bf16, 0};
+  p.o = dfa_gemv_desc{d->batch, d->hidden, qd, 2, DFA_EPI_RESIDUAL, 0, 0};
+  p.mlp_in = dfa_gemv_desc{d->batch, d->mlp, d->hidden, 2, DFA_EPI_SWIGLU, 0, 0};
+  p.mlp_out = dfa_gemv_desc{d->batch, d->hidden, d->mlp, 2, DFA_EPI_RESIDUAL_COUPLED, 0, 0};
+  int32_t split = 0;
+  dfa_status st = validate_attn(&p.attn, &split);
+  if (st != DFA_OK) return st;
+  size_t gemv_ws = 0;
+  for (const dfa_gemv_desc* g : {&p.q, &p.kv, &p.o, &p.mlp_in, &p.mlp_out}) {
+    GemvPlan gp;
+    st = validate_gemv(g, &gp);
+    if (st != DFA_OK) return st;
+    gemv_ws = std::max(gemv_ws, gemv_workspace(g, gp));
+  }
+  const size_t B = size_t(d->batch);
+  p.off_q = 0;
+  p.off_o = p.off_q + align256(2 * B * qd * sizeof(float));
+  p.off_h = p.off_o + align256(2 * B * qd * sizeof(float));
+  p.off_z = p.off_h + align256(2 * B * d->hidden * sizeof(float));
+  p.off_attn = p.off_z + align256(2 * B * d->mlp * sizeof(float));
+  p.off_gemv = p.off_attn + align256(workspace_bytes(&p.attn, split));
+  p.total = p.off_gemv + align256(gemv_ws);
+  if (lp) *lp = p;
+  return DFA_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t dfa_dual_gemv_workspace_size(const dfa_gemv_desc* desc) {
+  GemvPlan pl;
+  if (validate_gemv(desc, &pl) != DFA_OK) return 0;
+  return gemv_workspace(desc, pl);
+}
+
+dfa_status dfa_dual_gemv(const dfa_gemv_desc* d, const uint16_t* w, const uint16_t* w2, const float* x1,
+                         const float* x2, const float* couple, const float* res1, const float* res2, float* y1,
+                         float* y2, const dfa_kv_target* kv, void* workspace, size_t ws_bytes, void* stream) {
+  try {
+    return gemv_impl(d, w, w2, x1, x2, couple, res1, res2, y1, y2, kv, workspace, ws_bytes,
+                     static_cast<hipStream_t>(stream));
+  } catch (...) {
+    return fail(DFA_ERR_HIP, "unexpected host exception");
+  }
+}
+
+size_t dfa_decode_layer_workspace_size(const dfa_layer_desc* desc) {
+  LayerPlan lp;
+  return plan_layer(desc, &lp) == DFA_OK ? lp.total : 0;
+}
+
+dfa_status dfa_decode_layer(const dfa_layer_desc* d, const dfa_layer_weights* w, const float* x1, const float* x2,
+                            void* k_cache, void* v_cache, const int32_t* block_table, const int32_t* ctx_lens,
+                            float* out1, float* out2, void* workspace, size_t ws_bytes, void* stream) {
+  try {
+    LayerPlan lp;
+    dfa_status st = plan_layer(d, &lp);
+    if (st != DFA_OK) return st;
+    if (!w || !w->wq || !w->wk || !w->wv || !w->wo || !w->w_gate || !w->w_up || !w->w_down || !w->a)
+      return fail(DFA_ERR_NULL, "every weight matrix and the coupling vector a are required");
+    if (!x1 || !x2 || !out1 || !out2 || !k_cache || !v_cache || !block_table || !ctx_lens)
+      return fail(DFA_ERR_NULL, "x1, x2, out1, out2, the caches, block_table and ctx_lens are required");
+    if (!workspace) return fail(DFA_ERR_WORKSPACE, "workspace is required");
+    if (!aligned16(workspace)) return fail(DFA_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
+    if (ws_bytes < lp.total) return fail(DFA_ERR_WORKSPACE, "workspace smaller than dfa_decode_layer_workspace_size()");
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(workspace);
+    const size_t B = size_t(d->batch);
+    const size_t qd = size_t(d->num_q_heads) * d->head_dim;
+    float* q1 = reinterpret_cast<float*>(ws + lp.off_q);
+    float* q2 = q1 + B * qd;
+    float* o1 = reinterpret_cast<float*>(ws + lp.off_o);
+    float* o2 = o1 + B * qd;
+    float* h1 = reinterpret_cast<float*>(ws + lp.off_h);
+    float* h2 = h1 + B * d->hidden;
+    float* z1 = reinterpret_cast<float*>(ws + lp.off_z);
+    float* z2 = z1 + B * d->mlp;
+    void* aws = ws + lp.off_attn;
+    void* gws = ws + lp.off_gemv;
+    const size_t aws_bytes = lp.off_gemv - lp.off_attn, gws_bytes = lp.total - lp.off_gemv;
+    // 1. both flows' queries (aux query from its own embedding input x2)
+    st = gemv_impl(&lp.q, w->wq, nullptr, x1, x2, nullptr, nullptr, nullptr, q1, q2, nullptr, gws, gws_bytes, hs);
+    if (st != DFA_OK) return st;
+    // 2. primary keys and values, appended at position ctx_lens[b]; the auxiliary flow writes no KV
+    const dfa_kv_target kv{k_cache, v_cache, block_table, ctx_lens, d->num_kv_heads, d->head_dim, d->block_size,
+                           d->max_blocks_per_seq, d->num_blocks};
+    st = gemv_impl(&lp.kv, w->wk, w->wv, x1, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, &kv, gws,
+                   gws_bytes, hs);
+    if (st != DFA_OK) return st;
+    // 3. both flows attend the primary cache, now ctx_lens[b] + 1 positions; q2 coupled by a
+    st = attn_impl(&lp.attn, q1, q2, w->a, k_cache, v_cache, block_table, ctx_lens, 1, aws, aws_bytes, o1, o2, hs,
+                   nullptr);
+    if (st != DFA_OK) return st;
+    // 4. output projection + residual
+    st = gemv_impl(&lp.o, w->wo, nullptr, o1, o2, nullptr, x1, x2, h1, h2, nullptr, gws, gws_bytes, hs);
+    if (st != DFA_OK) return st;
+    // 5. SwiGLU, MLP-intermediate coupling b
+    st = gemv_impl(&lp.mlp_in, w->w_gate, w->w_up, h1, h2, w->b, nullptr, nullptr, z1, z2, nullptr, gws, gws_bytes,
+                   hs);
+    if (st != DFA_OK) return st;
+    // 6. down projection, MLP-output coupling c, residual
+    return gemv_impl(&lp.mlp_out, w->w_down, nullptr, z1, z2, w->c, h1, h2, out1, out2, nullptr, gws, gws_bytes, hs);
+  } catch (...) {
+    return fail(DFA_ERR_HIP, "unexpected host exception");
+  }
+}
+
+dfa_status dfa_pack_weight(const uint16_t* w, uint16_t* w_tiled, int32_t n, int32_t k, void* stream) {
+  if (!w || !w_tiled) return fail(DFA_ERR_NULL, "w and w_tiled are required");
+  if (n < 16 || n % 16 != 0 || k < 8 || k % 8 != 0) return fail(DFA_ERR_SHAPE, "n must be a multiple of 16, k of 8");
+  if (!aligned16(w) || !aligned16(w_tiled)) return fail(DFA_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(w), b0 = reinterpret_cast<uintptr_t>(w_tiled);
+  const uintptr_t bytes = uintptr_t(n) * uintptr_t(k) * 2;
+  if (a0 < b0 + bytes && b0 < a0 + bytes) return fail(DFA_ERR_SHAPE, "w and w_tiled overlap");
+  const hipError_t e = dfa::launch_pack_weight(w, w_tiled, n, k, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(DFA_ERR_HIP, std::string("pack launch: ") + hipGetErrorString(e));
+  return DFA_OK;
+}
+
 
 int32_t dfa_decode_attn_split_len(const dfa_attn_desc* desc) {
   int32_t split = 0;
@@ -199,31 +473,8 @@ dfa_status dfa_decode_attn_timed(const dfa_attn_desc* desc, const void* q1, cons
                                  const int32_t* ctx_lens, void* workspace, size_t ws_bytes, float* o1,
                                  float* o2, void* stream, const dfa_kernel_events* events) {
   try {
-    int32_t split = 0;
-    dfa_status st = validate_attn(desc, &split);
-    if (st != DFA_OK) return st;
-    st = check_tensors(desc, q1, q2, a, k_cache, v_cache, block_table, ctx_lens);
-    if (st != DFA_OK) return st;
-    if (!o1 || (desc->num_flows == 2 && !o2)) return fail(DFA_ERR_NULL, "o1 (and o2 with two flows) are required");
-    if (!aligned16(o1) || (desc->num_flows == 2 && !aligned16(o2)))
-      return fail(DFA_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
-    const int32_t ns = num_splits(desc, split);
-    if (ns > 1) {
-      st = check_workspace(desc, split, workspace, ws_bytes);
-      if (st != DFA_OK) return st;
-    }
-    dfa::AttnParams p = make_params(desc, split, q1, q2, a, k_cache, v_cache, block_table, ctx_lens);
-    hipStream_t hs = static_cast<hipStream_t>(stream);
-    if (ns == 1) {
-      p.direct = 1;
-      p.o1 = o1;
-      p.o2 = desc->num_flows == 2 ? o2 : nullptr;
-      return launch_split_stage(desc, p, hs, events);
-    }
-    p.part = static_cast<float*>(workspace);
-    st = launch_split_stage(desc, p, hs, events);
-    if (st != DFA_OK) return st;
-    return launch_combine_stage(desc, split, ctx_lens, workspace, o1, o2, hs);
+    return attn_impl(desc, q1, q2, a, k_cache, v_cache, block_table, ctx_lens, 0, workspace, ws_bytes, o1, o2,
+                     static_cast<hipStream_t>(stream), events);
   } catch (...) {
     return fail(DFA_ERR_HIP, "unexpected host exception");
   }
@@ -269,7 +520,7 @@ dfa_status dfa_combine(const dfa_attn_desc* desc, const int32_t* ctx_lens, const
       return fail(DFA_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
     st = check_workspace(desc, split, workspace, ws_bytes);
     if (st != DFA_OK) return st;
-    return launch_combine_stage(desc, split, ctx_lens, workspace, o1, o2, static_cast<hipStream_t>(stream));
+    return launch_combine_stage(desc, split, ctx_lens, 0, workspace, o1, o2, static_cast<hipStream_t>(stream));
   } catch (...) {
     return fail(DFA_ERR_HIP, "unexpected host exception");
   }

@@ -35,7 +35,7 @@ struct SplitRange {
 
 template <int D>
 __device__ __forceinline__ bool split_range(const AttnParams& p, int b, int g, int s, SplitRange& r) {
-  int len = p.ctx[b];
+  int len = p.ctx[b] + p.ctx_add;
   len = len < 0 ? 0 : (len > p.max_ctx ? p.max_ctx : len);
   r.len = len;
   r.start = s * p.split_len;

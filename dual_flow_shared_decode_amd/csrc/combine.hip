@@ -21,7 +21,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
   const int b = rowid / (p.hq * p.flows);
   const int rem = rowid - b * p.hq * p.flows;
   const int h = rem / p.flows, f = rem - h * p.flows;
-  int len = p.ctx[b];
+  int len = p.ctx[b] + p.ctx_add;
   len = len < 0 ? 0 : (len > p.max_ctx ? p.max_ctx : len);
   const int ns = min((len + p.split_len - 1) / p.split_len, p.n_splits);
   const float* rec = p.part + (size_t)rowid * p.n_splits * REC;

@@ -29,6 +29,7 @@ struct AttnParams {
   int32_t split_len, n_splits;
   int64_t blk_stride;  // elements per physical block: hkv * block_size * head_dim
   float qscale;        // scale * log2(e): scores come out in base-2 units
+  int32_t ctx_add;     // added to every ctx_lens entry (1 when attending a just-appended position)
   int32_t direct;      // 1: one split per sequence; normalise and write o1/o2
   int32_t q_f32;       // Q element type is float32 (else bf16)
 };
@@ -38,7 +39,28 @@ struct CombineParams {
   const int32_t* ctx;
   float* o1;
   float* o2;
-  int32_t batch, hq, flows, split_len, n_splits, max_ctx;
+  int32_t batch, hq, flows, split_len, n_splits, max_ctx, ctx_add;
+};
+
+enum : int32_t { kEpiNone = 0, kEpiResidual = 1, kEpiSwiglu = 2, kEpiResidualCoupled = 3, kEpiKvAppend = 4 };
+
+struct GemvParams {
+  const uint16_t* w;   // tiled [n/16][k/8][16][8]
+  const uint16_t* w2;  // second matrix (SwiGLU up, KV append values) or null
+  const float* x1;     // [batch, k]
+  const float* x2;     // [batch, k] (two flows)
+  const float* couple; // [n] or null
+  const float* res1;   // [batch, n]
+  const float* res2;
+  float* y1;           // [batch, n]
+  float* y2;
+  float* part;         // [k_split][mats][m_pad][n]
+  int32_t batch, n, k, flows, cbf, m_pad, k_split, k_range, pair, x_exact, epilogue;
+  uint16_t* kv_k;      // KV append target
+  uint16_t* kv_v;
+  const int32_t* kv_table;
+  const int32_t* kv_ctx;
+  int32_t kv_hkv, kv_head_dim, kv_bs_log2, kv_max_blocks, kv_num_blocks;
 };
 
 // Optional events recorded by the runtime at the start and end of a kernel's
@@ -52,6 +74,11 @@ struct KernelEvents {
 hipError_t launch_attn_bf16(const AttnParams& p, int head_dim, int rows_padded, hipStream_t s, const KernelEvents& ev);
 hipError_t launch_attn_f32(const AttnParams& p, int head_dim, hipStream_t s, const KernelEvents& ev);
 hipError_t launch_combine(const CombineParams& p, int head_dim, hipStream_t s);
+hipError_t launch_gemv(const GemvParams& p, hipStream_t s);
+hipError_t launch_gemv_finalize(const GemvParams& p, hipStream_t s);
+hipError_t launch_pack_weight(const uint16_t* w, uint16_t* wt, int n, int k, hipStream_t s);
+size_t gemv_rows_per_workgroup();
+size_t gemv_chunk();
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s);
 size_t stream_read_threads();
 

@@ -182,6 +182,116 @@ DFA_API dfa_status dfa_decode_attn_partials(const dfa_attn_desc* desc, const voi
 DFA_API dfa_status dfa_combine(const dfa_attn_desc* desc, const int32_t* ctx_lens, const void* workspace,
                        size_t workspace_bytes, float* o1, float* o2, void* stream);
 
+/*
+ * ------------------------------------------------------------------ dual GEMV
+ * Y_f = X_f W^T for both flows f from one read of a shared weight matrix W
+ * ("Arquitetura Central": the flows share the attention, MLP and output
+ * matrices; "Custos de Inferência vs. Treinamento": decode reads the unique
+ * weights once), followed by one of the layer's epilogues. Activations and
+ * outputs are float32 [batch, k] / [batch, n], row-major; weights bf16 in the
+ * tiled layout written by dfa_pack_weight. Accumulation is float32; every
+ * activation is split into two bf16 terms (hi = bf16(x), lo = bf16(x - hi))
+ * unless x_exact_bf16 says they are exact bf16 values.
+ */
+typedef enum dfa_epilogue {
+  DFA_EPI_NONE = 0,              /* y_f = x_f W^T */
+  DFA_EPI_RESIDUAL = 1,          /* y_f = res_f + x_f W^T */
+  DFA_EPI_SWIGLU = 2,            /* z_f = silu(x_f W^T) * (x_f W2^T), silu(u) = u / (1 + e^-u);
+                                    y_1 = z_1; y_2 = z_2 + couple * z_1 (couple = b, may be NULL) */
+  DFA_EPI_RESIDUAL_COUPLED = 3,  /* m_f = x_f W^T; y_1 = res_1 + m_1;
+                                    y_2 = res_2 + m_2 + couple * m_1 (couple = c, may be NULL) */
+  DFA_EPI_KV_APPEND = 4          /* one flow (primary): k = x_1 W^T, v = x_1 W2^T with n = Hkv * D,
+                                    rounded to bf16 (nearest, ties to even) and written to position
+                                    ctx_lens[b] of sequence b in the KV cache; y1, y2 (optional)
+                                    receive k and v as float32 */
+} dfa_epilogue;
+
+typedef struct dfa_gemv_desc {
+  int32_t batch;         /* sequences = rows per flow: 1..32 (two flows), 1..64 (one flow) */
+  int32_t n;             /* output columns = rows of W, multiple of 128 */
+  int32_t k;             /* input columns = columns of W, multiple of 128 */
+  int32_t num_flows;     /* 1 (primary only) or 2 */
+  int32_t epilogue;      /* dfa_epilogue */
+  int32_t x_exact_bf16;  /* 1: every activation value is exactly a bf16 value */
+  int32_t k_split;       /* k-ranges reduced through the workspace; 0 = library choice */
+} dfa_gemv_desc;
+
+/* KV cache written by DFA_EPI_KV_APPEND (same layout as dfa_decode_attn reads). */
+typedef struct dfa_kv_target {
+  void* k_cache;                /* bf16 [num_blocks, Hkv, D/8, block_size, 8] */
+  void* v_cache;                /* bf16 [num_blocks, Hkv, block_size/16, D, 16] */
+  const int32_t* block_table;   /* int32 [batch, max_blocks_per_seq] */
+  const int32_t* ctx_lens;      /* int32 [batch]: cached positions; the new one goes at ctx_lens[b] */
+  int32_t num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks;
+} dfa_kv_target;
+
+/* Workspace bytes of dfa_dual_gemv for `desc` (0 if invalid). */
+DFA_API size_t dfa_dual_gemv_workspace_size(const dfa_gemv_desc* desc);
+
+/*
+ * Runs the GEMV and its epilogue on `stream` (two launches). Required
+ * pointers: w, x1, y1 (y1/y2 optional for KV_APPEND), x2 and y2 with two
+ * flows, w2 for SWIGLU and KV_APPEND, res1 (res2 with two flows) for the
+ * residual epilogues, kv for KV_APPEND. couple may be NULL. The auxiliary
+ * flow's inputs (x2, res2, couple) never affect y1 or the KV cache.
+ */
+DFA_API dfa_status dfa_dual_gemv(const dfa_gemv_desc* desc, const uint16_t* w, const uint16_t* w2,
+                                 const float* x1, const float* x2, const float* couple, const float* res1,
+                                 const float* res2, float* y1, float* y2, const dfa_kv_target* kv,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Repacks a row-major bf16 weight [n, k] (nn.Linear layout) into the tiled
+ * layout of dfa_dual_gemv: element (r, c) goes to
+ *     ((r / 16) * (k / 8) + c / 8) * 128 + (r % 16) * 8 + c % 8.
+ * n multiple of 16, k multiple of 8; w and w_tiled must not overlap.
+ */
+DFA_API dfa_status dfa_pack_weight(const uint16_t* w, uint16_t* w_tiled, int32_t n, int32_t k, void* stream);
+
+/*
+ * ------------------------------------------------------------ decode layer
+ * One decode step of a whole dual-flow layer ("Arquitetura Central",
+ * "Mecanismos Chave"), for every sequence b at its new position L = ctx_lens[b]:
+ *     q_f = x_f Wq^T (both flows; x2 comes from the auxiliary flow's embedding)
+ *     k, v = x_1 Wk^T, x_1 Wv^T -> bf16 -> KV cache position L   (primary only)
+ *     o_f = dual-flow attention over positions [0, L] (dfa_decode_attn, with a)
+ *     h_f = x_f + o_f Wo^T
+ *     z_1 = silu(h_1 Wg^T) * (h_1 Wu^T),  z_2 = silu(h_2 Wg^T) * (h_2 Wu^T) + b * z_1
+ *     out_1 = h_1 + z_1 Wd^T,             out_2 = h_2 + z_2 Wd^T + c * (z_1 Wd^T)
+ * Eleven launches on `stream`, each weight read once for both flows. The
+ * caller advances ctx_lens afterwards. Requirements: those of dfa_decode_attn
+ * (max_ctx_len >= every ctx_lens[b] + 1) and of dfa_dual_gemv (batch <= 32;
+ * hidden, mlp, num_q_heads * head_dim and num_kv_heads * head_dim multiples
+ * of 128). x1, x2, out1, out2: float32 [batch, hidden]. The auxiliary flow's
+ * inputs (x2, a, b, c) never affect out1 or the cache.
+ */
+typedef struct dfa_layer_desc {
+  int32_t batch, hidden, num_q_heads, num_kv_heads, head_dim, mlp;
+  int32_t block_size, max_blocks_per_seq, num_blocks, max_ctx_len;
+  float scale;
+  int32_t x_exact_bf16;  /* 1: x1 and x2 hold exact bf16 values */
+} dfa_layer_desc;
+
+typedef struct dfa_layer_weights {
+  const uint16_t* wq;      /* [num_q_heads * head_dim, hidden], tiled (dfa_pack_weight) */
+  const uint16_t* wk;      /* [num_kv_heads * head_dim, hidden], tiled */
+  const uint16_t* wv;      /* [num_kv_heads * head_dim, hidden], tiled */
+  const uint16_t* wo;      /* [hidden, num_q_heads * head_dim], tiled */
+  const uint16_t* w_gate;  /* [mlp, hidden], tiled */
+  const uint16_t* w_up;    /* [mlp, hidden], tiled */
+  const uint16_t* w_down;  /* [hidden, mlp], tiled */
+  const float* a;          /* [num_q_heads * head_dim] query coupling */
+  const float* b;          /* [mlp] MLP-intermediate coupling (NULL = 0) */
+  const float* c;          /* [hidden] MLP-output coupling (NULL = 0) */
+} dfa_layer_weights;
+
+DFA_API size_t dfa_decode_layer_workspace_size(const dfa_layer_desc* desc);
+
+DFA_API dfa_status dfa_decode_layer(const dfa_layer_desc* desc, const dfa_layer_weights* weights,
+                                    const float* x1, const float* x2, void* k_cache, void* v_cache,
+                                    const int32_t* block_table, const int32_t* ctx_lens, float* out1,
+                                    float* out2, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Short fixed description of a status code. Never NULL. */
 DFA_API const char* dfa_status_string(dfa_status status);
 

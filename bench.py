@@ -115,12 +115,84 @@ def cpu_baseline(case, budget_s: float):
             "host_cpus": len(os.sched_getaffinity(0))}
 
 
+def layer_bytes(cfg):
+    """Bytes one layer step must move: every weight once, the cache (ctx + 1 positions) once, the
+    appended key/value, and the float32 activations in and out of each stage."""
+    import workloads as W
+    w = 2 * sum(a * b for a, b in W.weight_shapes(cfg).values())
+    kv_read = cfg.batch * (cfg.ctx + 1) * cfg.num_kv_heads * cfg.head_dim * 2 * 2
+    kv_write = cfg.batch * cfg.num_kv_heads * cfg.head_dim * 2 * 2
+    qd = cfg.num_q_heads * cfg.head_dim
+    act = 4 * cfg.batch * 2 * (cfg.hidden + qd + qd + qd + cfg.hidden + cfg.hidden + cfg.mlp + cfg.mlp + cfg.hidden)
+    return w + kv_read + kv_write + act
+
+
+def bench_layer(args):
+    """One dfa_decode_layer step of the full-layer workload (batch 32, hidden 4096, 32/8 heads of 128,
+    SwiGLU MLP 14336, 4096 cached positions)."""
+    import torch
+
+    import dual_flow_shared_decode_amd as dfa
+    import workloads as W
+    from workloads.device import to_device
+
+    cfg = W.C5
+    log("generating c5 inputs")
+    case = W.make_layer_case(cfg, W.SEEDS["c5"], pad_nan=False)
+    packed = {}
+    for name, w in case.w.items():
+        dev = to_device(w)
+        packed[name] = torch.empty_like(dev)
+        dfa.dfa_pack_weight(dev, packed[name], w.shape[0], w.shape[1])
+        del dev
+    dev = {k: to_device(getattr(case, k)) for k in ("x1", "x2", "a", "b", "c", "k_cache", "v_cache", "block_table",
+                                                    "ctx_lens")}
+    desc = dfa.LayerDesc(batch=cfg.batch, hidden=cfg.hidden, num_q_heads=cfg.num_q_heads,
+                         num_kv_heads=cfg.num_kv_heads, head_dim=cfg.head_dim, mlp=cfg.mlp,
+                         block_size=case.block_size, max_blocks_per_seq=case.max_blocks_per_seq,
+                         num_blocks=case.k_cache.shape[0], max_ctx_len=cfg.ctx + 1, scale=cfg.scale,
+                         x_exact_bf16=1)
+    wts = dfa.layer_weights(packed["wq"], packed["wk"], packed["wv"], packed["wo"], packed["wg"], packed["wu"],
+                            packed["wd"], dev["a"], dev["b"], dev["c"])
+    ws = torch.empty(dfa.dfa_decode_layer_workspace_size(desc) // 4 + 64, dtype=torch.float32, device="cuda")
+    out1 = torch.empty((cfg.batch, cfg.hidden), device="cuda")
+    out2 = torch.empty_like(out1)
+    stream = torch.cuda.current_stream()
+
+    def step():  # the cache slot at ctx_lens is rewritten with the same values every step
+        dfa.dfa_decode_layer(desc, wts, dev["x1"], dev["x2"], dev["k_cache"], dev["v_cache"], dev["block_table"],
+                             dev["ctx_lens"], out1, out2, ws, stream)
+    for _ in range(args.warmup):
+        step()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    nbytes = layer_bytes(cfg)
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    log(f"layer step {ms * 1e3:.1f} us, {nbytes / 1e6:.0f} MB -> {gbps:.0f} GB/s")
+    print(json.dumps({"metric": "dual-flow decode layer step: tokens/s (both flows) + achieved HBM GB/s vs peak",
+                      "value": 2 * cfg.batch / (ms * 1e-3), "unit": "tokens/s (both flows)", "n_gpus": 1,
+                      "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+                      "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+                      "config": {"workload": "c5: one dual-flow decode layer step, batch 32, hidden 4096, 32/8 heads "
+                                             "of 128, SwiGLU MLP 14336, 4096 cached positions",
+                                 "batch": cfg.batch},
+                      "achieved_gbps": gbps, "hbm_peak_gbps": HBM_PEAK_GBPS, "frac_of_peak": gbps / HBM_PEAK_GBPS,
+                      "algorithmic_bytes_per_step": nbytes}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="c2", choices=["c2", "c3", "c4"])
+    ap.add_argument("--config", default="c2", choices=["c2", "c3", "c4", "c5"],
+                    help="c2 (default): the attention workload the metric is quoted on; c5: a whole layer step")
     ap.add_argument("--split", type=int, default=0, help="positions per split (0: library choice)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -142,6 +214,9 @@ def main():
     from workloads.device import upload_attn_case
 
     torch.cuda.set_device(0)
+    if args.config == "c5":
+        bench_layer(args)
+        return
     cfg = W.ATTN_CONFIGS[args.config]
     log(f"generating {cfg.name} inputs")
     case = W.make_attn_case(cfg, W.SEEDS[cfg.name], pad_nan=False)

@@ -100,7 +100,7 @@ def lib() -> ctypes.CDLL:
             "dfa_decode_attn_timed": (ctypes.c_int, [D, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P, _P, _P,
                                                      ctypes.POINTER(KernelEvents)]),
             "dfa_decode_attn_partials": (ctypes.c_int, [D, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
-            "dfa_combine": (ctypes.c_int, [D, _P, _P, ctypes.c_size_t, _P, _P, _P]),
+            "dfa_combine": (ctypes.c_int, [D, _P, ctypes.c_size_t, _P, _P, _P]),
             "dfa_dual_gemv_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(GemvDesc)]),
             "dfa_dual_gemv": (ctypes.c_int, [ctypes.POINTER(GemvDesc), _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                              ctypes.POINTER(KvTarget), _P, ctypes.c_size_t, _P]),
@@ -198,9 +198,9 @@ def dfa_decode_attn_partials(desc, q1, q2, a, k_cache, v_cache, block_table, ctx
                                           _ptr(workspace), ws_bytes, _stream(stream)))
 
 
-def dfa_combine(desc, ctx_lens, workspace, o1, o2, stream=None):
+def dfa_combine(desc, workspace, o1, o2, stream=None):
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().dfa_combine(ctypes.byref(desc), _ptr(ctx_lens), _ptr(workspace), ws_bytes, _ptr(o1),
+    _check(lib().dfa_combine(ctypes.byref(desc), _ptr(workspace), ws_bytes, _ptr(o1),
                              _ptr(o2), _stream(stream)))
 
 

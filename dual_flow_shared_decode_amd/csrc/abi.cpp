@@ -28,18 +28,21 @@ int log2i(int64_t x) {
   return r;
 }
 
-// Positions per split chosen by the library (measured on MI355X, 256 CUs): a
-// single split per sequence when there are at least 128 (sequence, kv head)
-// pairs -- one workgroup per pair then streams at full rate, and the combine
-// launch would cost more than the extra parallelism gains; otherwise splits of
-// at least 2048 positions, enough of them for about 512 workgroups.
+// Positions per split chosen by the library (measured on MI355X, 256 CUs): one
+// workgroup per compute unit is what streams the cache at full rate -- 128
+// workgroups reach about 6 TB/s of plain reads, 256 about 6.7 -- while more
+// splits add records and combine traffic. So a single split per sequence when
+// there are at least 256 (sequence, kv head) pairs (ragged lengths included:
+// splitting them measured slower), else enough splits for about 256
+// workgroups, of at least 512 positions each.
 int64_t auto_split_len(const dfa_attn_desc* d) {
   const int64_t pairs = int64_t(d->batch) * d->num_kv_heads;
-  if (pairs >= 128) return (int64_t(d->max_ctx_len) + 31) / 32 * 32;
-  const int64_t want = (512 + pairs - 1) / pairs;
-  int64_t len = (int64_t(d->max_ctx_len) + want - 1) / want;
-  len = (len + 127) / 128 * 128;
-  return std::max<int64_t>(len, 2048);
+  const int64_t whole = (int64_t(d->max_ctx_len) + 31) / 32 * 32;
+  if (pairs >= 256) return whole;
+  const int64_t splits = (256 + pairs - 1) / pairs;
+  int64_t len = (int64_t(d->max_ctx_len) + splits - 1) / splits;
+  len = std::max<int64_t>((len + 255) / 256 * 256, 512);
+  return std::min(len, whole);
 }
 
 dfa_status validate_attn(const dfa_attn_desc* d, int32_t* split_out) {
@@ -148,20 +151,16 @@ dfa_status launch_split_stage(const dfa_attn_desc* d, const dfa::AttnParams& p, 
   return DFA_OK;
 }
 
-dfa_status launch_combine_stage(const dfa_attn_desc* d, int32_t split, const int32_t* ctx, int32_t ctx_add,
-                                const void* ws, float* o1, float* o2, hipStream_t st) {
+dfa_status launch_combine_stage(const dfa_attn_desc* d, int32_t split, const void* ws, float* o1, float* o2,
+                                hipStream_t st) {
   dfa::CombineParams c{};
-  c.ctx_add = ctx_add;
   c.part = static_cast<const float*>(ws);
-  c.ctx = ctx;
   c.o1 = o1;
   c.o2 = d->num_flows == 2 ? o2 : nullptr;
   c.batch = d->batch;
   c.hq = d->num_q_heads;
   c.flows = d->num_flows;
-  c.split_len = split;
   c.n_splits = num_splits(d, split);
-  c.max_ctx = d->max_ctx_len;
   const hipError_t e = dfa::launch_combine(c, d->head_dim, st);
   if (e != hipSuccess) return fail(DFA_ERR_HIP, std::string("combine launch: ") + hipGetErrorString(e));
   return DFA_OK;
@@ -202,7 +201,7 @@ dfa_status attn_impl(const dfa_attn_desc* desc, const void* q1, const void* q2, 
   p.part = static_cast<float*>(workspace);
   st = launch_split_stage(desc, p, hs, events);
   if (st != DFA_OK) return st;
-  return launch_combine_stage(desc, split, ctx_lens, ctx_add, workspace, o1, o2, hs);
+  return launch_combine_stage(desc, split, workspace, o1, o2, hs);
 }
 
 // ------------------------------------------------------------------ dual GEMV
@@ -508,19 +507,19 @@ dfa_status dfa_decode_attn_partials(const dfa_attn_desc* desc, const void* q1, c
   }
 }
 
-dfa_status dfa_combine(const dfa_attn_desc* desc, const int32_t* ctx_lens, const void* workspace,
-                       size_t ws_bytes, float* o1, float* o2, void* stream) {
+dfa_status dfa_combine(const dfa_attn_desc* desc, const void* workspace, size_t ws_bytes, float* o1, float* o2,
+                       void* stream) {
   try {
     int32_t split = 0;
     dfa_status st = validate_attn(desc, &split);
     if (st != DFA_OK) return st;
-    if (!ctx_lens || !o1 || (desc->num_flows == 2 && !o2))
-      return fail(DFA_ERR_NULL, "ctx_lens, o1 (and o2 with two flows) are required");
-    if (!aligned16(ctx_lens) || !aligned16(o1) || (desc->num_flows == 2 && !aligned16(o2)))
+    if (!o1 || (desc->num_flows == 2 && !o2))
+      return fail(DFA_ERR_NULL, "o1 (and o2 with two flows) are required");
+    if (!aligned16(o1) || (desc->num_flows == 2 && !aligned16(o2)))
       return fail(DFA_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
     st = check_workspace(desc, split, workspace, ws_bytes);
     if (st != DFA_OK) return st;
-    return launch_combine_stage(desc, split, ctx_lens, 0, workspace, o1, o2, static_cast<hipStream_t>(stream));
+    return launch_combine_stage(desc, split, workspace, o1, o2, static_cast<hipStream_t>(stream));
   } catch (...) {
     return fail(DFA_ERR_HIP, "unexpected host exception");
   }

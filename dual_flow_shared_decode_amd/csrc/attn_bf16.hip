@@ -9,11 +9,12 @@
 // and each keeps its own online-softmax state; a merge in LDS ends the
 // workgroup.
 //
-// Cache layout (see include/dfa.h): keys [block][kv head][D/8][position][8],
-// values [block][kv head][position/16][D][16]. A chunk is 32 positions = two
-// 16-position tiles; every load of a tile reads whole 128-byte lines
-// (keys: 4 runs of 256 B, values: 512 B), so the cache is streamed with
-// non-temporal loads: each byte is read once and need not stay in L2.
+// Cache layout (see include/dfa.h): keys [block][kv head][position/16][D/8][16][8],
+// values [block][kv head][position/16][D][16]: a 16-position tile of either is
+// one contiguous run of 16*D elements. A chunk is 32 positions = two tiles;
+// every load instruction reads whole 128-byte lines (keys: 1 KB, values:
+// 512 B), so the cache is streamed with non-temporal loads: each byte is read
+// once and need not stay in L2.
 //
 // Per tile, on the matrix cores (lane l owns column n = l % 16 and k-group
 // grp = l / 16 of each operand; result (m = 4*grp + i, n) is lane l, register i):
@@ -77,11 +78,11 @@ __device__ __forceinline__ void load_chunk(const AttnParams& p, const uint16_t* 
     const int tt = tile_start(t0, u, end);
     const size_t blk = (size_t)tbl[(tt >> p.bs_log2) - jb0] * p.blk_stride;
     const int pos = tt & bs_mask;
-    const uint16_t* ka = kc + blk + ((size_t)grp << (p.bs_log2 + 3)) + (pos + n) * 8;
+    const uint16_t* ka = kc + blk + (size_t)(pos >> 4) * (D * 16) + (grp * 16 + n) * 8;
     const uint16_t* va = vc + blk + (size_t)(pos >> 4) * (D * 16) + n * 16 + 4 * grp;
 #pragma unroll
     for (int st = 0; st < D / 32; ++st)
-      ch.k[u][st] = __builtin_nontemporal_load((const bf16x8*)(ka + ((size_t)(4 * st) << (p.bs_log2 + 3))));
+      ch.k[u][st] = __builtin_nontemporal_load((const bf16x8*)(ka + 4 * st * 16 * 8));
 #pragma unroll
     for (int db = 0; db < D / 16; ++db)
       ch.v[u][db] = __builtin_nontemporal_load((const bf16x4*)(va + 16 * 16 * db));

@@ -27,8 +27,10 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // Positions [start, end) handled by workgroup (split s, sequence b); returns
-// false when the workgroup has nothing to do. Writes zero outputs for an empty
-// sequence in direct mode (split 0 only).
+// false when the split holds no position of the sequence. Such a workgroup
+// still writes its result: zero outputs in direct mode (an empty sequence),
+// else the empty record (O = 0, m = -inf, l = 0) of each row, so that every
+// record the combine reads is written by the same call.
 struct SplitRange {
   int start, end, len;
 };
@@ -40,19 +42,24 @@ __device__ __forceinline__ bool split_range(const AttnParams& p, int b, int g, i
   r.len = len;
   r.start = s * p.split_len;
   r.end = min(r.start + p.split_len, len);
-  if (len == 0) {
-    if (p.direct && s == 0) {
-      const int nr = p.flows * p.group;
-      for (int idx = threadIdx.x; idx < nr * D; idx += kThreads) {
-        const int row = idx / D, d = idx - row * D;
-        const int f = row / p.group, h = g * p.group + (row - f * p.group);
-        float* out = f ? p.o2 : p.o1;
-        out[((size_t)b * p.hq + h) * D + d] = 0.f;
-      }
+  if (r.start < len) return true;
+  const int nr = p.flows * p.group;
+  if (p.direct) {
+    for (int idx = threadIdx.x; idx < nr * D; idx += kThreads) {
+      const int row = idx / D, d = idx - row * D;
+      const int f = row / p.group, h = g * p.group + (row - f * p.group);
+      float* out = f ? p.o2 : p.o1;
+      out[((size_t)b * p.hq + h) * D + d] = 0.f;
     }
-    return false;
+  } else {
+    for (int idx = threadIdx.x; idx < nr * (D + 2); idx += kThreads) {
+      const int row = idx / (D + 2), d = idx - row * (D + 2);
+      const int f = row / p.group, h = g * p.group + (row - f * p.group);
+      float* rec = p.part + ((((size_t)b * p.hq + h) * p.flows + f) * p.n_splits + s) * (D + kRecPad);
+      rec[d] = d == D ? -INFINITY : 0.f;
+    }
   }
-  return r.start < len;
+  return false;
 }
 
 // Stages the physical block ids of the split's positions into LDS, clamped to

@@ -61,13 +61,14 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnParams p) {
     const int t0 = r.start + 64 * c;
     const int t = t0 + lane;
     const int tc = min(t, r.end - 1);
-    // key of position tc: dims 8j..8j+7 are 8 contiguous floats in group j
-    const float* kr = kc + (size_t)tbl[(tc >> p.bs_log2) - jb0] * p.blk_stride + (size_t)(tc & bs_mask) * 8;
+    // key of position tc: tile tc/16, then dims 8j..8j+7 are 8 contiguous floats in group j
+    const int kp = tc & bs_mask;
+    const float* kr = kc + (size_t)tbl[(tc >> p.bs_log2) - jb0] * p.blk_stride + (size_t)(kp >> 4) * (D * 16) + (kp & 15) * 8;
     float sc[kMaxRows];
 #pragma unroll
     for (int i = 0; i < kMaxRows; ++i) sc[i] = 0.f;
     for (int d4 = 0; d4 < D / 4; ++d4) {
-      const float4 kv = *(const float4*)(kr + ((size_t)(d4 >> 1) << (p.bs_log2 + 3)) + 4 * (d4 & 1));
+      const float4 kv = *(const float4*)(kr + (d4 >> 1) * 128 + 4 * (d4 & 1));
 #pragma unroll
       for (int i = 0; i < kMaxRows; ++i) {
         if (i < nr) {

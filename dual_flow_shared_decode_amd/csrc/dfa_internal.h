@@ -36,10 +36,9 @@ struct AttnParams {
 
 struct CombineParams {
   const float* part;
-  const int32_t* ctx;
   float* o1;
   float* o2;
-  int32_t batch, hq, flows, split_len, n_splits, max_ctx, ctx_add;
+  int32_t batch, hq, flows, n_splits;
 };
 
 enum : int32_t { kEpiNone = 0, kEpiResidual = 1, kEpiSwiglu = 2, kEpiResidualCoupled = 3, kEpiKvAppend = 4 };

@@ -242,8 +242,9 @@ __global__ __launch_bounds__(256) void gemv_finalize_kernel(GemvParams p) {
       blk = blk < 0 ? 0 : (blk >= p.kv_num_blocks ? p.kv_num_blocks - 1 : blk);
       const int g = n / p.kv_head_dim, d = n - g * p.kv_head_dim, slot = pos & (bs - 1);
       const size_t head = (size_t)blk * p.kv_hkv * p.kv_head_dim * bs + (size_t)g * p.kv_head_dim * bs;
-      // keys [D/8][bs][8], values [bs/16][D][16] inside a block and kv head
-      p.kv_k[head + (size_t)(d >> 3) * bs * 8 + (size_t)slot * 8 + (d & 7)] = bf16_rne(y[0][0]);
+      // keys [bs/16][D/8][16][8], values [bs/16][D][16] inside a block and kv head
+      p.kv_k[head + (size_t)(slot >> 4) * p.kv_head_dim * 16 + (size_t)(d >> 3) * 128 + (slot & 15) * 8 + (d & 7)] =
+          bf16_rne(y[0][0]);
       p.kv_v[head + (size_t)(slot >> 4) * p.kv_head_dim * 16 + (size_t)d * 16 + (slot & 15)] = bf16_rne(y[0][1]);
       break;
     }

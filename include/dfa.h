@@ -37,9 +37,11 @@
  * Layouts (row-major, innermost last):
  *  - Q1, Q2, O1, O2:   [batch, num_q_heads, head_dim]
  *  - a:                [num_q_heads * head_dim] float32
- *  - K cache:          [num_blocks, num_kv_heads, head_dim / 8, block_size, 8]
- *                      (keys in groups of 8 dimensions; within a group the
- *                      block's positions are contiguous, 8 elements each)
+ *  - K cache:          [num_blocks, num_kv_heads, block_size / 16,
+ *                       head_dim / 8, 16, 8]
+ *                      (keys in tiles of 16 positions; inside a tile, groups
+ *                      of 8 dimensions, each holding the 16 positions' 8
+ *                      elements: a tile is 16 * head_dim contiguous elements)
  *  - V cache:          [num_blocks, num_kv_heads, block_size / 16, head_dim, 16]
  *                      (values transposed inside tiles of 16 positions: for a
  *                      tile and a dimension, the 16 positions are contiguous)
@@ -162,8 +164,9 @@ DFA_API dfa_status dfa_decode_attn_timed(const dfa_attn_desc* desc, const void* 
  *     (((b * num_q_heads + h) * num_flows + f) * num_splits + s) * (head_dim + 4)
  * and holds head_dim floats of unnormalised output sum_t 2^(u_t - m) V_t, then
  * m = max_t u_t and l = sum_t 2^(u_t - m), with u_t = scale * log2(e) * <q, K_t>
- * over the split's positions, then two unused floats. Splits past the end of
- * a sequence are not written. With dfa_combine this is the same computation
+ * over the split's positions, then two unused floats. A split past the end of
+ * its sequence gets the empty record (O = 0, m = -inf, l = 0), so every
+ * record is written. With dfa_combine this is the same computation
  * as dfa_decode_attn; the records also let a caller merge splits computed
  * elsewhere (for example other devices holding other positions).
  */
@@ -174,13 +177,15 @@ DFA_API dfa_status dfa_decode_attn_partials(const dfa_attn_desc* desc, const voi
 
 /*
  * Log-sum-exp combine of the partial records in `workspace` (layout above)
- * into the normalised outputs: with M = max_s m_s over the
- * ceil(ctx_lens[b] / split_len) splits of sequence b,
+ * into the normalised outputs: with M = max_s m_s over the num_splits
+ * records of a row,
  *     O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
- * A sequence with ctx_lens[b] <= 0 gets zero outputs.
+ * Empty records add nothing; a row whose records are all empty (a sequence
+ * with no position) gets zero outputs. Every record must have been written
+ * (dfa_decode_attn_partials writes all of them).
  */
-DFA_API dfa_status dfa_combine(const dfa_attn_desc* desc, const int32_t* ctx_lens, const void* workspace,
-                       size_t workspace_bytes, float* o1, float* o2, void* stream);
+DFA_API dfa_status dfa_combine(const dfa_attn_desc* desc, const void* workspace, size_t workspace_bytes,
+                               float* o1, float* o2, void* stream);
 
 /*
  * ------------------------------------------------------------------ dual GEMV
@@ -218,7 +223,7 @@ typedef struct dfa_gemv_desc {
 
 /* KV cache written by DFA_EPI_KV_APPEND (same layout as dfa_decode_attn reads). */
 typedef struct dfa_kv_target {
-  void* k_cache;                /* bf16 [num_blocks, Hkv, D/8, block_size, 8] */
+  void* k_cache;                /* bf16 [num_blocks, Hkv, block_size/16, D/8, 16, 8] */
   void* v_cache;                /* bf16 [num_blocks, Hkv, block_size/16, D, 16] */
   const int32_t* block_table;   /* int32 [batch, max_blocks_per_seq] */
   const int32_t* ctx_lens;      /* int32 [batch]: cached positions; the new one goes at ctx_lens[b] */

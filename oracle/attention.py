@@ -17,10 +17,10 @@ query head h and flow f in {1, 2}, with g the kv head of h and L_b = ctx_lens[b]
 
 Decode attends every cached position of the sequence (the new token is the
 last one), so no causal mask is needed beyond the length. Cache layout: keys
-[num_blocks, Hkv, D/8, block, 8] (8-dimension groups, positions contiguous in a
-group); values [num_blocks, Hkv, block/16, D, 16] (transposed inside tiles of 16
-positions); position t of sequence b is in block table[b, t // block], slot
-t % block.
+[num_blocks, Hkv, block/16, D/8, 16, 8] (tiles of 16 positions, inside a tile
+8-dimension groups of the 16 positions); values [num_blocks, Hkv, block/16, D,
+16] (transposed inside tiles of 16 positions); position t of sequence b is in
+block table[b, t // block], slot t % block.
 """
 from typing import Dict, Iterable, Optional, Tuple
 
@@ -51,8 +51,8 @@ def block_rows(table_row: np.ndarray, length: int, block_size: int) -> np.ndarra
 def gather_keys(k_cache, table_row, length: int, g: int, block_size: int, dtype: str) -> np.ndarray:
     """Keys of positions [0, length) of one sequence and kv head, as float64 [length, D]."""
     blocks = block_rows(table_row, length, block_size)
-    k = np.swapaxes(k_cache[blocks, g], 1, 2)  # [nblk, D/8, block, 8] -> [nblk, block, D/8, 8]
-    return to_f64(k.reshape(-1, k.shape[2] * k.shape[3])[:length], dtype)
+    k = np.swapaxes(k_cache[blocks, g], 2, 3)  # [nblk, block/16, D/8, 16, 8] -> [nblk, block/16, 16, D/8, 8]
+    return to_f64(k.reshape(-1, k.shape[3] * k.shape[4])[:length], dtype)
 
 
 def gather_values(v_cache, table_row, length: int, g: int, block_size: int, dtype: str) -> np.ndarray:

@@ -38,7 +38,7 @@ def _kv_rows(k_cache, v_cache, table_row, length, g, block, kv_dtype):
     for t in range(length):
         blk = int(table_row[t // block])
         slot = t - (t // block) * block
-        keys.append([_val(k_cache[blk, g, j // 8, slot, j % 8], kv_dtype) for j in range(d)])
+        keys.append([_val(k_cache[blk, g, slot // 16, j // 8, slot % 16, j % 8], kv_dtype) for j in range(d)])
         values.append([_val(v_cache[blk, g, slot // 16, j, slot % 16], kv_dtype) for j in range(d)])
     return keys, values
 

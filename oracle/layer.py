@@ -62,7 +62,7 @@ def append_kv(k_cache, v_cache, block_table, ctx_lens, k_bits, v_bits, block_siz
         if blk < 0:
             raise ValueError("no cache block for the appended position")
         slot = pos % block_size
-        k_new[blk, :, :, slot, :] = k_bits[b].reshape(k_bits.shape[1], -1, 8)
+        k_new[blk, :, slot // 16, :, slot % 16, :] = k_bits[b].reshape(k_bits.shape[1], -1, 8)
         v_new[blk, :, slot // 16, :, slot % 16] = v_bits[b]
     return k_new, v_new
 

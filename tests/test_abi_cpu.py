@@ -48,10 +48,13 @@ def test_split_plan_and_workspace_size():
     ns = dfa.dfa_decode_attn_num_splits(d)
     assert split % 32 == 0 and ns == -(-4096 // split)
     assert dfa.dfa_decode_attn_workspace_size(d) == 16 * 32 * 2 * ns * (128 + 4) * 4
-    # 128 (sequence, kv head) pairs: one split each; 32 pairs of 131072: splits of >= 2048 positions
-    assert ns == 1
+    # about 256 workgroups: 128 (sequence, kv head) pairs take 2 splits, 32 pairs 8, 256 pairs 1
+    assert ns == 2 and split == 2048
     d4 = c2_desc(batch=4, block_size=131072, max_ctx_len=131072)
-    assert dfa.dfa_decode_attn_split_len(d4) >= 2048 and dfa.dfa_decode_attn_num_splits(d4) >= 8
+    assert dfa.dfa_decode_attn_split_len(d4) == 16384 and dfa.dfa_decode_attn_num_splits(d4) == 8
+    assert dfa.dfa_decode_attn_num_splits(c2_desc(batch=32)) == 1
+    # short contexts: splits never go below 512 positions
+    assert dfa.dfa_decode_attn_split_len(c2_desc(batch=1, block_size=1024, max_ctx_len=1000)) == 512
     d1 = c2_desc(split_len=4096)
     assert dfa.dfa_decode_attn_num_splits(d1) == 1
     assert dfa.dfa_decode_attn_split_len(c2_desc(split_len=96)) == 96
@@ -120,7 +123,7 @@ def test_workspace_and_alignment_errors():
             _call_attn(d, ws_bytes=need - 4, **{name: FAKE + 4})
         assert _lib.STATUS[e.value.status] == "DFA_ERR_ALIGNMENT", name
     with pytest.raises(dfa.DfaError) as e:
-        _lib._check(_lib.lib().dfa_combine(ctypes.byref(d), FAKE, FAKE, need - 4, FAKE, FAKE, None))
+        _lib._check(_lib.lib().dfa_combine(ctypes.byref(d), FAKE, need - 4, FAKE, FAKE, None))
     assert _lib.STATUS[e.value.status] == "DFA_ERR_WORKSPACE"
     with pytest.raises(dfa.DfaError) as e:
         _lib._check(_lib.lib().dfa_decode_attn_partials(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,

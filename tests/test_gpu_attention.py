@@ -194,7 +194,7 @@ def test_partials_then_combine_equals_decode_attn():
     p2 = torch.full_like(p1, float("nan"))
     dfa.dfa_decode_attn_partials(d, t["q1"], t["q2"], t["a"], t["k_cache"], t["v_cache"], t["block_table"],
                                  t["ctx_lens"], ws)
-    dfa.dfa_combine(d, t["ctx_lens"], ws, p1, p2)
+    dfa.dfa_combine(d, ws, p1, p2)
     torch.cuda.synchronize()
     # the same splits and merge; a one-split sequence is normalised as o / l by the fused
     # kernel and as o * (1 / l) by dfa_combine, so allow rounding

@@ -71,13 +71,14 @@ def test_append_writes_only_the_new_primary_slot():
     case = W.make_layer_case(TINY, 25)
     got = run(case)
     bs = case.block_size
-    changed_k = np.argwhere(np.any(got["k_cache"] != case.k_cache, axis=(2, 4)))  # [blk, g, slot]
+    changed_k = np.argwhere(np.any(got["k_cache"] != case.k_cache, axis=(3, 5)))  # [blk, g, tile, s]
     expect = sorted((int(case.block_table[b, case.ctx_lens[b] // bs]), g, int(case.ctx_lens[b] % bs))
                     for b in range(TINY.batch) for g in range(TINY.num_kv_heads))
-    assert sorted(map(tuple, changed_k.tolist())) == expect
+    assert sorted((int(i), int(g), int(t) * 16 + int(s)) for i, g, t, s in changed_k) == expect
     for b in range(TINY.batch):
         blk, slot = case.block_table[b, case.ctx_lens[b] // bs], case.ctx_lens[b] % bs
-        assert np.array_equal(got["k_cache"][blk, :, :, slot, :].reshape(TINY.num_kv_heads, -1), got["k1_bits"][b])
+        assert np.array_equal(got["k_cache"][blk, :, slot // 16, :, slot % 16, :].reshape(TINY.num_kv_heads, -1),
+                              got["k1_bits"][b])
         assert np.array_equal(got["v_cache"][blk, :, slot // 16, :, slot % 16], got["v1_bits"][b])
     changed_v = np.argwhere(np.any(got["v_cache"] != case.v_cache, axis=3))  # [blk, g, tile, s]
     assert sorted((int(i), int(g), int(t) * 16 + int(s)) for i, g, t, s in changed_v) == expect

@@ -50,7 +50,7 @@ def test_logical_rows_land_where_the_table_says():
     k_rows, v_rows = W.kv_rows(9, b, g, int(case.ctx_lens[b]), cfg.head_dim, "bf16")
     for t in range(int(case.ctx_lens[b])):
         blk = case.block_table[b, t // 16]
-        assert np.array_equal(case.k_cache[blk, g, :, t % 16, :].reshape(-1), k_rows[t])
+        assert np.array_equal(case.k_cache[blk, g, 0, :, t % 16, :].reshape(-1), k_rows[t])
         assert np.array_equal(case.v_cache[blk, g, 0, :, t % 16], v_rows[t])
 
 
@@ -70,7 +70,7 @@ def test_permute_blocks_is_layout_only():
     for b in range(3):
         for t in range(int(case.ctx_lens[b])):
             j, s = divmod(t, 16)
-            assert np.array_equal(case.k_cache[case.block_table[b, j], :, :, s], k2[t2[b, j], :, :, s])
+            assert np.array_equal(case.k_cache[case.block_table[b, j], :, 0, :, s], k2[t2[b, j], :, 0, :, s])
             assert np.array_equal(case.v_cache[case.block_table[b, j], :, 0, :, s], v2[t2[b, j], :, 0, :, s])
 
 
@@ -80,4 +80,4 @@ def test_layer_case_shapes():
     assert case.w["wq"].shape == (64, 64) and case.w["wk"].shape == (32, 64)
     assert case.w["wd"].shape == (64, 96)
     assert np.array_equal(W.bf16_bits_to_f32(W.f32_to_bf16_bits(case.x1)), case.x1)
-    assert case.k_cache.shape == (2, 2, 2, 32, 8) and case.v_cache.shape == (2, 2, 2, 16, 16)
+    assert case.k_cache.shape == (2, 2, 2, 2, 16, 8) and case.v_cache.shape == (2, 2, 2, 16, 16)

@@ -9,9 +9,10 @@ from ``[seed, tag, b, g]``, so any chunk can be regenerated on its own.
 
 Cache layout (one layer), shared by every consumer:
 
-* ``k_cache``: ``[num_blocks, num_kv_heads, head_dim // 8, block_size, 8]`` --
-  keys in groups of 8 dimensions; within a group, the block's positions are
-  contiguous (8 elements each).
+* ``k_cache``: ``[num_blocks, num_kv_heads, block_size // 16, head_dim // 8, 16, 8]``
+  -- keys in tiles of 16 positions; inside a tile, groups of 8 dimensions, and
+  inside a group the 16 positions' 8 elements each (a tile is one contiguous
+  run of 16 * head_dim elements).
 * ``v_cache``: ``[num_blocks, num_kv_heads, block_size // 16, head_dim, 16]`` --
   values transposed inside tiles of 16 positions: for each tile and dimension,
   the 16 positions are contiguous.
@@ -186,7 +187,7 @@ def empty_cache(layout: CacheLayout, num_kv_heads: int, head_dim: int, dtype: st
     bs = layout.block_size
     if bs % 16 or head_dim % 8:
         raise ValueError("block_size must be a multiple of 16 and head_dim of 8")
-    shape_k = (layout.num_blocks, num_kv_heads, head_dim // 8, bs, 8)
+    shape_k = (layout.num_blocks, num_kv_heads, bs // 16, head_dim // 8, 16, 8)
     shape_v = (layout.num_blocks, num_kv_heads, bs // 16, head_dim, 16)
     if dtype == "bf16":
         return (np.full(shape_k, BF16_NAN_BITS, dtype=np.uint16),
@@ -203,7 +204,7 @@ def store_rows(k_cache, v_cache, layout: CacheLayout, b: int, g: int, k_rows, v_
         raise ValueError("position outside the allocated blocks")
     slot = pos % bs
     n, d = k_rows.shape
-    k_cache[blk, g, :, slot, :] = k_rows.reshape(n, d // 8, 8)
+    k_cache[blk, g, slot // 16, :, slot % 16, :] = k_rows.reshape(n, d // 8, 8)
     v_cache[blk, g, slot // 16, :, slot % 16] = v_rows
 
 

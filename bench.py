@@ -281,7 +281,7 @@ def main():
     kern_ms = kernel_ms(step2, args.steps)
     step_bytes = kern_bytes = algorithmic_bytes(case, 2)
     rows = cfg.num_q_heads // cfg.num_kv_heads * 2
-    kernel_name = (f"attn_bf16_kernel<{cfg.head_dim}, {8 if rows <= 8 else 16}>" if cfg.dtype == "bf16"
+    kernel_name = (f"attn_bf16_kernel<{cfg.head_dim}, {8 if rows <= 8 else 16}, false>" if cfg.dtype == "bf16"
                    else f"attn_f32_kernel<{cfg.head_dim}>")
     step_gbps = step_bytes / (ms * 1e-3) / 1e9
     kern_gbps = kern_bytes / (kern_ms * 1e-3) / 1e9

@@ -18,9 +18,12 @@ LIB = os.path.join(PKG, "libdfa.so")
 SOURCES = ["abi.cpp", "attn_bf16.hip", "attn_f32.hip", "combine.hip", "gemv.hip", "measure.hip"]
 ARCH = os.environ.get("DFA_OFFLOAD_ARCH", "gfx950")
 # Packed fp32 VALU ops are disabled: the compiler would otherwise form them from
-# plain float code.
+# plain float code. MFMA accumulators are kept in ordinary VGPRs: the kernels
+# rescale and reduce them with vector ALU code, which would otherwise copy
+# them out of and back into the accumulation registers on every chunk.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form=1",
          "-fvisibility=hidden", "-Wall", "-Wno-unused-function"]
 
 

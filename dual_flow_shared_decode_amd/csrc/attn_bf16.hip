@@ -68,28 +68,69 @@ struct Chunk {
 // masked; reading it keeps every address inside an allocated block).
 __device__ __forceinline__ int tile_start(int t0, int u, int end) { return min(t0 + 16 * u, (end - 1) & ~15); }
 
+// Buffer resource word 3 for raw (untyped) buffer access on gfx9-family
+// targets, and the cache-policy operand of a non-temporal load.
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kNT = 2;
+
+// Largest lag (base-2 units) of a row's running max behind the scores it has
+// weighted: the weights 2^(s - m_run) stay at most 2^kLazyRescale.
+constexpr float kLazyRescale = 8.f;
+
+// Loads one chunk through buffer resources: a tile's base address is
+// wave-uniform (scalar registers), each lane's byte offsets within the tile
+// are fixed (koff for keys, voff for values), and the hardware returns zeros
+// for any offset past the tile.
 template <int D>
 __device__ __forceinline__ void load_chunk(const AttnParams& p, const uint16_t* __restrict__ kc,
                                            const uint16_t* __restrict__ vc, const int* tbl, int jb0,
-                                           int t0, int end, int n, int grp, Chunk<D>& ch) {
+                                           int t0, int end, uint32_t koff, uint32_t voff, Chunk<D>& ch) {
+  constexpr int kTileBytes = D * 16 * 2;
   const int bs_mask = (1 << p.bs_log2) - 1;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int tt = tile_start(t0, u, end);
-    const size_t blk = (size_t)tbl[(tt >> p.bs_log2) - jb0] * p.blk_stride;
-    const int pos = tt & bs_mask;
-    const uint16_t* ka = kc + blk + (size_t)(pos >> 4) * (D * 16) + (grp * 16 + n) * 8;
-    const uint16_t* va = vc + blk + (size_t)(pos >> 4) * (D * 16) + n * 16 + 4 * grp;
+    const int blk = __builtin_amdgcn_readfirstlane(tbl[(tt >> p.bs_log2) - jb0]);
+    const size_t tile = (size_t)blk * p.blk_stride + (size_t)((tt & bs_mask) >> 4) * (D * 16);
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(kc + tile), (short)0, kTileBytes, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(vc + tile), (short)0, kTileBytes, kBufferWord3);
 #pragma unroll
     for (int st = 0; st < D / 32; ++st)
-      ch.k[u][st] = __builtin_nontemporal_load((const bf16x8*)(ka + 4 * st * 16 * 8));
+      ch.k[u][st] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, koff + st * 1024, 0, kNT));
 #pragma unroll
     for (int db = 0; db < D / 16; ++db)
-      ch.v[u][db] = __builtin_nontemporal_load((const bf16x4*)(va + 16 * 16 * db));
+      ch.v[u][db] = __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(rv, voff + db * 512, 0, kNT));
   }
 }
 
-template <int D, int NRP>
+// Raw query operand of one lane and k-step: 8 consecutive dimensions, as
+// stored (bf16 or float32).
+template <bool QF32>
+struct QRaw {
+  bf16x8 v;
+  __device__ __forceinline__ void load(const void* base, size_t off) {
+    v = *(const bf16x8*)((const uint16_t*)base + off);
+  }
+  __device__ __forceinline__ float at(int j) const { return (float)v[j]; }
+};
+template <>
+struct QRaw<true> {
+  float4 lo4, hi4;
+  __device__ __forceinline__ void load(const void* base, size_t off) {
+    const float4* q = (const float4*)((const float*)base + off);
+    lo4 = q[0];
+    hi4 = q[1];
+  }
+  __device__ __forceinline__ float at(int j) const {
+    const float4& w = j < 4 ? lo4 : hi4;
+    const int i = j & 3;
+    return i == 0 ? w.x : (i == 1 ? w.y : (i == 2 ? w.z : w.w));
+  }
+};
+
+template <int D, int NRP, bool QF32>
 __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnParams p) {
   constexpr int KS = D / 32;
   constexpr int DB = D / 16;
@@ -100,96 +141,83 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) float so[kWaves * NRP * D];
 
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  SplitRange r;
-  if (!split_range<D>(p, b, g, s, r)) return;
-  const int jb0 = stage_table(p, b, r, tbl);
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, grp = lane >> 4;
   const int row = PACKED ? (n & 7) : n;
   const int nr = p.flows * p.group;
+  const bool two = p.flows == 2;
 
-  // ---- query operands: scaled (and for flow 2 coupled) rows, split hi/lo ----
-  bf16x8 qa[KS], qb[KS];
-  {
-    float x[KS][8];
-    if (row < nr) {
-      const int f = row / p.group, h = g * p.group + (row - f * p.group);
-      const size_t qoff = ((size_t)b * p.hq + h) * D;
+  // ---- prologue: the length, the queries and the split's block-table slice
+  // are independent loads, issued together; the first cache loads wait only
+  // for the table. Padding rows (row >= nr) load row nr - 1 and are zeroed. ----
+  const int len_raw = p.ctx[b];
+  const int rr = min(row, nr - 1);
+  const int f = rr / p.group, h = g * p.group + (rr - f * p.group);
+  const size_t qoff = ((size_t)b * p.hq + h) * D;
+  QRaw<QF32> q1r[KS], q2r[KS];
+  float4 ar[KS][2];
 #pragma unroll
-      for (int st = 0; st < KS; ++st) {
-        const int d0 = 32 * st + 8 * grp;
-        float v1[8], v2[8];
-        if (p.q_f32) {
-          const float4* q = (const float4*)((const float*)p.q1 + qoff + d0);
-          float4 u0 = q[0], u1 = q[1];
-          v1[0] = u0.x; v1[1] = u0.y; v1[2] = u0.z; v1[3] = u0.w;
-          v1[4] = u1.x; v1[5] = u1.y; v1[6] = u1.z; v1[7] = u1.w;
-        } else {
-          bf16x8 u = *(const bf16x8*)((const uint16_t*)p.q1 + qoff + d0);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) v1[j] = (float)u[j];
-        }
-        if (f == 1) {
-          if (p.q_f32) {
-            const float4* q = (const float4*)((const float*)p.q2 + qoff + d0);
-            float4 u0 = q[0], u1 = q[1];
-            v2[0] = u0.x; v2[1] = u0.y; v2[2] = u0.z; v2[3] = u0.w;
-            v2[4] = u1.x; v2[5] = u1.y; v2[6] = u1.z; v2[7] = u1.w;
-          } else {
-            bf16x8 u = *(const bf16x8*)((const uint16_t*)p.q2 + qoff + d0);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) v2[j] = (float)u[j];
-          }
-          const float4* av = (const float4*)(p.a + (size_t)h * D + d0);
-          float4 a0 = av[0], a1 = av[1];
-          const float aa[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-#pragma unroll
-          for (int j = 0; j < 8; ++j) x[st][j] = fmaf(aa[j], v1[j], v2[j]) * p.qscale;
-        } else {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) x[st][j] = v1[j] * p.qscale;
-        }
-      }
-    } else {
-#pragma unroll
-      for (int st = 0; st < KS; ++st)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) x[st][j] = 0.f;
+  for (int st = 0; st < KS; ++st) {
+    const int d0 = 32 * st + 8 * grp;
+    q1r[st].load(p.q1, qoff + d0);
+    if (two) {
+      q2r[st].load(p.q2, qoff + d0);
+      const float4* av = (const float4*)(p.a + (size_t)h * D + d0);
+      ar[st][0] = av[0];
+      ar[st][1] = av[1];
     }
+  }
+  const int jb0 = stage_split_table(p, b, s, tbl);
+  __syncthreads();  // the table slice is read by every wave
+  SplitRange r;
+  if (!split_bounds<D>(p, b, g, s, len_raw, r)) return;
+
+  // ---- first chunk's loads, then the query operands while they are in flight ----
+  const int bs = 1 << p.bs_log2;
+  const uint16_t* __restrict__ kc = (const uint16_t*)p.k + (size_t)g * bs * D;
+  const uint16_t* __restrict__ vc = (const uint16_t*)p.v + (size_t)g * D * bs;
+  const int nchunks = (r.end - r.start + 31) >> 5;
+  const uint32_t koff = (grp * 16 + n) * 16, voff = (n * 16 + 4 * grp) * 2;  // bytes within a tile
+  Chunk<D> ca, cb;
+  int c = wave;
+  if (c < nchunks) load_chunk<D>(p, kc, vc, tbl, jb0, r.start + 32 * c, r.end, koff, voff, ca);
+
+  // scaled (and for flow 2 coupled) query rows, split hi/lo
+  bf16x8 qa[KS], qb[KS];
 #pragma unroll
-    for (int st = 0; st < KS; ++st) {
+  for (int st = 0; st < KS; ++st) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const __bf16 hi = (__bf16)x[st][j];
-        const __bf16 lo = (__bf16)(x[st][j] - (float)hi);
-        if (PACKED) {
-          qa[st][j] = (n < 8) ? hi : lo;
-        } else {
-          qa[st][j] = hi;
-          qb[st][j] = lo;
-        }
+    for (int j = 0; j < 8; ++j) {
+      const float v1 = q1r[st].at(j);
+      float x = v1;
+      if (two) {
+        const float a = j < 4 ? (&ar[st][0].x)[j] : (&ar[st][1].x)[j - 4];
+        x = f == 1 ? fmaf(a, v1, q2r[st].at(j)) : v1;
+      }
+      x = row < nr ? x * p.qscale : 0.f;
+      const __bf16 hi = (__bf16)x;
+      const __bf16 lo = (__bf16)(x - (float)hi);
+      if (PACKED) {
+        qa[st][j] = (n < 8) ? hi : lo;
+      } else {
+        qa[st][j] = hi;
+        qb[st][j] = lo;
       }
     }
   }
 
   // ---- stream the split's positions in 32-position chunks ----
-  const int bs = 1 << p.bs_log2;
-  const uint16_t* __restrict__ kc = (const uint16_t*)p.k + (size_t)g * bs * D;
-  const uint16_t* __restrict__ vc = (const uint16_t*)p.v + (size_t)g * D * bs;
-  const int nchunks = (r.end - r.start + 31) >> 5;
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  Chunk<D> nxt;
-  int c = wave;
-  if (c < nchunks) load_chunk<D>(p, kc, vc, tbl, jb0, r.start + 32 * c, r.end, n, grp, nxt);
-  for (; c < nchunks; c += kWaves) {
-    Chunk<D> cur = nxt;
-    if (c + kWaves < nchunks)
-      load_chunk<D>(p, kc, vc, tbl, jb0, r.start + 32 * (c + kWaves), r.end, n, grp, nxt);
+  // One chunk: scores, online softmax, weighted values. The running max of a
+  // row moves only when a chunk's max exceeds it by more than kLazyRescale
+  // (base-2 units; a wave-wide vote), so the weights 2^(s - m_run) stay below
+  // 2^kLazyRescale and most chunks skip rescaling the accumulators. The final
+  // (O, m, l) of a row describe the same softmax whatever m_run ended as.
+  auto process = [&](Chunk<D>& cur, int c) __attribute__((always_inline)) {
     const int t0 = r.start + 32 * c;
     f32x4 sv[2];
 #pragma unroll
@@ -237,18 +265,21 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnParams p) {
     for (int j = 1; j < 8; ++j) cmax = fmaxf(cmax, sc[j]);
     cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
     cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-    const float m_new = fmaxf(m_run, cmax);
-    const float alpha = fast_exp2(m_run - m_new);
+    if (__builtin_amdgcn_ballot_w64(cmax > m_run + kLazyRescale) != 0) {
+      const float m_new = fmaxf(m_run, cmax);
+      const float alpha = fast_exp2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+      m_run = m_new;
+    }
     float pv[8], psum = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      pv[j] = fast_exp2(sc[j] - m_new);
+      pv[j] = fast_exp2(sc[j] - m_run);
       psum += pv[j];
     }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+    l_run += psum;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       bf16x4 pa, pb;
@@ -271,6 +302,18 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnParams p) {
         for (int db = 0; db < DB; ++db) oacc[db] = mfma16(cur.v[u][db], pb, oacc[db]);
       }
     }
+  };
+
+  // Wave w takes chunks w, w + kWaves, ...; two register buffers alternate so
+  // that the next chunk's loads are in flight while the current one is used.
+  for (; c < nchunks; c += 2 * kWaves) {
+    if (c + kWaves < nchunks)
+      load_chunk<D>(p, kc, vc, tbl, jb0, r.start + 32 * (c + kWaves), r.end, koff, voff, cb);
+    process(ca, c);
+    if (c + kWaves >= nchunks) break;
+    if (c + 2 * kWaves < nchunks)
+      load_chunk<D>(p, kc, vc, tbl, jb0, r.start + 32 * (c + 2 * kWaves), r.end, koff, voff, ca);
+    process(cb, c + kWaves);
   }
 
   // ---- wave state to LDS, then merge the waves ----
@@ -295,13 +338,30 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnParams p) {
   merge_waves<D, NRP>(p, b, g, s, sm, sl, so);
 }
 
+// LDS a workgroup of attn_bf16_kernel<D, NRP> declares, and the dynamic LDS
+// its launch adds so that one workgroup fills more than half of a compute
+// unit's 160 KB: each CU then runs one workgroup at a time and takes the next
+// one when it finishes, which balances ragged sequence lengths (two resident
+// workgroups per CU were measured 4% slower on lengths U[1024, 8192] and no
+// faster on uniform ones).
+template <int D, int NRP>
+constexpr size_t one_per_cu_lds() {
+  constexpr size_t kCuLds = 160 * 1024;
+  constexpr size_t stat = kMaxTableSlice * 4 + 2 * kWaves * NRP * 4 + kWaves * NRP * D * 4;
+  return stat > kCuLds / 2 ? 0 : kCuLds / 2 + 256 - stat;
+}
+
 hipError_t launch_attn_bf16(const AttnParams& p, int head_dim, int rows_padded, hipStream_t stream,
                             const KernelEvents& ev) {
   const dim3 grid(p.n_splits, p.hkv, p.batch), block(kThreads);
-  if (head_dim == 128 && rows_padded == 8) return launch_kernel(attn_bf16_kernel<128, 8>, grid, block, stream, ev, p);
-  if (head_dim == 128 && rows_padded == 16) return launch_kernel(attn_bf16_kernel<128, 16>, grid, block, stream, ev, p);
-  if (head_dim == 64 && rows_padded == 8) return launch_kernel(attn_bf16_kernel<64, 8>, grid, block, stream, ev, p);
-  if (head_dim == 64 && rows_padded == 16) return launch_kernel(attn_bf16_kernel<64, 16>, grid, block, stream, ev, p);
+#define DFA_ATTN_CASE(D_, NRP_)                                                                              \
+  if (head_dim == D_ && rows_padded == NRP_)                                                                 \
+    return p.q_f32 ? launch_kernel(attn_bf16_kernel<D_, NRP_, true>, grid, block, stream, ev, p,              \
+                                   one_per_cu_lds<D_, NRP_>())                                                \
+                   : launch_kernel(attn_bf16_kernel<D_, NRP_, false>, grid, block, stream, ev, p,             \
+                                   one_per_cu_lds<D_, NRP_>());
+  DFA_ATTN_CASE(128, 8) DFA_ATTN_CASE(128, 16) DFA_ATTN_CASE(64, 8) DFA_ATTN_CASE(64, 16)
+#undef DFA_ATTN_CASE
   return hipErrorInvalidValue;
 }
 

@@ -26,6 +26,30 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Result of a split that holds no position of its sequence: zero outputs in
+// direct mode (an empty sequence), else the empty record (O = 0, m = -inf,
+// l = 0) of each row, so that every record the combine reads is written by the
+// same call.
+template <int D, int NT>
+__device__ __forceinline__ void write_empty(const AttnParams& p, int b, int g, int s) {
+  const int nr = p.flows * p.group;
+  if (p.direct) {
+    for (int idx = threadIdx.x; idx < nr * D; idx += NT) {
+      const int row = idx / D, d = idx - row * D;
+      const int f = row / p.group, h = g * p.group + (row - f * p.group);
+      float* out = f ? p.o2 : p.o1;
+      out[((size_t)b * p.hq + h) * D + d] = 0.f;
+    }
+  } else {
+    for (int idx = threadIdx.x; idx < nr * (D + 2); idx += NT) {
+      const int row = idx / (D + 2), d = idx - row * (D + 2);
+      const int f = row / p.group, h = g * p.group + (row - f * p.group);
+      float* rec = p.part + ((((size_t)b * p.hq + h) * p.flows + f) * p.n_splits + s) * (D + kRecPad);
+      rec[d] = d == D ? -INFINITY : 0.f;
+    }
+  }
+}
+
 // Positions [start, end) handled by workgroup (split s, sequence b); returns
 // false when the split holds no position of the sequence. Such a workgroup
 // still writes its result: zero outputs in direct mode (an empty sequence),
@@ -43,22 +67,7 @@ __device__ __forceinline__ bool split_range(const AttnParams& p, int b, int g, i
   r.start = s * p.split_len;
   r.end = min(r.start + p.split_len, len);
   if (r.start < len) return true;
-  const int nr = p.flows * p.group;
-  if (p.direct) {
-    for (int idx = threadIdx.x; idx < nr * D; idx += kThreads) {
-      const int row = idx / D, d = idx - row * D;
-      const int f = row / p.group, h = g * p.group + (row - f * p.group);
-      float* out = f ? p.o2 : p.o1;
-      out[((size_t)b * p.hq + h) * D + d] = 0.f;
-    }
-  } else {
-    for (int idx = threadIdx.x; idx < nr * (D + 2); idx += kThreads) {
-      const int row = idx / (D + 2), d = idx - row * (D + 2);
-      const int f = row / p.group, h = g * p.group + (row - f * p.group);
-      float* rec = p.part + ((((size_t)b * p.hq + h) * p.flows + f) * p.n_splits + s) * (D + kRecPad);
-      rec[d] = d == D ? -INFINITY : 0.f;
-    }
-  }
+  write_empty<D, kThreads>(p, b, g, s);
   return false;
 }
 
@@ -76,6 +85,37 @@ __device__ __forceinline__ int stage_table(const AttnParams& p, int b, const Spl
   }
   __syncthreads();  // every wave reads entries other waves wrote
   return jb0;
+}
+
+// Stages the physical block ids of every block split s can touch (from its
+// first position on; it does not need the sequence length) into LDS, clamped
+// to [0, num_blocks) so that no cache access can leave the cache tensors.
+// The caller issues a workgroup barrier before any wave reads the entries.
+template <int NT = kThreads>
+__device__ __forceinline__ int stage_split_table(const AttnParams& p, int b, int s, int* tbl) {
+  const int jb0 = (s * p.split_len) >> p.bs_log2;
+  const int nb = min(((p.split_len - 1) >> p.bs_log2) + 2, p.max_blocks - jb0);
+  const int32_t* row = p.table + (size_t)b * p.max_blocks + jb0;
+  for (int j = threadIdx.x; j < nb; j += NT) {
+    int blk = row[j];
+    blk = blk < 0 ? 0 : (blk >= p.num_blocks ? p.num_blocks - 1 : blk);
+    tbl[j] = blk;
+  }
+  return jb0;
+}
+
+// Bounds of split s given the raw length ctx[b]; as split_range, including
+// the zero outputs / empty records of a split past the end of its sequence.
+template <int D, int NT = kThreads>
+__device__ __forceinline__ bool split_bounds(const AttnParams& p, int b, int g, int s, int len_raw, SplitRange& r) {
+  int len = len_raw + p.ctx_add;
+  len = len < 0 ? 0 : (len > p.max_ctx ? p.max_ctx : len);
+  r.len = len;
+  r.start = s * p.split_len;
+  r.end = min(r.start + p.split_len, len);
+  if (r.start < len) return true;
+  write_empty<D, NT>(p, b, g, s);
+  return false;
 }
 
 // Cross-wave merge. Each wave w left, for each of its rows, the running max

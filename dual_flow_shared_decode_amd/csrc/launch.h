@@ -1,5 +1,6 @@
 // Kernel launch with optional dispatch events (hipExtLaunchKernelGGL records
-// them from the dispatch itself, without extra commands on the stream).
+// them from the dispatch itself, without extra commands on the stream) and
+// optional dynamic LDS bytes.
 #pragma once
 
 #include <hip/hip_ext.h>
@@ -11,11 +12,11 @@ namespace dfa {
 
 template <typename Kernel, typename Params>
 hipError_t launch_kernel(Kernel kernel, dim3 grid, dim3 block, hipStream_t stream, const KernelEvents& ev,
-                         const Params& params) {
+                         const Params& params, size_t lds_bytes = 0) {
   if (ev.start || ev.stop)
-    hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, ev.start, ev.stop, 0, params);
+    hipExtLaunchKernelGGL(kernel, grid, block, lds_bytes, stream, ev.start, ev.stop, 0, params);
   else
-    hipLaunchKernelGGL(kernel, grid, block, 0, stream, params);
+    hipLaunchKernelGGL(kernel, grid, block, lds_bytes, stream, params);
   return hipGetLastError();
 }
 

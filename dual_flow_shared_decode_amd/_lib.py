@@ -210,8 +210,11 @@ def dfa_dual_gemv_workspace_size(desc: GemvDesc) -> int:
 
 def kv_target(k_cache, v_cache, block_table, ctx_lens, num_kv_heads, head_dim, block_size,
               max_blocks_per_seq, num_blocks) -> KvTarget:
-    return KvTarget(_ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(ctx_lens), num_kv_heads, head_dim,
-                    block_size, max_blocks_per_seq, num_blocks)
+    """Device addresses of the cache to append to; the structure keeps the tensors alive."""
+    kv = KvTarget(_ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(ctx_lens), num_kv_heads, head_dim,
+                  block_size, max_blocks_per_seq, num_blocks)
+    kv._tensors = (k_cache, v_cache, block_table, ctx_lens)
+    return kv
 
 
 def dfa_dual_gemv(desc, w, w2, x1, x2, couple, res1, res2, y1, y2, kv, workspace, stream=None):
@@ -231,8 +234,12 @@ def dfa_decode_layer_workspace_size(desc: LayerDesc) -> int:
 
 
 def layer_weights(wq, wk, wv, wo, w_gate, w_up, w_down, a, b, c) -> LayerWeights:
-    """Device addresses of packed weights and coupling vectors (tensors or None)."""
-    return LayerWeights(*[_ptr(t) for t in (wq, wk, wv, wo, w_gate, w_up, w_down, a, b, c)])
+    """Device addresses of packed weights and coupling vectors (tensors or None); the structure
+    keeps the tensors alive."""
+    tensors = (wq, wk, wv, wo, w_gate, w_up, w_down, a, b, c)
+    lw = LayerWeights(*[_ptr(t) for t in tensors])
+    lw._tensors = tensors
+    return lw
 
 
 def dfa_decode_layer(desc, weights, x1, x2, k_cache, v_cache, block_table, ctx_lens, out1, out2, workspace,

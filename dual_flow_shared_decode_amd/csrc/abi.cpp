@@ -214,7 +214,7 @@ dfa_status validate_gemv(const dfa_gemv_desc* d, GemvPlan* plan) {
   if (d->num_flows != 1 && d->num_flows != 2) return fail(DFA_ERR_SHAPE, "num_flows must be 1 or 2");
   if (d->batch < 1 || d->batch * d->num_flows > 64)
     return fail(DFA_ERR_UNSUPPORTED, "batch must be in [1, 32] with two flows, [1, 64] with one");
-  if (d->n < 128 || d->n % 128 != 0) return fail(DFA_ERR_SHAPE, "n must be a positive multiple of 128");
+  if (d->n < 64 || d->n % 64 != 0) return fail(DFA_ERR_SHAPE, "n must be a positive multiple of 64");
   if (d->k < 128 || d->k % 128 != 0) return fail(DFA_ERR_SHAPE, "k must be a positive multiple of 128");
   if (d->epilogue < DFA_EPI_NONE || d->epilogue > DFA_EPI_KV_APPEND) return fail(DFA_ERR_SHAPE, "unknown epilogue");
   if (d->epilogue == DFA_EPI_KV_APPEND && d->num_flows != 1)
@@ -227,7 +227,9 @@ dfa_status validate_gemv(const dfa_gemv_desc* d, GemvPlan* plan) {
   pl.m_pad = d->num_flows * pl.cbf * 16;
   const int64_t chunks = d->k / int64_t(dfa::gemv_chunk());
   const int64_t row_groups = d->n / int64_t(dfa::gemv_rows_per_workgroup());
-  int64_t ks = d->k_split > 0 ? d->k_split : std::max<int64_t>(1, (512 + row_groups - 1) / row_groups);
+  // Library choice: about one workgroup per compute unit (256); a matrix with
+  // at least 192 row groups runs unsplit, so its epilogue needs no second launch.
+  int64_t ks = d->k_split > 0 ? d->k_split : (row_groups >= 192 ? 1 : (256 + row_groups - 1) / row_groups);
   ks = std::min<int64_t>(ks, chunks);
   const int64_t chunks_per = (chunks + ks - 1) / ks;
   pl.k_range = int32_t(chunks_per * dfa::gemv_chunk());
@@ -238,6 +240,7 @@ dfa_status validate_gemv(const dfa_gemv_desc* d, GemvPlan* plan) {
 }
 
 size_t gemv_workspace(const dfa_gemv_desc* d, const GemvPlan& pl) {
+  if (pl.k_split == 1) return 0;  // the epilogue runs in the GEMV kernel
   return size_t(pl.k_split) * pl.mats * pl.m_pad * size_t(d->n) * sizeof(float);
 }
 
@@ -260,8 +263,9 @@ dfa_status gemv_impl(const dfa_gemv_desc* d, const uint16_t* w, const uint16_t* 
     const void* ptrs[] = {w, w2, x1, x2, couple, res1, res2, y1, y2, workspace};
     for (const void* q : ptrs)
       if (q && !aligned16(q)) return fail(DFA_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
-    if (!workspace) return fail(DFA_ERR_WORKSPACE, "workspace is required");
-    if (ws_bytes < gemv_workspace(d, pl)) return fail(DFA_ERR_WORKSPACE, "workspace smaller than dfa_dual_gemv_workspace_size()");
+    const size_t need = gemv_workspace(d, pl);
+    if (need > 0 && !workspace) return fail(DFA_ERR_WORKSPACE, "workspace is required when k_split > 1");
+    if (ws_bytes < need) return fail(DFA_ERR_WORKSPACE, "workspace smaller than dfa_dual_gemv_workspace_size()");
     dfa::GemvParams p{};
     if (kvapp) {
       if (kv->num_kv_heads < 1 || kv->head_dim < 8 || kv->head_dim % 8 != 0 ||
@@ -304,8 +308,10 @@ dfa_status gemv_impl(const dfa_gemv_desc* d, const uint16_t* w, const uint16_t* 
     p.epilogue = d->epilogue;
     hipError_t e = dfa::launch_gemv(p, hs);
     if (e != hipSuccess) return fail(DFA_ERR_HIP, std::string("gemv launch: ") + hipGetErrorString(e));
-    e = dfa::launch_gemv_finalize(p, hs);
-    if (e != hipSuccess) return fail(DFA_ERR_HIP, std::string("gemv epilogue launch: ") + hipGetErrorString(e));
+    if (pl.k_split > 1) {
+      e = dfa::launch_gemv_finalize(p, hs);
+      if (e != hipSuccess) return fail(DFA_ERR_HIP, std::string("gemv epilogue launch: ") + hipGetErrorString(e));
+    }
     return DFA_OK;
   }
 }

@@ -19,13 +19,20 @@
 //
 // Activation rows: flow f, sequence s is MFMA column block f*CBF + s/16, column
 // s % 16 (each flow padded to CBF*16 rows), so the two flows of a sequence end
-// up in the same lane and register -- the couplings are elementwise.
+// up in the same lane and register.
 //
-// Workgroup = 4 waves = 128 weight rows (2 tiles of 16 per wave) x one k-range
-// (split-K). Per 128-column chunk the workgroup converts the activations to
-// hi/lo bf16 in LDS, laid out as the B operand ([block][k/8][16][8]). Partial
-// sums go to the workspace [k-split][matrix][row][n]; gemv_finalize sums them
-// in a fixed order and applies the epilogue.
+// Workgroup = 8 waves = 64 weight rows (four 16-row tiles, of each matrix) x
+// one k-range (split-K); two wave groups split the k-steps of every stage,
+// so each SIMD runs two waves that share the stage's B operands. The k-range
+// is streamed in 128-column stages, three in flight: a stage's weights (in
+// registers) and raw activations (in registers, first touched when they are
+// converted) are fetched together, and per stage the workgroup converts the
+// next stage's activations to hi/lo bf16 in LDS (double-buffered), laid out
+// as the B operand ([block][k/8][16][8]). With one k-range the epilogue runs
+// in the same kernel; otherwise partial sums go to the workspace
+// [k-split][matrix][row][n] and gemv_finalize adds them in a fixed order and
+// applies the epilogue (so the primary flow's results never depend on the
+// auxiliary flow's inputs).
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -35,13 +42,6 @@ namespace dfa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kGemvWaves = 4;
-constexpr int kGemvThreads = 64 * kGemvWaves;
-constexpr int kTilesPerWave = 2;
-constexpr int kRowsPerWg = 16 * kTilesPerWave * kGemvWaves;  // 128 weight rows
-constexpr int kChunk = 128;                                  // k columns staged per step
-constexpr int kKSteps = kChunk / 32;
 
 // ---------------------------------------------------------------- packing
 __global__ __launch_bounds__(256) void pack_weight_kernel(const uint16_t* __restrict__ w, uint16_t* __restrict__ wt,
@@ -65,126 +65,21 @@ hipError_t launch_pack_weight(const uint16_t* w, uint16_t* wt, int n, int k, hip
 }
 
 // ---------------------------------------------------------------- GEMV
+namespace {
+constexpr int kTiles = 4;                      // 16-row weight tiles per workgroup
+constexpr int kGroups = 2;                     // wave groups sharing the tiles (1 or 2)
+constexpr int kGemvWaves = kGroups * kTiles;
+constexpr int kGemvThreads = 64 * kGemvWaves;
+constexpr int kRowsPerWg = 16 * kTiles;
+constexpr int kStage = 128;                    // k columns per pipeline stage
+constexpr int kSteps = kStage / 32;            // MFMA k-steps per stage
+constexpr int kHalfSteps = kSteps / kGroups;   // k-steps of one wave group per stage
+}  // namespace
+
 __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// NCB: activation column blocks (flows * CBF); PAIR: a second matrix (w2) on the
-// same activations; LO: split activations into hi + lo.
-template <int NCB, bool PAIR, bool LO>
-__global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvParams p) {
-  constexpr int NH = LO ? 2 : 1;
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][NH][NCB][kChunk / 8][16][8];
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int col = lane & 15, grp = lane >> 4;
-  const int ks = blockIdx.y;
-  const int k_begin = ks * p.k_range, k_end = min(k_begin + p.k_range, p.k);
-  const int nchunks = (k_end - k_begin) / kChunk;
-  const int kg_total = p.k / 8;
-  const int tile0 = (blockIdx.x * kRowsPerWg) / 16 + wave * kTilesPerWave;  // first 16-row tile of this wave
-
-  // stage activation chunk c (columns k_begin + c*kChunk ..) into xs[buf]
-  auto stage = [&](int c, int buf) {
-    const int kc = k_begin + c * kChunk;
-    for (int item = threadIdx.x; item < NCB * 16 * (kChunk / 8); item += kGemvThreads) {
-      const int kg = item % (kChunk / 8);
-      const int m = item / (kChunk / 8);  // padded activation row: block m/16, column m%16
-      const int cb = m / 16, f = cb / p.cbf, s = (cb - f * p.cbf) * 16 + (m & 15);
-      float v[8];
-      if (s < p.batch) {
-        const float* src = (f ? p.x2 : p.x1) + (size_t)s * p.k + kc + kg * 8;
-        const float4 a = *(const float4*)src, b = *(const float4*)(src + 4);
-        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = 0.f;
-      }
-      bf16x8 hi, lo;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        hi[j] = (__bf16)v[j];
-        lo[j] = (__bf16)(v[j] - (float)hi[j]);
-      }
-      *(bf16x8*)&xs[buf][0][cb][kg][m & 15][0] = hi;
-      if (LO) *(bf16x8*)&xs[buf][NH - 1][cb][kg][m & 15][0] = lo;
-    }
-  };
-
-  // weight operands of one chunk: per tile and k-step, row `col` of the tile, 8 columns
-  struct WChunk {
-    bf16x8 a[kTilesPerWave][kKSteps];
-    bf16x8 b[PAIR ? kTilesPerWave : 1][kKSteps];
-  };
-  auto load_w = [&](int c, WChunk& wc) {
-    const int kg0 = (k_begin + c * kChunk) / 8;
-#pragma unroll
-    for (int t = 0; t < kTilesPerWave; ++t) {
-      const size_t base = (((size_t)(tile0 + t) * kg_total + kg0 + grp) * 16 + col) * 8;
-#pragma unroll
-      for (int st = 0; st < kKSteps; ++st) {
-        wc.a[t][st] = __builtin_nontemporal_load((const bf16x8*)(p.w + base + (size_t)st * 4 * 16 * 8));
-        if (PAIR) wc.b[t][st] = __builtin_nontemporal_load((const bf16x8*)(p.w2 + base + (size_t)st * 4 * 16 * 8));
-      }
-    }
-  };
-
-  f32x4 acc[kTilesPerWave][NCB], acc2[PAIR ? kTilesPerWave : 1][NCB];
-#pragma unroll
-  for (int t = 0; t < kTilesPerWave; ++t)
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      acc[t][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (PAIR) acc2[t][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-
-  WChunk wnext;
-  if (nchunks > 0) {
-    load_w(0, wnext);
-    stage(0, 0);
-  }
-  __syncthreads();
-  for (int c = 0; c < nchunks; ++c) {
-    const int buf = c & 1;
-    WChunk wc = wnext;
-    if (c + 1 < nchunks) {
-      load_w(c + 1, wnext);
-      stage(c + 1, buf ^ 1);
-    }
-#pragma unroll
-    for (int st = 0; st < kKSteps; ++st) {
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
-#pragma unroll
-        for (int h = 0; h < NH; ++h) {
-          const bf16x8 xb = *(const bf16x8*)&xs[buf][h][cb][4 * st + grp][col][0];
-#pragma unroll
-          for (int t = 0; t < kTilesPerWave; ++t) {
-            acc[t][cb] = mfma(wc.a[t][st], xb, acc[t][cb]);
-            if (PAIR) acc2[t][cb] = mfma(wc.b[t][st], xb, acc2[t][cb]);
-          }
-        }
-      }
-    }
-    __syncthreads();
-  }
-
-  // partial sums: part[ks][mat][m][n], lane holds rows m = cb*16 + col, n = tile*16 + 4*grp + i
-  const size_t mat_stride = (size_t)p.m_pad * p.n;
-  float* out = p.part + (size_t)ks * (PAIR ? 2 : 1) * mat_stride;
-#pragma unroll
-  for (int t = 0; t < kTilesPerWave; ++t) {
-    const int n0 = (tile0 + t) * 16 + 4 * grp;
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      const size_t off = (size_t)(cb * 16 + col) * p.n + n0;
-      *(f32x4*)(out + off) = acc[t][cb];
-      if (PAIR) *(f32x4*)(out + mat_stride + off) = acc2[t][cb];
-    }
-  }
-}
-
-// ---------------------------------------------------------------- epilogue
 __device__ __forceinline__ float silu(float u) { return u / (1.f + __expf(-u)); }
 
 // Round to the nearest bf16, ties to even (finite inputs).
@@ -193,62 +88,334 @@ __device__ __forceinline__ uint16_t bf16_rne(float x) {
   return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
-// One thread per (sequence s, column n): both flows' sums over the k-splits
-// (fixed order), then the epilogue.
-__global__ __launch_bounds__(256) void gemv_finalize_kernel(GemvParams p) {
-  const int n = blockIdx.x * 256 + threadIdx.x;
-  const int s = blockIdx.y;
-  if (n >= p.n) return;
-  const size_t mat_stride = (size_t)p.m_pad * p.n;
-  const int mats = p.pair ? 2 : 1;
-  float y[2][2] = {{0.f, 0.f}, {0.f, 0.f}};  // [flow][matrix]
-  for (int f = 0; f < p.flows; ++f) {
-    const size_t m = (size_t)(f * p.cbf * 16 + s);
-    for (int ks = 0; ks < p.k_split; ++ks)
-      for (int mat = 0; mat < mats; ++mat) y[f][mat] += p.part[((size_t)ks * mats + mat) * mat_stride + m * p.n + n];
-  }
-  const size_t o = (size_t)s * p.n + n;
+__device__ __forceinline__ void store4(float* dst, const float (&v)[4]) {
+  *(float4*)dst = make_float4(v[0], v[1], v[2], v[3]);
+}
+
+// Epilogue of one sequence s and four consecutive columns n0..n0+3, from the
+// sums y[flow][matrix][j] of both flows (flow 2 unused with one flow).
+__device__ __forceinline__ void apply_epilogue(const GemvParams& p, int s, int n0, const float (&y)[2][2][4]) {
+  const size_t o = (size_t)s * p.n + n0;
+  const bool two = p.flows == 2;
+  float r1[4], r2[4];
   switch (p.epilogue) {
     case kEpiNone:
-      p.y1[o] = y[0][0];
-      if (p.flows == 2) p.y2[o] = y[1][0];
+      store4(p.y1 + o, y[0][0]);
+      if (two) store4(p.y2 + o, y[1][0]);
       break;
-    case kEpiResidual:
-      p.y1[o] = p.res1[o] + y[0][0];
-      if (p.flows == 2) p.y2[o] = p.res2[o] + y[1][0];
+    case kEpiResidual: {
+      const float4 a = *(const float4*)(p.res1 + o);
+      r1[0] = a.x + y[0][0][0]; r1[1] = a.y + y[0][0][1]; r1[2] = a.z + y[0][0][2]; r1[3] = a.w + y[0][0][3];
+      store4(p.y1 + o, r1);
+      if (two) {
+        const float4 b = *(const float4*)(p.res2 + o);
+        r2[0] = b.x + y[1][0][0]; r2[1] = b.y + y[1][0][1]; r2[2] = b.z + y[1][0][2]; r2[3] = b.w + y[1][0][3];
+        store4(p.y2 + o, r2);
+      }
       break;
+    }
     case kEpiSwiglu: {
-      const float z1 = silu(y[0][0]) * y[0][1];
-      p.y1[o] = z1;
-      if (p.flows == 2) {
-        const float z2 = silu(y[1][0]) * y[1][1];
-        p.y2[o] = p.couple ? fmaf(p.couple[n], z1, z2) : z2;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) r1[j] = silu(y[0][0][j]) * y[0][1][j];
+      store4(p.y1 + o, r1);
+      if (two) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float z2 = silu(y[1][0][j]) * y[1][1][j];
+          r2[j] = p.couple ? fmaf(p.couple[n0 + j], r1[j], z2) : z2;
+        }
+        store4(p.y2 + o, r2);
       }
       break;
     }
     case kEpiResidualCoupled: {
-      p.y1[o] = p.res1[o] + y[0][0];
-      if (p.flows == 2) p.y2[o] = p.res2[o] + (p.couple ? fmaf(p.couple[n], y[0][0], y[1][0]) : y[1][0]);
+      const float4 a = *(const float4*)(p.res1 + o);
+      r1[0] = a.x + y[0][0][0]; r1[1] = a.y + y[0][0][1]; r1[2] = a.z + y[0][0][2]; r1[3] = a.w + y[0][0][3];
+      store4(p.y1 + o, r1);
+      if (two) {
+        const float4 b = *(const float4*)(p.res2 + o);
+        const float bb[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          r2[j] = bb[j] + (p.couple ? fmaf(p.couple[n0 + j], y[0][0][j], y[1][0][j]) : y[1][0][j]);
+        store4(p.y2 + o, r2);
+      }
       break;
     }
     case kEpiKvAppend: {
-      // primary only: k = row n of W, v = row n of W2, appended at position ctx_lens[s]
-      if (p.y1) p.y1[o] = y[0][0];
-      if (p.y2) p.y2[o] = y[0][1];
+      // primary only: k = rows n of W, v = rows n of W2, appended at position ctx_lens[s]
+      if (p.y1) store4(p.y1 + o, y[0][0]);
+      if (p.y2) store4(p.y2 + o, y[0][1]);
       const int bs = 1 << p.kv_bs_log2;
       int pos = p.kv_ctx[s];
       pos = pos < 0 ? 0 : (pos >= p.kv_max_blocks * bs ? p.kv_max_blocks * bs - 1 : pos);
       int blk = p.kv_table[(size_t)s * p.kv_max_blocks + (pos >> p.kv_bs_log2)];
       blk = blk < 0 ? 0 : (blk >= p.kv_num_blocks ? p.kv_num_blocks - 1 : blk);
-      const int g = n / p.kv_head_dim, d = n - g * p.kv_head_dim, slot = pos & (bs - 1);
+      const int g = n0 / p.kv_head_dim, d = n0 - g * p.kv_head_dim, slot = pos & (bs - 1);
       const size_t head = (size_t)blk * p.kv_hkv * p.kv_head_dim * bs + (size_t)g * p.kv_head_dim * bs;
-      // keys [bs/16][D/8][16][8], values [bs/16][D][16] inside a block and kv head
-      p.kv_k[head + (size_t)(slot >> 4) * p.kv_head_dim * 16 + (size_t)(d >> 3) * 128 + (slot & 15) * 8 + (d & 7)] =
-          bf16_rne(y[0][0]);
-      p.kv_v[head + (size_t)(slot >> 4) * p.kv_head_dim * 16 + (size_t)d * 16 + (slot & 15)] = bf16_rne(y[0][1]);
+      const size_t tile = head + (size_t)(slot >> 4) * p.kv_head_dim * 16;
+      // keys [bs/16][D/8][16][8]: dims d..d+3 are consecutive inside one 8-dim group
+      uint2 kb;
+      kb.x = (uint32_t)bf16_rne(y[0][0][0]) | ((uint32_t)bf16_rne(y[0][0][1]) << 16);
+      kb.y = (uint32_t)bf16_rne(y[0][0][2]) | ((uint32_t)bf16_rne(y[0][0][3]) << 16);
+      *(uint2*)(p.kv_k + tile + (size_t)(d >> 3) * 128 + (slot & 15) * 8 + (d & 7)) = kb;
+      // values [bs/16][D][16]: one element per dim
+#pragma unroll
+      for (int j = 0; j < 4; ++j) p.kv_v[tile + (size_t)(d + j) * 16 + (slot & 15)] = bf16_rne(y[0][1][j]);
       break;
     }
   }
+}
+
+// Raw activations of one stage held by one thread: the stage has NCB*16 rows
+// x kStage/8 groups of 8 columns; thread t takes groups t, t + threads, ...
+template <int NCB>
+struct XStage {
+  static constexpr int kTotal = NCB * 16 * (kStage / 8);  // 8-column groups of one stage
+  static constexpr int kItems = (kTotal + kGemvThreads - 1) / kGemvThreads;
+  float4 v[kItems][2];
+  bool live[kItems];  // false: the group is padding and converts to zeros
+};
+
+template <int NCB>
+__device__ __forceinline__ void fetch_x(const GemvParams& p, int k_begin, int st, XStage<NCB>& xr) {
+  const int kc = k_begin + st * kStage;
+#pragma unroll
+  for (int it = 0; it < XStage<NCB>::kItems; ++it) {
+    const int item = threadIdx.x + it * kGemvThreads;
+    const int kg = item % (kStage / 8), m = item / (kStage / 8);
+    const int cb = m >> 4, f = cb / p.cbf, s = (cb - f * p.cbf) * 16 + (m & 15);
+    // groups past the stage (fewer than threads) or past the batch read row 0
+    // of x1, which always exists, and are replaced by zeros
+    const bool live = item < XStage<NCB>::kTotal && s < p.batch;
+    const float4* src = (const float4*)(live ? (f ? p.x2 : p.x1) + (size_t)s * p.k + kc + kg * 8 : p.x1 + kc);
+    // the values are not touched here: the conversion (put_x) is the first use,
+    // so the loads stay in flight until then
+    xr.v[it][0] = src[0];
+    xr.v[it][1] = src[1];
+    xr.live[it] = live;
+  }
+}
+
+// Converts a stage to hi (and lo) bf16 B operands in LDS: xs[h][cb][k/8][16][8].
+template <int NCB, int NH>
+__device__ __forceinline__ void put_x(const XStage<NCB>& xr, uint16_t* xs) {
+#pragma unroll
+  for (int it = 0; it < XStage<NCB>::kItems; ++it) {
+    const int item = threadIdx.x + it * kGemvThreads;
+    const int kg = item % (kStage / 8), m = item / (kStage / 8);
+    const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 q0 = xr.live[it] ? xr.v[it][0] : z, q1 = xr.live[it] ? xr.v[it][1] : z;
+    bf16x8 hi, lo;
+    hi[0] = (__bf16)q0.x; hi[1] = (__bf16)q0.y; hi[2] = (__bf16)q0.z; hi[3] = (__bf16)q0.w;
+    hi[4] = (__bf16)q1.x; hi[5] = (__bf16)q1.y; hi[6] = (__bf16)q1.z; hi[7] = (__bf16)q1.w;
+    if (NH == 2) {
+      lo[0] = (__bf16)(q0.x - (float)hi[0]); lo[1] = (__bf16)(q0.y - (float)hi[1]);
+      lo[2] = (__bf16)(q0.z - (float)hi[2]); lo[3] = (__bf16)(q0.w - (float)hi[3]);
+      lo[4] = (__bf16)(q1.x - (float)hi[4]); lo[5] = (__bf16)(q1.y - (float)hi[5]);
+      lo[6] = (__bf16)(q1.z - (float)hi[6]); lo[7] = (__bf16)(q1.w - (float)hi[7]);
+    }
+    const size_t off = (((size_t)(m >> 4) * (kStage / 8) + kg) * 16 + (m & 15)) * 8;
+    if (item < XStage<NCB>::kTotal) {
+      *(bf16x8*)(xs + off) = hi;
+      if (NH == 2) *(bf16x8*)(xs + (size_t)NCB * kStage * 16 + off) = lo;
+    }
+  }
+}
+
+// NCB: activation column blocks (flows * CBF); PAIR: a second matrix (w2) on the
+// same activations; LO: split activations into hi + lo.
+//
+// Wave w works on tile w % 4 with the k-steps of wave group w / 4: group g
+// takes k-steps 2g, 2g + 1 of every stage, so two waves per SIMD share the
+// stage's B operands and each holds half of the weights in flight.
+template <int NCB, bool PAIR, bool LO>
+__global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvParams p) {
+  constexpr int NH = LO ? 2 : 1;
+  constexpr int MATS = PAIR ? 2 : 1;
+  constexpr int DEPTH = 3;  // stages in flight: weights and activations of each are fetched together
+  // LDS: the double-buffered B operands, reused after the loop to stage the
+  // results for the epilogue (whichever is larger sets the size)
+  constexpr size_t kXsBytes = 2 * NH * NCB * (kStage / 8) * 16 * 8 * sizeof(uint16_t);
+  constexpr size_t kResBytes = MATS * NCB * 16 * kRowsPerWg * sizeof(float);
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kXsBytes > kResBytes ? kXsBytes : kResBytes];
+  __shared__ __attribute__((aligned(16))) float red[kGroups == 2 ? MATS : 1][NCB][kTiles][64][4];  // group 1's sums
+  auto xs = reinterpret_cast<uint16_t(*)[NH][NCB][kStage / 8][16][8]>(smem);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int wt = wave & (kTiles - 1), wg = wave / kTiles;
+  const int tile = blockIdx.x * kTiles + wt;  // this wave's 16-row weight tile
+  const int ks = blockIdx.y;
+  const int k_begin = ks * p.k_range;
+  const int nst = (min(k_begin + p.k_range, p.k) - k_begin) / kStage;
+  const int kg_total = p.k / 8;
+
+  // weight operands of one stage: per matrix and this group's k-steps, row `col` of the tile
+  struct WStage {
+    bf16x8 a[MATS][kHalfSteps];
+  };
+  auto fetch_w = [&](int st, WStage& w) __attribute__((always_inline)) {
+    const int kg0 = (k_begin + st * kStage) / 8 + wg * kHalfSteps * 4;
+    const size_t base = (((size_t)tile * kg_total + kg0 + grp) * 16 + col) * 8;
+#pragma unroll
+    for (int k2 = 0; k2 < kHalfSteps; ++k2) {
+      w.a[0][k2] = __builtin_nontemporal_load((const bf16x8*)(p.w + base + (size_t)k2 * 4 * 16 * 8));
+      if (PAIR) w.a[MATS - 1][k2] = __builtin_nontemporal_load((const bf16x8*)(p.w2 + base + (size_t)k2 * 4 * 16 * 8));
+    }
+  };
+
+  f32x4 acc[MATS][NCB];
+#pragma unroll
+  for (int mat = 0; mat < MATS; ++mat)
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) acc[mat][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Loads complete in issue order: a stage's activations and weights are
+  // fetched together DEPTH stages ahead, and the activations of stage st + 1
+  // are converted (waiting for stage st + 1 only) while later stages stay in
+  // flight.
+  WStage w0, w1, w2;  // three separately named buffers stay in registers
+  XStage<NCB> x0, x1, x2;
+  if (nst > 0) {
+    fetch_x<NCB>(p, k_begin, 0, x0);
+    fetch_w(0, w0);
+  }
+  if (nst > 1) {
+    fetch_x<NCB>(p, k_begin, 1, x1);
+    fetch_w(1, w1);
+  }
+  if (nst > 2) {
+    fetch_x<NCB>(p, k_begin, 2, x2);
+    fetch_w(2, w2);
+  }
+  if (nst > 0) put_x<NCB, NH>(x0, &xs[0][0][0][0][0][0]);
+  __syncthreads();
+  // stage st: multiply with weights wj (B operands in xs[st & 1]); meanwhile
+  // convert stage st + 1 from xn and fetch stage st + DEPTH into wj, xj
+  auto step = [&](int st, WStage& wj, XStage<NCB>& xj, const XStage<NCB>& xn) __attribute__((always_inline)) {
+    const int buf = st & 1;
+    if (st + 1 < nst) put_x<NCB, NH>(xn, &xs[buf ^ 1][0][0][0][0][0]);
+    bf16x8 xb[kHalfSteps][NCB][NH];
+#pragma unroll
+    for (int k2 = 0; k2 < kHalfSteps; ++k2)
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+          xb[k2][cb][h] = *(const bf16x8*)&xs[buf][h][cb][4 * (wg * kHalfSteps + k2) + grp][col][0];
+#pragma unroll
+    for (int k2 = 0; k2 < kHalfSteps; ++k2)
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+#pragma unroll
+          for (int mat = 0; mat < MATS; ++mat)
+            acc[mat][cb] = mfma(wj.a[mat][k2], xb[k2][cb][h], acc[mat][cb]);
+    if (st + DEPTH < nst) {
+      fetch_x<NCB>(p, k_begin, st + DEPTH, xj);
+      fetch_w(st + DEPTH, wj);
+    }
+    __syncthreads();
+  };
+  static_assert(DEPTH == 3, "the loop below rotates three stage buffers");
+  for (int s0 = 0; s0 < nst; s0 += 3) {
+    step(s0, w0, x0, x1);
+    if (s0 + 1 >= nst) break;
+    step(s0 + 1, w1, x1, x2);
+    if (s0 + 2 >= nst) break;
+    step(s0 + 2, w2, x2, x0);
+  }
+
+  // group 1 hands its sums to group 0 (fixed order: group 0 + group 1)
+  if (kGroups == 2 && wg == 1) {
+#pragma unroll
+    for (int mat = 0; mat < MATS; ++mat)
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) *(f32x4*)&red[mat][cb][wt][lane][0] = acc[mat][cb];
+  }
+  __syncthreads();
+  // lane of group 0 holds Y[m = cb*16 + col][n = tile*16 + 4*grp + i] in acc[mat][cb][i]
+  const int n0 = tile * 16 + 4 * grp;
+  if (kGroups == 2 && wg == 0) {
+#pragma unroll
+    for (int mat = 0; mat < MATS; ++mat)
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) acc[mat][cb] += *(const f32x4*)&red[mat][cb][wt][lane][0];
+  }
+  if (p.k_split > 1) {
+    if (wg == 0) {
+      const size_t mat_stride = (size_t)p.m_pad * p.n;
+      float* out = p.part + (size_t)ks * MATS * mat_stride;
+#pragma unroll
+      for (int mat = 0; mat < MATS; ++mat)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+          *(f32x4*)(out + mat * mat_stride + (size_t)(cb * 16 + col) * p.n + n0) = acc[mat][cb];
+    }
+    return;
+  }
+  // one k-range: the epilogue runs here. Results pass through LDS (the
+  // activation buffers are free after the last barrier) so that each thread
+  // finishes whole (sequence, 4-column) groups of both flows.
+  float* res = reinterpret_cast<float*>(smem);  // [mat][m][kRowsPerWg columns]
+  if (wg == 0) {
+#pragma unroll
+    for (int mat = 0; mat < MATS; ++mat)
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+        *(f32x4*)(res + ((size_t)mat * NCB * 16 + cb * 16 + col) * kRowsPerWg + wt * 16 + 4 * grp) = acc[mat][cb];
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < p.batch * (kRowsPerWg / 4); idx += kGemvThreads) {
+    const int s = idx / (kRowsPerWg / 4), c4 = (idx - s * (kRowsPerWg / 4)) * 4;
+    float y[2][2][4];
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int mat = 0; mat < 2; ++mat) {
+        const bool have = f < p.flows && mat < MATS;
+        const int m = (f * p.cbf + (s >> 4)) * 16 + (s & 15);
+        const float4 v = have ? *(const float4*)(res + ((size_t)(mat < MATS ? mat : 0) * NCB * 16 + m) * kRowsPerWg + c4)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
+        y[f][mat][0] = v.x; y[f][mat][1] = v.y; y[f][mat][2] = v.z; y[f][mat][3] = v.w;
+      }
+    apply_epilogue(p, s, blockIdx.x * kRowsPerWg + c4, y);
+  }
+}
+
+// One thread per (sequence s, 4 columns): both flows' sums over the k-splits
+// (fixed order), then the epilogue.
+__global__ __launch_bounds__(64) void gemv_finalize_kernel(GemvParams p) {
+  const int n0 = (blockIdx.x * 64 + threadIdx.x) * 4;
+  const int s = blockIdx.y;
+  if (n0 >= p.n) return;
+  const size_t mat_stride = (size_t)p.m_pad * p.n;
+  const int mats = p.pair ? 2 : 1;
+  float y[2][2][4];
+#pragma unroll
+  for (int f = 0; f < 2; ++f)
+#pragma unroll
+    for (int mat = 0; mat < 2; ++mat)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) y[f][mat][j] = 0.f;
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+    if (f >= p.flows) break;
+    const size_t m = (size_t)(f * p.cbf * 16 + s);
+#pragma unroll
+    for (int mat = 0; mat < 2; ++mat) {
+      if (mat >= mats) break;
+      const float* src = p.part + mat * mat_stride + m * p.n + n0;
+#pragma unroll 4
+      for (int ks = 0; ks < p.k_split; ++ks) {
+        const float4 v = *(const float4*)(src + (size_t)ks * mats * mat_stride);
+        y[f][mat][0] += v.x; y[f][mat][1] += v.y; y[f][mat][2] += v.z; y[f][mat][3] += v.w;
+      }
+    }
+  }
+  apply_epilogue(p, s, n0, y);
 }
 
 hipError_t launch_gemv(const GemvParams& p, hipStream_t stream) {
@@ -269,12 +436,12 @@ hipError_t launch_gemv(const GemvParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_gemv_finalize(const GemvParams& p, hipStream_t stream) {
-  const dim3 grid((p.n + 255) / 256, p.batch), block(256);
+  const dim3 grid((p.n / 4 + 63) / 64, p.batch), block(64);
   hipLaunchKernelGGL(gemv_finalize_kernel, grid, block, 0, stream, p);
   return hipGetLastError();
 }
 
 size_t gemv_rows_per_workgroup() { return kRowsPerWg; }
-size_t gemv_chunk() { return kChunk; }
+size_t gemv_chunk() { return kStage; }
 
 }  // namespace dfa

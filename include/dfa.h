@@ -213,12 +213,13 @@ typedef enum dfa_epilogue {
 
 typedef struct dfa_gemv_desc {
   int32_t batch;         /* sequences = rows per flow: 1..32 (two flows), 1..64 (one flow) */
-  int32_t n;             /* output columns = rows of W, multiple of 128 */
+  int32_t n;             /* output columns = rows of W, multiple of 64 */
   int32_t k;             /* input columns = columns of W, multiple of 128 */
   int32_t num_flows;     /* 1 (primary only) or 2 */
   int32_t epilogue;      /* dfa_epilogue */
   int32_t x_exact_bf16;  /* 1: every activation value is exactly a bf16 value */
-  int32_t k_split;       /* k-ranges reduced through the workspace; 0 = library choice */
+  int32_t k_split;       /* k-ranges reduced through the workspace (1: none, the epilogue
+                            runs in the GEMV kernel); 0 = library choice */
 } dfa_gemv_desc;
 
 /* KV cache written by DFA_EPI_KV_APPEND (same layout as dfa_decode_attn reads). */
@@ -230,11 +231,12 @@ typedef struct dfa_kv_target {
   int32_t num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks;
 } dfa_kv_target;
 
-/* Workspace bytes of dfa_dual_gemv for `desc` (0 if invalid). */
+/* Workspace bytes of dfa_dual_gemv for `desc` (0 if invalid or if the plan has one k-range). */
 DFA_API size_t dfa_dual_gemv_workspace_size(const dfa_gemv_desc* desc);
 
 /*
- * Runs the GEMV and its epilogue on `stream` (two launches). Required
+ * Runs the GEMV and its epilogue on `stream` (one launch with one k-range, else
+ * two: the split GEMV and the fixed-order reduction with the epilogue). Required
  * pointers: w, x1, y1 (y1/y2 optional for KV_APPEND), x2 and y2 with two
  * flows, w2 for SWIGLU and KV_APPEND, res1 (res2 with two flows) for the
  * residual epilogues, kv for KV_APPEND. couple may be NULL. The auxiliary

@@ -95,6 +95,17 @@ def test_gemv_epilogues(batch, k_split):
     assert_close(y2, r2 + LY.couple(LY.linear(x2d, w), cpl.astype(np.float64), m1), what="coupled y2")
 
 
+@pytest.mark.parametrize("k_split", [1, 3])
+def test_gemv_rows_multiple_of_64(k_split):
+    rng = np.random.default_rng(11 + k_split)
+    x1, x2 = rng.standard_normal((2, 7, 384)).astype(np.float32)
+    w = rand_w(rng, 192, 384)
+    say(f"case gemv n=192 k_split={k_split}")
+    y1, y2 = gemv(dfa.DFA_EPI_NONE, w, x1, x2, k_split=k_split)
+    assert_close(y1, LY.linear(x1.astype(np.float64), w), what="n=192 y1")
+    assert_close(y2, LY.linear(x2.astype(np.float64), w), what="n=192 y2")
+
+
 @pytest.mark.parametrize("batch", [40, 64])
 def test_gemv_one_flow_wide_batch(batch):
     rng = np.random.default_rng(batch)
@@ -116,11 +127,45 @@ def test_exact_bf16_activations_skip_low_halves():
     assert_close(b1, LY.linear(x1.astype(np.float64), w), what="exact y1")
 
 
+@pytest.mark.parametrize("k_split", [1, 2])
+def test_gemv_kv_append(k_split):
+    """The primary-only append, in the GEMV kernel (one k-range) and after the split reduction."""
+    cfg = SMALL_LAYER.replace(num_kv_heads=2, hidden=384)
+    case = W.make_layer_case(cfg, 40 + k_split)
+    kd = cfg.num_kv_heads * cfg.head_dim
+    k_cache, v_cache = to_device(case.k_cache), to_device(case.v_cache)
+    table, ctx = to_device(case.block_table), to_device(case.ctx_lens)  # kept alive: kv holds raw addresses
+    kv = dfa.kv_target(k_cache, v_cache, table, ctx, cfg.num_kv_heads, cfg.head_dim, case.block_size,
+                       case.max_blocks_per_seq, case.k_cache.shape[0])
+    say(f"case gemv kv append k_split={k_split}")
+    y1, y2 = gemv(dfa.DFA_EPI_KV_APPEND, case.w["wk"], case.x1, w2_bits=case.w["wv"], x_exact=1, k_split=k_split,
+                  kv=kv, y_kv=True)
+    k_lin, v_lin = LY.linear(case.x1, case.w["wk"]), LY.linear(case.x1, case.w["wv"])
+    assert_close(y1, k_lin, what="appended k as float32")
+    assert_close(y2, v_lin, what="appended v as float32")
+    shape = (cfg.batch, cfg.num_kv_heads, cfg.head_dim)
+    ref_k, ref_v = LY.append_kv(case.k_cache, case.v_cache, case.block_table, case.ctx_lens,
+                                F.f64_to_bf16_bits(k_lin).reshape(shape), F.f64_to_bf16_bits(v_lin).reshape(shape),
+                                case.block_size)
+    n_app = cfg.batch * kd
+    for name, g, r, orig in (("k", k_cache, ref_k, case.k_cache), ("v", v_cache, ref_v, case.v_cache)):
+        g = g.cpu().numpy().view(np.uint16)
+        diff = g != r
+        assert diff.sum() <= n_app, name
+        if diff.any():
+            assert bf16_ulp_diff(g[diff], r[diff]).max() <= 1, name
+        assert (g != orig).sum() <= n_app, name
+
+
 def test_gemv_rejects_bad_shapes():
     d = dfa.GemvDesc(batch=33, n=128, k=128, num_flows=2, epilogue=0, x_exact_bf16=0, k_split=0)
     assert dfa.dfa_dual_gemv_workspace_size(d) == 0
-    d = dfa.GemvDesc(batch=4, n=100, k=128, num_flows=2, epilogue=0, x_exact_bf16=0, k_split=0)
+    d = dfa.GemvDesc(batch=4, n=96, k=128, num_flows=2, epilogue=0, x_exact_bf16=0, k_split=2)
     assert dfa.dfa_dual_gemv_workspace_size(d) == 0
+    d = dfa.GemvDesc(batch=4, n=192, k=128, num_flows=2, epilogue=0, x_exact_bf16=0, k_split=1)
+    assert dfa.dfa_dual_gemv_workspace_size(d) == 0  # valid; one k-range needs no workspace
+    d = dfa.GemvDesc(batch=4, n=192, k=256, num_flows=2, epilogue=0, x_exact_bf16=0, k_split=2)
+    assert dfa.dfa_dual_gemv_workspace_size(d) == 2 * 32 * 192 * 4  # 2 splits x 2 flows x 16 padded rows
 
 
 # ---------------------------------------------------------------- full layer

@@ -77,6 +77,11 @@ constexpr int kNT = 2;
 // weighted: the weights 2^(s - m_run) stay at most 2^kLazyRescale.
 constexpr float kLazyRescale = 8.f;
 
+// Waves per workgroup (8 measured no faster: the cache stream, not the
+// arithmetic between loads, sets the pace).
+constexpr int kAttnWaves = 4;
+constexpr int kAttnThreads = 64 * kAttnWaves;
+
 // Loads one chunk through buffer resources: a tile's base address is
 // wave-uniform (scalar registers), each lane's byte offsets within the tile
 // are fixed (koff for keys, voff for values), and the hardware returns zeros
@@ -131,14 +136,14 @@ struct QRaw<true> {
 };
 
 template <int D, int NRP, bool QF32>
-__global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnParams p) {
+__global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(AttnParams p) {
   constexpr int KS = D / 32;
   constexpr int DB = D / 16;
   constexpr bool PACKED = (NRP == 8);
   __shared__ int tbl[kMaxTableSlice];
-  __shared__ float sm[kWaves * NRP];
-  __shared__ float sl[kWaves * NRP];
-  __shared__ __attribute__((aligned(16))) float so[kWaves * NRP * D];
+  __shared__ float sm[kAttnWaves * NRP];
+  __shared__ float sl[kAttnWaves * NRP];
+  __shared__ __attribute__((aligned(16))) float so[kAttnWaves * NRP * D];
 
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -167,10 +172,10 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnParams p) {
       ar[st][1] = av[1];
     }
   }
-  const int jb0 = stage_split_table(p, b, s, tbl);
+  const int jb0 = stage_split_table<kAttnThreads>(p, b, s, tbl);
   __syncthreads();  // the table slice is read by every wave
   SplitRange r;
-  if (!split_bounds<D>(p, b, g, s, len_raw, r)) return;
+  if (!split_bounds<D, kAttnThreads>(p, b, g, s, len_raw, r)) return;
 
   // ---- first chunk's loads, then the query operands while they are in flight ----
   const int bs = 1 << p.bs_log2;
@@ -304,16 +309,16 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnParams p) {
     }
   };
 
-  // Wave w takes chunks w, w + kWaves, ...; two register buffers alternate so
+  // Wave w takes chunks w, w + kAttnWaves, ...; two register buffers alternate so
   // that the next chunk's loads are in flight while the current one is used.
-  for (; c < nchunks; c += 2 * kWaves) {
-    if (c + kWaves < nchunks)
-      load_chunk<D>(p, kc, vc, tbl, jb0, r.start + 32 * (c + kWaves), r.end, koff, voff, cb);
+  for (; c < nchunks; c += 2 * kAttnWaves) {
+    if (c + kAttnWaves < nchunks)
+      load_chunk<D>(p, kc, vc, tbl, jb0, r.start + 32 * (c + kAttnWaves), r.end, koff, voff, cb);
     process(ca, c);
-    if (c + kWaves >= nchunks) break;
-    if (c + 2 * kWaves < nchunks)
-      load_chunk<D>(p, kc, vc, tbl, jb0, r.start + 32 * (c + 2 * kWaves), r.end, koff, voff, ca);
-    process(cb, c + kWaves);
+    if (c + kAttnWaves >= nchunks) break;
+    if (c + 2 * kAttnWaves < nchunks)
+      load_chunk<D>(p, kc, vc, tbl, jb0, r.start + 32 * (c + 2 * kAttnWaves), r.end, koff, voff, ca);
+    process(cb, c + kAttnWaves);
   }
 
   // ---- wave state to LDS, then merge the waves ----
@@ -335,7 +340,7 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnParams p) {
     }
   }
   __syncthreads();
-  merge_waves<D, NRP>(p, b, g, s, sm, sl, so);
+  merge_waves<D, NRP, kAttnWaves>(p, b, g, s, sm, sl, so);
 }
 
 // LDS a workgroup of attn_bf16_kernel<D, NRP> declares, and the dynamic LDS
@@ -347,13 +352,13 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnParams p) {
 template <int D, int NRP>
 constexpr size_t one_per_cu_lds() {
   constexpr size_t kCuLds = 160 * 1024;
-  constexpr size_t stat = kMaxTableSlice * 4 + 2 * kWaves * NRP * 4 + kWaves * NRP * D * 4;
+  constexpr size_t stat = kMaxTableSlice * 4 + 2 * kAttnWaves * NRP * 4 + kAttnWaves * NRP * D * 4;
   return stat > kCuLds / 2 ? 0 : kCuLds / 2 + 256 - stat;
 }
 
 hipError_t launch_attn_bf16(const AttnParams& p, int head_dim, int rows_padded, hipStream_t stream,
                             const KernelEvents& ev) {
-  const dim3 grid(p.n_splits, p.hkv, p.batch), block(kThreads);
+  const dim3 grid(p.n_splits, p.hkv, p.batch), block(kAttnThreads);
 #define DFA_ATTN_CASE(D_, NRP_)                                                                              \
   if (head_dim == D_ && rows_padded == NRP_)                                                                 \
     return p.q_f32 ? launch_kernel(attn_bf16_kernel<D_, NRP_, true>, grid, block, stream, ev, p,              \

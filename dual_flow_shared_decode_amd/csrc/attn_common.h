@@ -120,21 +120,21 @@ __device__ __forceinline__ bool split_bounds(const AttnParams& p, int b, int g, 
 
 // Cross-wave merge. Each wave w left, for each of its rows, the running max
 // sm[w*NRP+row], sum sl[w*NRP+row] and unnormalised output so[(w*NRP+row)*D+d]
-// (all in base-2 units). Writes the normalised output in direct mode (one
+// (all in base-2 units), for waves w < NW. Writes the normalised output in direct mode (one
 // split per sequence), otherwise the split record (O, m, l) of each row.
-template <int D, int NRP>
+template <int D, int NRP, int NW = kWaves>
 __device__ __forceinline__ void merge_waves(const AttnParams& p, int b, int g, int s,
                                             const float* sm, const float* sl, const float* so) {
   const int nr = p.flows * p.group;
   const bool to_out = p.direct;
-  for (int idx = threadIdx.x; idx < nr * D; idx += kThreads) {
+  for (int idx = threadIdx.x; idx < nr * D; idx += 64 * NW) {
     const int row = idx / D, d = idx - row * D;
     float mx = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, sm[w * NRP + row]);
+    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, sm[w * NRP + row]);
     float o = 0.f, l = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float e = fast_exp2(sm[w * NRP + row] - mx);
       o += e * so[(w * NRP + row) * D + d];
       l += e * sl[w * NRP + row];

@@ -27,8 +27,10 @@
 // is streamed in 128-column stages, three in flight: a stage's weights (in
 // registers) and raw activations (in registers, first touched when they are
 // converted) are fetched together, and per stage the workgroup converts the
-// next stage's activations to hi/lo bf16 in LDS (double-buffered), laid out
-// as the B operand ([block][k/8][16][8]). With one k-range the epilogue runs
+// next stage's activations to hi/lo bf16 in LDS (double-buffered; per column
+// block, row r's 8-column groups are stored in slot group ^ r so that both
+// the conversion's writes and the MFMA operand reads are free of bank
+// conflicts). With one k-range the epilogue runs
 // in the same kernel; otherwise partial sums go to the workspace
 // [k-split][matrix][row][n] and gemv_finalize adds them in a fixed order and
 // applies the epilogue (so the primary flow's results never depend on the
@@ -73,6 +75,7 @@ constexpr int kGemvThreads = 64 * kGemvWaves;
 constexpr int kRowsPerWg = 16 * kTiles;
 constexpr int kStage = 128;                    // k columns per pipeline stage
 constexpr int kSteps = kStage / 32;            // MFMA k-steps per stage
+static_assert(kStage / 8 == 16, "the LDS swizzle pairs 16 column groups with 16 rows");
 constexpr int kHalfSteps = kSteps / kGroups;   // k-steps of one wave group per stage
 }  // namespace
 
@@ -197,7 +200,7 @@ __device__ __forceinline__ void fetch_x(const GemvParams& p, int k_begin, int st
   }
 }
 
-// Converts a stage to hi (and lo) bf16 B operands in LDS: xs[h][cb][k/8][16][8].
+// Converts a stage to hi (and lo) bf16 B operands in LDS: xs[h][cb][row][k/8 ^ row][8].
 template <int NCB, int NH>
 __device__ __forceinline__ void put_x(const XStage<NCB>& xr, uint16_t* xs) {
 #pragma unroll
@@ -215,7 +218,11 @@ __device__ __forceinline__ void put_x(const XStage<NCB>& xr, uint16_t* xs) {
       lo[4] = (__bf16)(q1.x - (float)hi[4]); lo[5] = (__bf16)(q1.y - (float)hi[5]);
       lo[6] = (__bf16)(q1.z - (float)hi[6]); lo[7] = (__bf16)(q1.w - (float)hi[7]);
     }
-    const size_t off = (((size_t)(m >> 4) * (kStage / 8) + kg) * 16 + (m & 15)) * 8;
+    // row r of column block cb, 8-column group kg -> slot kg ^ r of row r: the
+    // 16 groups a row's threads write land in 16 different banks, and so do
+    // the 16 rows an MFMA operand read takes from one group
+    const int r = m & 15;
+    const size_t off = (((size_t)(m >> 4) * 16 + r) * (kStage / 8) + (kg ^ r)) * 8;
     if (item < XStage<NCB>::kTotal) {
       *(bf16x8*)(xs + off) = hi;
       if (NH == 2) *(bf16x8*)(xs + (size_t)NCB * kStage * 16 + off) = lo;
@@ -240,7 +247,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvParams p) {
   constexpr size_t kResBytes = MATS * NCB * 16 * kRowsPerWg * sizeof(float);
   __shared__ __attribute__((aligned(16))) unsigned char smem[kXsBytes > kResBytes ? kXsBytes : kResBytes];
   __shared__ __attribute__((aligned(16))) float red[kGroups == 2 ? MATS : 1][NCB][kTiles][64][4];  // group 1's sums
-  auto xs = reinterpret_cast<uint16_t(*)[NH][NCB][kStage / 8][16][8]>(smem);
+  auto xs = reinterpret_cast<uint16_t(*)[NH][NCB][16][kStage / 8][8]>(smem);  // [buf][h][cb][row][group ^ row][8]
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
@@ -303,7 +310,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvParams p) {
       for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
         for (int h = 0; h < NH; ++h)
-          xb[k2][cb][h] = *(const bf16x8*)&xs[buf][h][cb][4 * (wg * kHalfSteps + k2) + grp][col][0];
+          xb[k2][cb][h] = *(const bf16x8*)&xs[buf][h][cb][col][(4 * (wg * kHalfSteps + k2) + grp) ^ col][0];
 #pragma unroll
     for (int k2 = 0; k2 < kHalfSteps; ++k2)
 #pragma unroll

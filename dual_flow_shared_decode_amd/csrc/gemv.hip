@@ -300,7 +300,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvParams p) {
   __syncthreads();
   // stage st: multiply with weights wj (B operands in xs[st & 1]); meanwhile
   // convert stage st + 1 from xn and fetch stage st + DEPTH into wj, xj
-  auto step = [&](int st, WStage& wj, XStage<NCB>& xj, const XStage<NCB>& xn) __attribute__((always_inline)) {
+  auto step = [&](int st, WStage& wj, XStage<NCB>& xj, const XStage<NCB>& xn, bool fetch) __attribute__((always_inline)) {
     const int buf = st & 1;
     if (st + 1 < nst) put_x<NCB, NH>(xn, &xs[buf ^ 1][0][0][0][0][0]);
     bf16x8 xb[kHalfSteps][NCB][NH];
@@ -320,19 +320,29 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvParams p) {
 #pragma unroll
           for (int mat = 0; mat < MATS; ++mat)
             acc[mat][cb] = mfma(wj.a[mat][k2], xb[k2][cb][h], acc[mat][cb]);
-    if (st + DEPTH < nst) {
+    if (fetch) {
       fetch_x<NCB>(p, k_begin, st + DEPTH, xj);
       fetch_w(st + DEPTH, wj);
     }
     __syncthreads();
   };
-  static_assert(DEPTH == 3, "the loop below rotates three stage buffers");
-  for (int s0 = 0; s0 < nst; s0 += 3) {
-    step(s0, w0, x0, x1);
+  static_assert(DEPTH == 3, "the loops below rotate three stage buffers");
+  // Steady state: every step fetches, so each iteration issues the same loads
+  // and the waits before a stage's first use cover only that stage's loads
+  // (with fetches that may or may not happen, the counts differ between
+  // paths and the compiler must wait for all outstanding loads).
+  int s0 = 0;
+  for (; s0 + 2 + DEPTH < nst; s0 += 3) {
+    step(s0, w0, x0, x1, true);
+    step(s0 + 1, w1, x1, x2, true);
+    step(s0 + 2, w2, x2, x0, true);
+  }
+  for (; s0 < nst; s0 += 3) {  // the last stages: fetch while stages remain
+    step(s0, w0, x0, x1, s0 + DEPTH < nst);
     if (s0 + 1 >= nst) break;
-    step(s0 + 1, w1, x1, x2);
+    step(s0 + 1, w1, x1, x2, s0 + 1 + DEPTH < nst);
     if (s0 + 2 >= nst) break;
-    step(s0 + 2, w2, x2, x0);
+    step(s0 + 2, w2, x2, x0, s0 + 2 + DEPTH < nst);
   }
 
   // group 1 hands its sums to group 0 (fixed order: group 0 + group 1)

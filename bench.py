@@ -264,7 +264,7 @@ def main():
         return start.elapsed_time(end) / steps, wall
 
     def kernel_ms(step, steps):
-        """Mean duration of the attention kernel, from events recorded by each launch's dispatch."""
+        """Durations (ms) of the attention kernel, from events recorded by each launch's dispatch."""
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
         for e0, e1 in evs:  # the events must exist before a dispatch can record them
             e0.record(stream)
@@ -273,12 +273,16 @@ def main():
         for i, ev in enumerate(evs):
             step(i, ev)
         torch.cuda.synchronize()
-        return sum(e0.elapsed_time(e1) for e0, e1 in evs) / steps
+        return [e0.elapsed_time(e1) for e0, e1 in evs]
 
     d2, step2 = runner(2)
     log(f"split length {dfa.dfa_decode_attn_split_len(d2)}, {dfa.dfa_decode_attn_num_splits(d2)} splits; timing")
     ms, wall = timed(step2, args.steps, args.warmup)
-    kern_ms = kernel_ms(step2, args.steps)
+    kern_all = sorted(kernel_ms(step2, args.steps))
+    kern_ms = sum(kern_all) / len(kern_all)
+
+    def pct(v, q):  # nearest-rank percentile of a sorted list
+        return v[min(len(v) - 1, max(0, int(math.ceil(q / 100 * len(v))) - 1))]
     step_bytes = kern_bytes = algorithmic_bytes(case, 2)
     rows = cfg.num_q_heads // cfg.num_kv_heads * 2
     kernel_name = (f"attn_bf16_kernel<{cfg.head_dim}, {8 if rows <= 8 else 16}, false>" if cfg.dtype == "bf16"
@@ -307,7 +311,8 @@ def main():
            "roofline": {"bound": "hbm", "kernel": kernel_name, "achieved": kern_gbps,
                         "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": kern_gbps / HBM_PEAK_GBPS,
                         "traffic": measured_traffic(cfg.name), "algorithmic_bytes_per_launch": kern_bytes,
-                        "avg_launch_us": kern_ms * 1e3}}
+                        "avg_launch_us": kern_ms * 1e3, "median_launch_us": pct(kern_all, 50) * 1e3,
+                        "p10_launch_us": pct(kern_all, 10) * 1e3, "p90_launch_us": pct(kern_all, 90) * 1e3}}
 
     if args.copy_calibration:
         n = args.copy_calibration << 20
@@ -321,7 +326,7 @@ def main():
     if not args.no_extras:
         d1, step1 = runner(1)
         ms1, _ = timed(step1, args.steps, args.warmup)
-        kern1 = kernel_ms(step1, args.steps)
+        kern1 = sum(kernel_ms(step1, args.steps)) / args.steps
         rec["ms_per_step_one_flow"] = ms1
         rec["aux_increment"] = ms / ms1 - 1.0
         rec["aux_increment_kernel"] = kern_ms / kern1 - 1.0

@@ -9,6 +9,8 @@ aux == primary without coupling, one position returns its value, paging and
 split plans do not change the result). Unused cache slots hold NaN, so any read
 past a sequence shows up as a non-finite output.
 """
+import copy
+
 import numpy as np
 import pytest
 import torch
@@ -160,6 +162,34 @@ def test_physical_block_order_does_not_matter():
                                                                       case2.block_table, 5)
     o1b, o2b = run_attn(case2, split_len=64)
     assert np.array_equal(o1a, o1b) and np.array_equal(o2a, o2b)
+
+
+def test_paged_equals_contiguous():
+    """The same sequences in 16-position blocks (shuffled) and in one block each give the same bits."""
+    cfg = W.C2.replace(batch=3, ctx_lens=(100, 333, 64), capacity=512)
+    contiguous = W.make_attn_case(cfg, 2013)
+    paged = W.make_attn_case(cfg.replace(block_size=16, shuffle_blocks=True), 2013)
+    say("case paged vs contiguous")
+    assert np.array_equal(W.bf16_bits_to_f32(contiguous.q1), W.bf16_bits_to_f32(paged.q1))
+    a1, a2 = run_attn(contiguous, split_len=128)
+    b1, b2 = run_attn(paged, split_len=128)
+    assert np.array_equal(a1, b1) and np.array_equal(a2, b2)
+
+
+def test_gqa_equals_mha_with_repeated_kv_heads():
+    """Grouped-query attention is multi-head attention with each kv head repeated G times."""
+    gqa = W.make_attn_case(W.C2.replace(batch=2, num_q_heads=8, num_kv_heads=2, ctx_lens=(300, 77),
+                                        capacity=512), 2014)
+    mha = copy.copy(gqa)
+    mha.cfg = gqa.cfg.replace(num_kv_heads=8)
+    mha.k_cache = np.ascontiguousarray(np.repeat(gqa.k_cache, 4, axis=1))
+    mha.v_cache = np.ascontiguousarray(np.repeat(gqa.v_cache, 4, axis=1))
+    say("case gqa vs repeated-kv mha")
+    g1, g2 = run_attn(gqa, split_len=128)
+    m1, m2 = run_attn(mha, split_len=128)
+    # rows share a wave-wide rescale decision, so the two layouts may round differently
+    assert_close(m1, g1, tol=1e-6, what="mha o1 vs gqa o1")
+    assert_close(m2, g2, tol=1e-6, what="mha o2 vs gqa o2")
 
 
 def test_split_plans_agree():

@@ -116,6 +116,20 @@ def test_gemv_one_flow_wide_batch(batch):
     assert_close(y1, LY.linear(x1.astype(np.float64), w), what="one-flow y1")
 
 
+@pytest.mark.parametrize("k_split", [1, 2])
+def test_gemv_zero_weights_return_the_residual(k_split):
+    rng = np.random.default_rng(21 + k_split)
+    x1, x2 = rng.standard_normal((2, 9, 256)).astype(np.float32)
+    r1, r2 = rng.standard_normal((2, 9, 128)).astype(np.float32)
+    cpl = rng.standard_normal(128).astype(np.float32)
+    w = np.zeros((128, 256), dtype=np.uint16)  # +0.0 in bf16
+    say(f"case gemv zero weights k_split={k_split}")
+    y1, y2 = gemv(dfa.DFA_EPI_RESIDUAL, w, x1, x2, res1=r1, res2=r2, k_split=k_split)
+    assert np.array_equal(y1, r1) and np.array_equal(y2, r2)
+    y1, y2 = gemv(dfa.DFA_EPI_RESIDUAL_COUPLED, w, x1, x2, couple=cpl, res1=r1, res2=r2, k_split=k_split)
+    assert np.array_equal(y1, r1) and np.array_equal(y2, r2)
+
+
 def test_exact_bf16_activations_skip_low_halves():
     rng = np.random.default_rng(7)
     x1, x2 = (W.bf16_bits_to_f32(W.f32_to_bf16_bits(rng.standard_normal((2, 9, 512)).astype(np.float32))))

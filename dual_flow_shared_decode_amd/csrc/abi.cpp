@@ -194,6 +194,9 @@ dfa_status attn_impl(const dfa_attn_desc* desc, const void* q1, const void* q2, 
   p.ctx_add = ctx_add;
   if (ns == 1) {
     p.direct = 1;
+    // one workgroup per (sequence, kv head): take sequences longest first (the
+    // kernel ranks up to 64 lengths in one wave)
+    p.longest_first = desc->batch > 1 && desc->batch <= 64;
     p.o1 = o1;
     p.o2 = desc->num_flows == 2 ? o2 : nullptr;
     return launch_split_stage(desc, p, hs, events);

@@ -110,6 +110,23 @@ __device__ __forceinline__ void load_chunk(const AttnParams& p, const uint16_t* 
   }
 }
 
+// The sequence with the rank-th largest length (ties: lower index first), for
+// batches of at most 64 (one length per lane; every wave computes the same
+// permutation). Workgroups are dispatched in blockIdx order and one runs per
+// CU at a time, so with one split per sequence taking sequences longest first
+// (longest-processing-time order) keeps a long sequence from starting last.
+// `mine` is ctx[lane] (INT_MIN for lanes past the batch).
+__device__ __forceinline__ int longest_first(const AttnParams& p, int mine, int rank) {
+  const int lane = threadIdx.x & 63;
+  int above = 0;
+  for (int j = 0; j < p.batch; ++j) {
+    const int other = __builtin_amdgcn_readlane(mine, j);
+    above += (other > mine) || (other == mine && j < lane);
+  }
+  const unsigned long long hit = __ballot(lane < p.batch && above == rank);
+  return hit ? (int)__builtin_ctzll(hit) : rank;
+}
+
 // Raw query operand of one lane and k-step: 8 consecutive dimensions, as
 // stored (bf16 or float32).
 template <bool QF32>
@@ -145,7 +162,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(AttnParams p) {
   __shared__ float sl[kAttnWaves * NRP];
   __shared__ __attribute__((aligned(16))) float so[kAttnWaves * NRP * D];
 
-  const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int s = blockIdx.x, g = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, grp = lane >> 4;
   const int row = PACKED ? (n & 7) : n;
@@ -155,24 +172,40 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(AttnParams p) {
   // ---- prologue: the length, the queries and the split's block-table slice
   // are independent loads, issued together; the first cache loads wait only
   // for the table. Padding rows (row >= nr) load row nr - 1 and are zeroed. ----
-  const int len_raw = p.ctx[b];
   const int rr = min(row, nr - 1);
   const int f = rr / p.group, h = g * p.group + (rr - f * p.group);
-  const size_t qoff = ((size_t)b * p.hq + h) * D;
   QRaw<QF32> q1r[KS], q2r[KS];
   float4 ar[KS][2];
+  int jb0 = 0;
+  auto load_prologue = [&](int bb) __attribute__((always_inline)) {
+    const size_t qoff = ((size_t)bb * p.hq + h) * D;
 #pragma unroll
-  for (int st = 0; st < KS; ++st) {
-    const int d0 = 32 * st + 8 * grp;
-    q1r[st].load(p.q1, qoff + d0);
-    if (two) {
-      q2r[st].load(p.q2, qoff + d0);
-      const float4* av = (const float4*)(p.a + (size_t)h * D + d0);
-      ar[st][0] = av[0];
-      ar[st][1] = av[1];
+    for (int st = 0; st < KS; ++st) {
+      const int d0 = 32 * st + 8 * grp;
+      q1r[st].load(p.q1, qoff + d0);
+      if (two) {
+        q2r[st].load(p.q2, qoff + d0);
+        const float4* av = (const float4*)(p.a + (size_t)h * D + d0);
+        ar[st][0] = av[0];
+        ar[st][1] = av[1];
+      }
+    }
+    jb0 = stage_split_table<kAttnThreads>(p, bb, s, tbl);
+  };
+  // With longest-first order the loads for sequence blockIdx.z go out while
+  // the lengths are ranked, and are issued again only if the ranking picks
+  // another sequence (so uniform lengths cost no extra latency).
+  int b = blockIdx.z;
+  const int mine = p.longest_first && lane < p.batch ? p.ctx[lane] : INT_MIN;
+  load_prologue(b);
+  if (p.longest_first) {
+    const int bl = longest_first(p, mine, b);
+    if (bl != b) {
+      b = bl;
+      load_prologue(b);
     }
   }
-  const int jb0 = stage_split_table<kAttnThreads>(p, b, s, tbl);
+  const int len_raw = p.ctx[b];
   __syncthreads();  // the table slice is read by every wave
   SplitRange r;
   if (!split_bounds<D, kAttnThreads>(p, b, g, s, len_raw, r)) return;

@@ -32,6 +32,7 @@ struct AttnParams {
   int32_t ctx_add;     // added to every ctx_lens entry (1 when attending a just-appended position)
   int32_t direct;      // 1: one split per sequence; normalise and write o1/o2
   int32_t q_f32;       // Q element type is float32 (else bf16)
+  int32_t longest_first;  // 1: workgroup z takes sequences in descending length order
 };
 
 struct CombineParams {

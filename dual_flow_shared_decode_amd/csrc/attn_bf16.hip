@@ -20,10 +20,12 @@
 // grp = l / 16 of each operand; result (m = 4*grp + i, n) is lane l, register i):
 //   scores   S^T[pos][row] = K[pos][:] . Q[row][:]   v_mfma_f32_16x16x32_bf16,
 //            A = keys (lane: position n, dims 32*st + 8*grp ..+7), B = queries
-//   output   O^T[dim][row] += V^T[dim][pos] . P^T     v_mfma_f32_16x16x16_bf16,
-//            A = values (lane: dim 16*db + n, positions 4*grp ..+3), B = weights
-// The score result of a tile (lane: row n, positions 4*grp + i) is exactly the
-// weight operand the output product needs, so no data moves between lanes.
+//   output   O^T[dim][row] += V^T[dim][pos] . P^T     v_mfma_f32_16x16x32_bf16,
+//            A = values (lane: dim 16*db + n, positions 4*grp ..+3 of both
+//            tiles), B = weights
+// The score results of the two tiles (lane: row n, positions 4*grp + i of each)
+// are exactly the weight operand the output product needs, so no data moves
+// between lanes.
 //
 // Operands that are not exact bf16 (the scaled, coupled queries and the
 // softmax weights) are split as x = hi + lo with hi = bf16(x) and
@@ -40,8 +42,8 @@
 namespace dfa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float dpp_ror8(float x) {
@@ -53,14 +55,10 @@ __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f3
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ f32x4 mfma16(const bf16x4& a, const bf16x4& b, const f32x4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
-
 template <int D>
 struct Chunk {
   bf16x8 k[2][D / 32];  // per tile: keys of position n, one 8-dim group per k-step
-  bf16x4 v[2][D / 16];  // per tile: four positions 4*grp.. of dim 16*db + n
+  u32x4 v[D / 16];      // dim 16*db + n: positions 4*grp.. of tile 0 (words 0-1), then of tile 1 (words 2-3)
 };
 
 // First position of tile u of the chunk at t0, moved back onto the last tile
@@ -105,8 +103,11 @@ __device__ __forceinline__ void load_chunk(const AttnParams& p, const uint16_t* 
     for (int st = 0; st < D / 32; ++st)
       ch.k[u][st] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, koff + st * 1024, 0, kNT));
 #pragma unroll
-    for (int db = 0; db < D / 16; ++db)
-      ch.v[u][db] = __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(rv, voff + db * 512, 0, kNT));
+    for (int db = 0; db < D / 16; ++db) {
+      const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv, voff + db * 512, 0, kNT));
+      ch.v[db][2 * u] = w[0];
+      ch.v[db][2 * u + 1] = w[1];
+    }
   }
 }
 
@@ -158,8 +159,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(AttnParams p) {
   constexpr int DB = D / 16;
   constexpr bool PACKED = (NRP == 8);
   __shared__ int tbl[kMaxTableSlice];
-  __shared__ float sm[kAttnWaves * NRP];
-  __shared__ float sl[kAttnWaves * NRP];
+  __shared__ __attribute__((aligned(16))) float sm[kAttnWaves * NRP];
+  __shared__ __attribute__((aligned(16))) float sl[kAttnWaves * NRP];
   __shared__ __attribute__((aligned(16))) float so[kAttnWaves * NRP * D];
 
   const int s = blockIdx.x, g = blockIdx.y;
@@ -288,10 +289,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(AttnParams p) {
           keep[h] = (tv + 2 * h < r.end ? 0x0000FFFFu : 0u) | (tv + 2 * h + 1 < r.end ? 0xFFFF0000u : 0u);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          u32x2 w = __builtin_bit_cast(u32x2, cur.v[u][db]);
-          w[0] &= keep[0];
-          w[1] &= keep[1];
-          cur.v[u][db] = __builtin_bit_cast(bf16x4, w);
+          cur.v[db][2 * u] &= keep[0];
+          cur.v[db][2 * u + 1] &= keep[1];
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -318,27 +317,27 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(AttnParams p) {
       psum += pv[j];
     }
     l_run += psum;
+    // Both tiles in one product: k-slot 8*grp + j of the lane is position
+    // 4*grp + j of tile 0 for j < 4 and 4*grp + j - 4 of tile 1 otherwise, in
+    // the values (words 0-1, 2-3) and in the weights (pv[j]) alike.
+    bf16x8 pa, pb;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      bf16x4 pa, pb;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float x = pv[4 * u + i];
-        const __bf16 hi = (__bf16)x;
-        const __bf16 lo = (__bf16)(x - (float)hi);
-        if (PACKED) {
-          pa[i] = (n < 8) ? hi : lo;
-        } else {
-          pa[i] = hi;
-          pb[i] = lo;
-        }
+    for (int j = 0; j < 8; ++j) {
+      const float x = pv[j];
+      const __bf16 hi = (__bf16)x;
+      const __bf16 lo = (__bf16)(x - (float)hi);
+      if (PACKED) {
+        pa[j] = (n < 8) ? hi : lo;
+      } else {
+        pa[j] = hi;
+        pb[j] = lo;
       }
+    }
 #pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[db] = mfma16(cur.v[u][db], pa, oacc[db]);
-      if (!PACKED) {
+    for (int db = 0; db < DB; ++db) oacc[db] = mfma(__builtin_bit_cast(bf16x8, cur.v[db]), pa, oacc[db]);
+    if (!PACKED) {
 #pragma unroll
-        for (int db = 0; db < DB; ++db) oacc[db] = mfma16(cur.v[u][db], pb, oacc[db]);
-      }
+      for (int db = 0; db < DB; ++db) oacc[db] = mfma(__builtin_bit_cast(bf16x8, cur.v[db]), pb, oacc[db]);
     }
   };
 
@@ -368,8 +367,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(AttnParams p) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) *(f32x4*)(dst + 16 * db) = oacc[db];
     if (grp == 0) {
-      sm[wave * NRP + row] = m_run;
-      sl[wave * NRP + row] = l_run;
+      sm[row * kAttnWaves + wave] = m_run;
+      sl[row * kAttnWaves + wave] = l_run;
     }
   }
   __syncthreads();

@@ -119,37 +119,46 @@ __device__ __forceinline__ bool split_bounds(const AttnParams& p, int b, int g, 
 }
 
 // Cross-wave merge. Each wave w left, for each of its rows, the running max
-// sm[w*NRP+row], sum sl[w*NRP+row] and unnormalised output so[(w*NRP+row)*D+d]
-// (all in base-2 units), for waves w < NW. Writes the normalised output in direct mode (one
-// split per sequence), otherwise the split record (O, m, l) of each row.
+// sm[row*NW+w], sum sl[row*NW+w] and unnormalised output so[(w*NRP+row)*D+d]
+// (all in base-2 units), for waves w < NW. Writes the normalised output in
+// direct mode (one split per sequence), otherwise the split record (O, m, l)
+// of each row. A thread takes four consecutive dimensions of a row, so every
+// LDS read and global store moves 16 bytes. A wave that took no position
+// left (m, l, O) = (-inf, 0, 0) and gets weight 0; some wave holds a position
+// of a non-empty split, so the row max is finite.
 template <int D, int NRP, int NW = kWaves>
 __device__ __forceinline__ void merge_waves(const AttnParams& p, int b, int g, int s,
                                             const float* sm, const float* sl, const float* so) {
+  static_assert(NW == 4, "the four waves' (m, l) of a row are read as one float4");
+  constexpr int D4 = D / 4;
   const int nr = p.flows * p.group;
-  const bool to_out = p.direct;
-  for (int idx = threadIdx.x; idx < nr * D; idx += 64 * NW) {
-    const int row = idx / D, d = idx - row * D;
-    float mx = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, sm[w * NRP + row]);
-    float o = 0.f, l = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float e = fast_exp2(sm[w * NRP + row] - mx);
-      o += e * so[(w * NRP + row) * D + d];
-      l += e * sl[w * NRP + row];
-    }
-    const int f = row / p.group, h = g * p.group + (row - f * p.group);
-    if (to_out) {
-      float* out = f ? p.o2 : p.o1;
-      out[((size_t)b * p.hq + h) * D + d] = o / l;
+  for (int idx = threadIdx.x; idx < nr * D4; idx += 64 * NW) {
+    const int row = idx / D4, d = 4 * (idx - row * D4);
+    const float4 m4 = *(const float4*)(sm + row * NW);
+    const float4 l4 = *(const float4*)(sl + row * NW);
+    const float mx = fmaxf(fmaxf(m4.x, m4.y), fmaxf(m4.z, m4.w));
+    const float e0 = fast_exp2(m4.x - mx), e1 = fast_exp2(m4.y - mx);
+    const float e2 = fast_exp2(m4.z - mx), e3 = fast_exp2(m4.w - mx);
+    const float4 v0 = *(const float4*)(so + (0 * NRP + row) * D + d);
+    const float4 v1 = *(const float4*)(so + (1 * NRP + row) * D + d);
+    const float4 v2 = *(const float4*)(so + (2 * NRP + row) * D + d);
+    const float4 v3 = *(const float4*)(so + (3 * NRP + row) * D + d);
+    float4 o;
+    o.x = e0 * v0.x + e1 * v1.x + e2 * v2.x + e3 * v3.x;
+    o.y = e0 * v0.y + e1 * v1.y + e2 * v2.y + e3 * v3.y;
+    o.z = e0 * v0.z + e1 * v1.z + e2 * v2.z + e3 * v3.z;
+    o.w = e0 * v0.w + e1 * v1.w + e2 * v2.w + e3 * v3.w;
+    const float l = e0 * l4.x + e1 * l4.y + e2 * l4.z + e3 * l4.w;
+    const int f = row >= p.group ? 1 : 0;  // at most two flows
+    const int h = g * p.group + row - f * p.group;
+    if (p.direct) {
+      const float inv = 1.f / l;
+      float* out = (f ? p.o2 : p.o1) + ((size_t)b * p.hq + h) * D + d;
+      *(float4*)out = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
     } else {
       float* rec = p.part + ((((size_t)b * p.hq + h) * p.flows + f) * p.n_splits + s) * (D + kRecPad);
-      rec[d] = o;
-      if (d == 0) {
-        rec[D] = mx;
-        rec[D + 1] = l;
-      }
+      *(float4*)(rec + d) = o;
+      if (d == 0) *(float2*)(rec + D) = make_float2(mx, l);
     }
   }
 }

@@ -24,9 +24,9 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnParams p) {
   constexpr int DJ = D / 64;
   __shared__ int tbl[kMaxTableSlice];
   __shared__ __attribute__((aligned(16))) float qs[kMaxRows * D];
-  __shared__ float sm[kWaves * kMaxRows];
-  __shared__ float sl[kWaves * kMaxRows];
-  __shared__ float so[kWaves * kMaxRows * D];
+  __shared__ __attribute__((aligned(16))) float sm[kWaves * kMaxRows];
+  __shared__ __attribute__((aligned(16))) float sl[kWaves * kMaxRows];
+  __shared__ __attribute__((aligned(16))) float so[kWaves * kMaxRows * D];
 
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   SplitRange r;
@@ -113,8 +113,8 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnParams p) {
   for (int i = 0; i < kMaxRows; ++i) {
     if (i < nr) {
       if (lane == 0) {
-        sm[wave * kMaxRows + i] = m[i];
-        sl[wave * kMaxRows + i] = l[i];
+        sm[i * kWaves + wave] = m[i];
+        sl[i * kWaves + wave] = l[i];
       }
 #pragma unroll
       for (int j = 0; j < DJ; ++j) so[(wave * kMaxRows + i) * D + lane + 64 * j] = acc[i][j];

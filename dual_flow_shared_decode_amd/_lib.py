@@ -48,7 +48,7 @@ class GemvDesc(ctypes.Structure):
 
     _fields_ = [("batch", ctypes.c_int32), ("n", ctypes.c_int32), ("k", ctypes.c_int32),
                 ("num_flows", ctypes.c_int32), ("epilogue", ctypes.c_int32), ("x_exact_bf16", ctypes.c_int32),
-                ("k_split", ctypes.c_int32)]
+                ("k_split", ctypes.c_int32), ("rows_per_wg", ctypes.c_int32)]
 
 
 class KvTarget(ctypes.Structure):

@@ -209,7 +209,7 @@ dfa_status attn_impl(const dfa_attn_desc* desc, const void* q1, const void* q2, 
 
 // ------------------------------------------------------------------ dual GEMV
 struct GemvPlan {
-  int32_t cbf, m_pad, k_split, k_range, mats;
+  int32_t cbf, m_pad, k_split, k_range, mats, rows_per_wg;
 };
 
 dfa_status validate_gemv(const dfa_gemv_desc* d, GemvPlan* plan) {
@@ -223,16 +223,27 @@ dfa_status validate_gemv(const dfa_gemv_desc* d, GemvPlan* plan) {
   if (d->epilogue == DFA_EPI_KV_APPEND && d->num_flows != 1)
     return fail(DFA_ERR_SHAPE, "the KV append is the primary flow's alone (num_flows 1)");
   if (d->k_split < 0) return fail(DFA_ERR_SHAPE, "k_split must be >= 0");
+  if (d->rows_per_wg != 0 && d->rows_per_wg != 64 && d->rows_per_wg != 128)
+    return fail(DFA_ERR_SHAPE, "rows_per_wg must be 0, 64 or 128");
+  if (d->rows_per_wg == 128 && d->n % 128 != 0) return fail(DFA_ERR_SHAPE, "rows_per_wg 128 needs n % 128 == 0");
   GemvPlan pl;
   pl.cbf = (d->batch + 15) / 16;  // 16-row activation blocks per flow; kernels exist for 1, 2, 4 blocks in all
   if (d->num_flows * pl.cbf > 4) return fail(DFA_ERR_UNSUPPORTED, "too many activation rows");
   if (pl.cbf == 3) pl.cbf = 4;    // one flow, 33..48 rows: padded to 64
   pl.m_pad = d->num_flows * pl.cbf * 16;
   const int64_t chunks = d->k / int64_t(dfa::gemv_chunk());
-  const int64_t row_groups = d->n / int64_t(dfa::gemv_rows_per_workgroup());
-  // Library choice: about one workgroup per compute unit (256); a matrix with
-  // at least 192 row groups runs unsplit, so its epilogue needs no second launch.
-  int64_t ks = d->k_split > 0 ? d->k_split : (row_groups >= 192 ? 1 : (256 + row_groups - 1) / row_groups);
+  // Library choice of the workgroup's rows (measured on MI355X, batch 32, two
+  // flows): 64, unless the matrix is large (at least 48 Mi elements) and too
+  // narrow to fill the chip unsplit at 64 rows -- then 128, so that the
+  // activations a workgroup loads per stage serve twice the weight rows and
+  // twice the weight bytes are in flight (4096 x 14336: 37.5 -> 33.4 us; a
+  // 14336-row matrix runs unsplit at 64 rows and is faster so).
+  const bool big = int64_t(d->n) * d->k >= (int64_t(48) << 20);
+  pl.rows_per_wg = d->rows_per_wg > 0 ? d->rows_per_wg : ((big && d->n % 128 == 0 && d->n / 64 < 192) ? 128 : 64);
+  const int64_t row_groups = d->n / pl.rows_per_wg;
+  // About one workgroup per compute unit (at most 256); a matrix with at
+  // least 192 row groups runs unsplit, so its epilogue needs no second launch.
+  int64_t ks = d->k_split > 0 ? d->k_split : (row_groups >= 192 ? 1 : std::max<int64_t>(1, 256 / row_groups));
   ks = std::min<int64_t>(ks, chunks);
   const int64_t chunks_per = (chunks + ks - 1) / ks;
   pl.k_range = int32_t(chunks_per * dfa::gemv_chunk());
@@ -309,6 +320,7 @@ dfa_status gemv_impl(const dfa_gemv_desc* d, const uint16_t* w, const uint16_t* 
     p.pair = pair;
     p.x_exact = d->x_exact_bf16 != 0;
     p.epilogue = d->epilogue;
+    p.rows_per_wg = pl.rows_per_wg;
     hipError_t e = dfa::launch_gemv(p, hs);
     if (e != hipSuccess) return fail(DFA_ERR_HIP, std::string("gemv launch: ") + hipGetErrorString(e));
     if (pl.k_split > 1) {
@@ -336,11 +348,11 @@ dfa_status plan_layer(const dfa_layer_desc* d, LayerPlan* lp) {
   p.attn = dfa_attn_desc{d->batch, d->num_q_heads, d->num_kv_heads, d->head_dim, d->block_size,
                          d->max_blocks_per_seq, d->num_blocks, d->max_ctx_len, 2, 0, d->scale, DFA_F32, DFA_BF16};
   const int32_t qd = d->num_q_heads * d->head_dim, kd = d->num_kv_heads * d->head_dim;
-  p.q = dfa_gemv_desc{d->batch, qd, d->hidden, 2, DFA_EPI_NONE, d->x_exact_bf16, 0};
-  p.kv = dfa_gemv_desc{d->batch, kd, d->hidden, 1, DFA_EPI_KV_APPEND, d->x_exact_bf16, 0};
-  p.o = dfa_gemv_desc{d->batch, d->hidden, qd, 2, DFA_EPI_RESIDUAL, 0, 0};
-  p.mlp_in = dfa_gemv_desc{d->batch, d->mlp, d->hidden, 2, DFA_EPI_SWIGLU, 0, 0};
-  p.mlp_out = dfa_gemv_desc{d->batch, d->hidden, d->mlp, 2, DFA_EPI_RESIDUAL_COUPLED, 0, 0};
+  p.q = dfa_gemv_desc{d->batch, qd, d->hidden, 2, DFA_EPI_NONE, d->x_exact_bf16, 0, 0};
+  p.kv = dfa_gemv_desc{d->batch, kd, d->hidden, 1, DFA_EPI_KV_APPEND, d->x_exact_bf16, 0, 0};
+  p.o = dfa_gemv_desc{d->batch, d->hidden, qd, 2, DFA_EPI_RESIDUAL, 0, 0, 0};
+  p.mlp_in = dfa_gemv_desc{d->batch, d->mlp, d->hidden, 2, DFA_EPI_SWIGLU, 0, 0, 0};
+  p.mlp_out = dfa_gemv_desc{d->batch, d->hidden, d->mlp, 2, DFA_EPI_RESIDUAL_COUPLED, 0, 0, 0};
   int32_t split = 0;
   dfa_status st = validate_attn(&p.attn, &split);
   if (st != DFA_OK) return st;

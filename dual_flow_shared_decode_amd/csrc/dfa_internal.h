@@ -56,6 +56,7 @@ struct GemvParams {
   float* y2;
   float* part;         // [k_split][mats][m_pad][n]
   int32_t batch, n, k, flows, cbf, m_pad, k_split, k_range, pair, x_exact, epilogue;
+  int32_t rows_per_wg;  // weight rows per workgroup: 64 or 128
   uint16_t* kv_k;      // KV append target
   uint16_t* kv_v;
   const int32_t* kv_table;
@@ -77,7 +78,6 @@ hipError_t launch_combine(const CombineParams& p, int head_dim, hipStream_t s);
 hipError_t launch_gemv(const GemvParams& p, hipStream_t s);
 hipError_t launch_gemv_finalize(const GemvParams& p, hipStream_t s);
 hipError_t launch_pack_weight(const uint16_t* w, uint16_t* wt, int n, int k, hipStream_t s);
-size_t gemv_rows_per_workgroup();
 size_t gemv_chunk();
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s);
 size_t stream_read_threads();

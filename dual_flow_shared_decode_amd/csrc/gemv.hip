@@ -68,15 +68,11 @@ hipError_t launch_pack_weight(const uint16_t* w, uint16_t* wt, int n, int k, hip
 
 // ---------------------------------------------------------------- GEMV
 namespace {
-constexpr int kTiles = 4;                      // 16-row weight tiles per workgroup
-constexpr int kGroups = 2;                     // wave groups sharing the tiles (1 or 2)
-constexpr int kGemvWaves = kGroups * kTiles;
+constexpr int kGemvWaves = 8;
 constexpr int kGemvThreads = 64 * kGemvWaves;
-constexpr int kRowsPerWg = 16 * kTiles;
 constexpr int kStage = 128;                    // k columns per pipeline stage
 constexpr int kSteps = kStage / 32;            // MFMA k-steps per stage
 static_assert(kStage / 8 == 16, "the LDS swizzle pairs 16 column groups with 16 rows");
-constexpr int kHalfSteps = kSteps / kGroups;   // k-steps of one wave group per stage
 }  // namespace
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
@@ -236,8 +232,12 @@ __device__ __forceinline__ void put_x(const XStage<NCB>& xr, uint16_t* xs) {
 // Wave w works on tile w % 4 with the k-steps of wave group w / 4: group g
 // takes k-steps 2g, 2g + 1 of every stage, so two waves per SIMD share the
 // stage's B operands and each holds half of the weights in flight.
-template <int NCB, bool PAIR, bool LO>
+template <int NCB, bool PAIR, bool LO, int TILES>
 __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvParams p) {
+  constexpr int kTiles = TILES;                  // 16-row weight tiles per workgroup (4 or 8)
+  constexpr int kGroups = kGemvWaves / kTiles;   // wave groups sharing the tiles (2 or 1)
+  constexpr int kRowsPerWg = 16 * kTiles;
+  constexpr int kHalfSteps = kSteps / kGroups;   // k-steps of one wave group per stage
   constexpr int NH = LO ? 2 : 1;
   constexpr int MATS = PAIR ? 2 : 1;
   constexpr int DEPTH = 3;  // stages in flight: weights and activations of each are fetched together
@@ -246,7 +246,8 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvParams p) {
   constexpr size_t kXsBytes = 2 * NH * NCB * (kStage / 8) * 16 * 8 * sizeof(uint16_t);
   constexpr size_t kResBytes = MATS * NCB * 16 * kRowsPerWg * sizeof(float);
   __shared__ __attribute__((aligned(16))) unsigned char smem[kXsBytes > kResBytes ? kXsBytes : kResBytes];
-  __shared__ __attribute__((aligned(16))) float red[kGroups == 2 ? MATS : 1][NCB][kTiles][64][4];  // group 1's sums
+  constexpr int kRed = kGroups == 2 ? 1 : 0;  // group 1's sums, handed to group 0
+  __shared__ __attribute__((aligned(16))) float red[kRed ? MATS : 1][kRed ? NCB : 1][kRed ? kTiles : 1][64][4];
   auto xs = reinterpret_cast<uint16_t(*)[NH][NCB][16][kStage / 8][8]>(smem);  // [buf][h][cb][row][group ^ row][8]
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -403,13 +404,19 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvParams p) {
 }
 
 // One thread per (sequence s, 4 columns): both flows' sums over the k-splits
-// (fixed order), then the epilogue.
-__global__ __launch_bounds__(64) void gemv_finalize_kernel(GemvParams p) {
-  const int n0 = (blockIdx.x * 64 + threadIdx.x) * 4;
-  const int s = blockIdx.y;
-  if (n0 >= p.n) return;
+// (fixed order), then the epilogue. KS > 0: exactly KS splits, every load
+// issued before the first add; KS == 0: any number, four loads at a time.
+constexpr int kFinalizeThreads = 256;
+
+template <int KS>
+__global__ __launch_bounds__(kFinalizeThreads) void gemv_finalize_kernel(GemvParams p) {
+  const int groups = p.n / 4;
+  const int item = blockIdx.x * kFinalizeThreads + threadIdx.x;
+  if (item >= p.batch * groups) return;
+  const int s = item / groups, n0 = (item - s * groups) * 4;
   const size_t mat_stride = (size_t)p.m_pad * p.n;
   const int mats = p.pair ? 2 : 1;
+  const int nks = KS > 0 ? KS : p.k_split;
   float y[2][2][4];
 #pragma unroll
   for (int f = 0; f < 2; ++f)
@@ -425,10 +432,20 @@ __global__ __launch_bounds__(64) void gemv_finalize_kernel(GemvParams p) {
     for (int mat = 0; mat < 2; ++mat) {
       if (mat >= mats) break;
       const float* src = p.part + mat * mat_stride + m * p.n + n0;
+      if (KS > 0) {
+        float4 v[KS > 0 ? KS : 1];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) v[ks] = *(const float4*)(src + (size_t)ks * mats * mat_stride);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          y[f][mat][0] += v[ks].x; y[f][mat][1] += v[ks].y; y[f][mat][2] += v[ks].z; y[f][mat][3] += v[ks].w;
+        }
+      } else {
 #pragma unroll 4
-      for (int ks = 0; ks < p.k_split; ++ks) {
-        const float4 v = *(const float4*)(src + (size_t)ks * mats * mat_stride);
-        y[f][mat][0] += v.x; y[f][mat][1] += v.y; y[f][mat][2] += v.z; y[f][mat][3] += v.w;
+        for (int ks = 0; ks < nks; ++ks) {
+          const float4 v = *(const float4*)(src + (size_t)ks * mats * mat_stride);
+          y[f][mat][0] += v.x; y[f][mat][1] += v.y; y[f][mat][2] += v.z; y[f][mat][3] += v.w;
+        }
       }
     }
   }
@@ -436,13 +453,15 @@ __global__ __launch_bounds__(64) void gemv_finalize_kernel(GemvParams p) {
 }
 
 hipError_t launch_gemv(const GemvParams& p, hipStream_t stream) {
-  const dim3 grid(p.n / kRowsPerWg, p.k_split), block(kGemvThreads);
+  const dim3 grid(p.n / p.rows_per_wg, p.k_split), block(kGemvThreads);
   const int ncb = p.flows * p.cbf;
   const bool lo = !p.x_exact;
-#define DFA_GEMV_CASE(NCB_, PAIR_, LO_)                                                          \
-  if (ncb == NCB_ && p.pair == PAIR_ && lo == LO_) {                                             \
-    hipLaunchKernelGGL((gemv_kernel<NCB_, PAIR_, LO_>), grid, block, 0, stream, p);              \
-    return hipGetLastError();                                                                    \
+  const int tiles = p.rows_per_wg / 16;
+#define DFA_GEMV_CASE(NCB_, PAIR_, LO_)                                                               \
+  if (ncb == NCB_ && p.pair == PAIR_ && lo == LO_) {                                                  \
+    if (tiles == 8) hipLaunchKernelGGL((gemv_kernel<NCB_, PAIR_, LO_, 8>), grid, block, 0, stream, p); \
+    else hipLaunchKernelGGL((gemv_kernel<NCB_, PAIR_, LO_, 4>), grid, block, 0, stream, p);            \
+    return hipGetLastError();                                                                         \
   }
   DFA_GEMV_CASE(1, false, false) DFA_GEMV_CASE(1, false, true) DFA_GEMV_CASE(1, true, false)
   DFA_GEMV_CASE(1, true, true) DFA_GEMV_CASE(2, false, false) DFA_GEMV_CASE(2, false, true)
@@ -453,12 +472,20 @@ hipError_t launch_gemv(const GemvParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_gemv_finalize(const GemvParams& p, hipStream_t stream) {
-  const dim3 grid((p.n / 4 + 63) / 64, p.batch), block(64);
-  hipLaunchKernelGGL(gemv_finalize_kernel, grid, block, 0, stream, p);
+  const dim3 grid((p.batch * (p.n / 4) + kFinalizeThreads - 1) / kFinalizeThreads), block(kFinalizeThreads);
+  switch (p.k_split) {
+#define DFA_FINALIZE_CASE(N)                                                      \
+  case N:                                                                         \
+    hipLaunchKernelGGL((gemv_finalize_kernel<N>), grid, block, 0, stream, p);     \
+    break;
+    DFA_FINALIZE_CASE(2) DFA_FINALIZE_CASE(3) DFA_FINALIZE_CASE(4) DFA_FINALIZE_CASE(8) DFA_FINALIZE_CASE(16)
+#undef DFA_FINALIZE_CASE
+    default:
+      hipLaunchKernelGGL((gemv_finalize_kernel<0>), grid, block, 0, stream, p);
+  }
   return hipGetLastError();
 }
 
-size_t gemv_rows_per_workgroup() { return kRowsPerWg; }
 size_t gemv_chunk() { return kStage; }
 
 }  // namespace dfa

@@ -220,6 +220,8 @@ typedef struct dfa_gemv_desc {
   int32_t x_exact_bf16;  /* 1: every activation value is exactly a bf16 value */
   int32_t k_split;       /* k-ranges reduced through the workspace (1: none, the epilogue
                             runs in the GEMV kernel); 0 = library choice */
+  int32_t rows_per_wg;   /* weight rows per workgroup: 64, or 128 (needs n % 128 == 0);
+                            0 = library choice. Results do not depend on it. */
 } dfa_gemv_desc;
 
 /* KV cache written by DFA_EPI_KV_APPEND (same layout as dfa_decode_attn reads). */

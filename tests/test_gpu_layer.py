@@ -49,11 +49,12 @@ def test_pack_weight_layout():
 
 
 def gemv(epi, w_bits, x1, x2=None, w2_bits=None, couple=None, res1=None, res2=None, x_exact=0, k_split=0,
-         kv=None, y_kv=False):
+         kv=None, y_kv=False, rows=0):
     n, k = w_bits.shape
     flows = 1 if x2 is None else 2
     batch = x1.shape[0]
-    d = dfa.GemvDesc(batch=batch, n=n, k=k, num_flows=flows, epilogue=epi, x_exact_bf16=x_exact, k_split=k_split)
+    d = dfa.GemvDesc(batch=batch, n=n, k=k, num_flows=flows, epilogue=epi, x_exact_bf16=x_exact, k_split=k_split,
+                     rows_per_wg=rows)
     ws = torch.empty(max(dfa.dfa_dual_gemv_workspace_size(d) // 4, 4), dtype=torch.float32, device="cuda")
     t = lambda a: None if a is None else to_device(np.ascontiguousarray(a, dtype=np.float32))
     y1 = torch.full((batch, n), float("nan"), device="cuda") if (epi != dfa.DFA_EPI_KV_APPEND or y_kv) else None
@@ -68,8 +69,9 @@ def rand_w(rng, n, k, std=0.02):
     return W.f32_to_bf16_bits(rng.standard_normal((n, k)).astype(np.float32) * np.float32(std))
 
 
-@pytest.mark.parametrize("batch,k_split", [(1, 0), (17, 0), (32, 1), (32, 2), (5, 3)])
-def test_gemv_epilogues(batch, k_split):
+@pytest.mark.parametrize("batch,k_split,rows", [(1, 0, 0), (17, 0, 0), (32, 1, 0), (32, 2, 0), (5, 3, 0),
+                                               (32, 1, 128), (17, 2, 128), (1, 3, 128)])
+def test_gemv_epilogues(batch, k_split, rows):
     rng = np.random.default_rng(batch * 10 + k_split)
     n, k = 256, 384
     x1, x2 = rng.standard_normal((2, batch, k)).astype(np.float32)
@@ -77,19 +79,20 @@ def test_gemv_epilogues(batch, k_split):
     cpl = rng.standard_normal(n).astype(np.float32) * np.float32(0.1)
     w, w2 = rand_w(rng, n, k), rand_w(rng, n, k)
     x1d, x2d = x1.astype(np.float64), x2.astype(np.float64)
-    say(f"case gemv batch={batch} k_split={k_split}")
-    y1, y2 = gemv(dfa.DFA_EPI_NONE, w, x1, x2, k_split=k_split)
+    say(f"case gemv batch={batch} k_split={k_split} rows={rows}")
+    y1, y2 = gemv(dfa.DFA_EPI_NONE, w, x1, x2, k_split=k_split, rows=rows)
     assert_close(y1, LY.linear(x1d, w), what="none y1")
     assert_close(y2, LY.linear(x2d, w), what="none y2")
-    y1, y2 = gemv(dfa.DFA_EPI_RESIDUAL, w, x1, x2, res1=r1, res2=r2, k_split=k_split)
+    y1, y2 = gemv(dfa.DFA_EPI_RESIDUAL, w, x1, x2, res1=r1, res2=r2, k_split=k_split, rows=rows)
     assert_close(y1, r1 + LY.linear(x1d, w), what="residual y1")
     assert_close(y2, r2 + LY.linear(x2d, w), what="residual y2")
-    y1, y2 = gemv(dfa.DFA_EPI_SWIGLU, w, x1, x2, w2_bits=w2, couple=cpl, k_split=k_split)
+    y1, y2 = gemv(dfa.DFA_EPI_SWIGLU, w, x1, x2, w2_bits=w2, couple=cpl, k_split=k_split, rows=rows)
     z1 = LY.silu(LY.linear(x1d, w)) * LY.linear(x1d, w2)
     z2 = LY.couple(LY.silu(LY.linear(x2d, w)) * LY.linear(x2d, w2), cpl.astype(np.float64), z1)
     assert_close(y1, z1, what="swiglu z1")
     assert_close(y2, z2, what="swiglu z2'")
-    y1, y2 = gemv(dfa.DFA_EPI_RESIDUAL_COUPLED, w, x1, x2, couple=cpl, res1=r1, res2=r2, k_split=k_split)
+    y1, y2 = gemv(dfa.DFA_EPI_RESIDUAL_COUPLED, w, x1, x2, couple=cpl, res1=r1, res2=r2, k_split=k_split,
+                  rows=rows)
     m1 = LY.linear(x1d, w)
     assert_close(y1, r1 + m1, what="coupled y1")
     assert_close(y2, r2 + LY.couple(LY.linear(x2d, w), cpl.astype(np.float64), m1), what="coupled y2")
@@ -180,6 +183,9 @@ def test_gemv_rejects_bad_shapes():
     assert dfa.dfa_dual_gemv_workspace_size(d) == 0  # valid; one k-range needs no workspace
     d = dfa.GemvDesc(batch=4, n=192, k=256, num_flows=2, epilogue=0, x_exact_bf16=0, k_split=2)
     assert dfa.dfa_dual_gemv_workspace_size(d) == 2 * 32 * 192 * 4  # 2 splits x 2 flows x 16 padded rows
+    for rows, n in ((96, 256), (128, 192)):  # not 0/64/128; 128 rows need n % 128 == 0
+        d = dfa.GemvDesc(batch=4, n=n, k=256, num_flows=2, epilogue=0, x_exact_bf16=0, k_split=2, rows_per_wg=rows)
+        assert dfa.dfa_dual_gemv_workspace_size(d) == 0
 
 
 # ---------------------------------------------------------------- full layer

@@ -321,6 +321,8 @@ dfa_status gemv_impl(const dfa_gemv_desc* d, const uint16_t* w, const uint16_t* 
     p.x_exact = d->x_exact_bf16 != 0;
     p.epilogue = d->epilogue;
     p.rows_per_wg = pl.rows_per_wg;
+    p.w_seg1 = p.w_seg2 = w;  // one matrix
+    p.seg1_row = p.seg2_row = d->n;
     hipError_t e = dfa::launch_gemv(p, hs);
     if (e != hipSuccess) return fail(DFA_ERR_HIP, std::string("gemv launch: ") + hipGetErrorString(e));
     if (pl.k_split > 1) {
@@ -334,9 +336,70 @@ dfa_status gemv_impl(const dfa_gemv_desc* d, const uint16_t* w, const uint16_t* 
 // ------------------------------------------------------------------ decode layer
 struct LayerPlan {
   dfa_attn_desc attn;
-  dfa_gemv_desc q, kv, o, mlp_in, mlp_out;
+  dfa_gemv_desc qkv, o, mlp_in, mlp_out;
+  GemvPlan qkv_plan;
   size_t off_q, off_o, off_h, off_z, off_attn, off_gemv, total;
 };
+
+// The query, key and value projections as one GEMV over the rows [Wq; Wk; Wv]
+// (the three matrices stay separate in memory): both flows are computed for
+// every row (the weights are read once either way), the finalize stores both
+// flows' queries and appends the primary's keys and values to the cache.
+// Its plan always splits k, so that keys and values meet in the finalize.
+GemvPlan plan_qkv(const dfa_gemv_desc& d) {
+  GemvPlan pl;
+  validate_gemv(&d, &pl);
+  if (pl.k_split < 2) {
+    dfa_gemv_desc d2 = d;
+    d2.k_split = 2;
+    validate_gemv(&d2, &pl);
+  }
+  return pl;
+}
+
+dfa_status qkv_impl(const dfa_layer_desc* d, const GemvPlan& pl, const dfa_layer_weights* w, const float* x1,
+                    const float* x2, float* q1, float* q2, const dfa_kv_target& kv, void* workspace,
+                    hipStream_t hs) {
+  const int32_t qd = d->num_q_heads * d->head_dim, kd = d->num_kv_heads * d->head_dim;
+  dfa::GemvParams p{};
+  p.w = w->wq;
+  p.w_seg1 = w->wk;
+  p.w_seg2 = w->wv;
+  p.seg1_row = qd;
+  p.seg2_row = qd + kd;
+  p.q_cols = qd;
+  p.kv_cols = kd;
+  p.x1 = x1;
+  p.x2 = x2;
+  p.y1 = q1;
+  p.y2 = q2;
+  p.part = static_cast<float*>(workspace);
+  p.batch = d->batch;
+  p.n = qd + 2 * kd;
+  p.k = d->hidden;
+  p.flows = 2;
+  p.cbf = pl.cbf;
+  p.m_pad = pl.m_pad;
+  p.k_split = pl.k_split;
+  p.k_range = pl.k_range;
+  p.pair = 0;
+  p.x_exact = d->x_exact_bf16 != 0;
+  p.epilogue = dfa::kEpiQkv;
+  p.rows_per_wg = pl.rows_per_wg;
+  p.kv_k = static_cast<uint16_t*>(kv.k_cache);
+  p.kv_v = static_cast<uint16_t*>(kv.v_cache);
+  p.kv_table = kv.block_table;
+  p.kv_ctx = kv.ctx_lens;
+  p.kv_hkv = kv.num_kv_heads;
+  p.kv_head_dim = kv.head_dim;
+  p.kv_bs_log2 = log2i(kv.block_size);
+  p.kv_max_blocks = kv.max_blocks_per_seq;
+  p.kv_num_blocks = kv.num_blocks;
+  hipError_t e = dfa::launch_gemv(p, hs);
+  if (e == hipSuccess) e = dfa::launch_gemv_finalize(p, hs);
+  if (e != hipSuccess) return fail(DFA_ERR_HIP, std::string("qkv gemv launch: ") + hipGetErrorString(e));
+  return DFA_OK;
+}
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
@@ -348,8 +411,7 @@ dfa_status plan_layer(const dfa_layer_desc* d, LayerPlan* lp) {
   p.attn = dfa_attn_desc{d->batch, d->num_q_heads, d->num_kv_heads, d->head_dim, d->block_size,
                          d->max_blocks_per_seq, d->num_blocks, d->max_ctx_len, 2, 0, d->scale, DFA_F32, DFA_BF16};
   const int32_t qd = d->num_q_heads * d->head_dim, kd = d->num_kv_heads * d->head_dim;
-  p.q = dfa_gemv_desc{d->batch, qd, d->hidden, 2, DFA_EPI_NONE, d->x_exact_bf16, 0, 0};
-  p.kv = dfa_gemv_desc{d->batch, kd, d->hidden, 1, DFA_EPI_KV_APPEND, d->x_exact_bf16, 0, 0};
+  p.qkv = dfa_gemv_desc{d->batch, qd + 2 * kd, d->hidden, 2, DFA_EPI_NONE, d->x_exact_bf16, 0, 0};
   p.o = dfa_gemv_desc{d->batch, d->hidden, qd, 2, DFA_EPI_RESIDUAL, 0, 0, 0};
   p.mlp_in = dfa_gemv_desc{d->batch, d->mlp, d->hidden, 2, DFA_EPI_SWIGLU, 0, 0, 0};
   p.mlp_out = dfa_gemv_desc{d->batch, d->hidden, d->mlp, 2, DFA_EPI_RESIDUAL_COUPLED, 0, 0, 0};
@@ -357,12 +419,14 @@ dfa_status plan_layer(const dfa_layer_desc* d, LayerPlan* lp) {
   dfa_status st = validate_attn(&p.attn, &split);
   if (st != DFA_OK) return st;
   size_t gemv_ws = 0;
-  for (const dfa_gemv_desc* g : {&p.q, &p.kv, &p.o, &p.mlp_in, &p.mlp_out}) {
+  for (const dfa_gemv_desc* g : {&p.qkv, &p.o, &p.mlp_in, &p.mlp_out}) {
     GemvPlan gp;
     st = validate_gemv(g, &gp);
     if (st != DFA_OK) return st;
     gemv_ws = std::max(gemv_ws, gemv_workspace(g, gp));
   }
+  p.qkv_plan = plan_qkv(p.qkv);
+  gemv_ws = std::max(gemv_ws, gemv_workspace(&p.qkv, p.qkv_plan));
   const size_t B = size_t(d->batch);
   p.off_q = 0;
   p.off_o = p.off_q + align256(2 * B * qd * sizeof(float));
@@ -430,14 +494,11 @@ dfa_status dfa_decode_layer(const dfa_layer_desc* d, const dfa_layer_weights* w,
     void* aws = ws + lp.off_attn;
     void* gws = ws + lp.off_gemv;
     const size_t aws_bytes = lp.off_gemv - lp.off_attn, gws_bytes = lp.total - lp.off_gemv;
-    // 1. both flows' queries (aux query from its own embedding input x2)
-    st = gemv_impl(&lp.q, w->wq, nullptr, x1, x2, nullptr, nullptr, nullptr, q1, q2, nullptr, gws, gws_bytes, hs);
-    if (st != DFA_OK) return st;
-    // 2. primary keys and values, appended at position ctx_lens[b]; the auxiliary flow writes no KV
+    // 1-2. both flows' queries (aux query from its own embedding input x2) and the primary's
+    // keys and values, appended at position ctx_lens[b]; the auxiliary flow writes no KV
     const dfa_kv_target kv{k_cache, v_cache, block_table, ctx_lens, d->num_kv_heads, d->head_dim, d->block_size,
                            d->max_blocks_per_seq, d->num_blocks};
-    st = gemv_impl(&lp.kv, w->wk, w->wv, x1, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, &kv, gws,
-                   gws_bytes, hs);
+    st = qkv_impl(d, lp.qkv_plan, w, x1, x2, q1, q2, kv, gws, hs);
     if (st != DFA_OK) return st;
     // 3. both flows attend the primary cache, now ctx_lens[b] + 1 positions; q2 coupled by a
     st = attn_impl(&lp.attn, q1, q2, w->a, k_cache, v_cache, block_table, ctx_lens, 1, aws, aws_bytes, o1, o2, hs,

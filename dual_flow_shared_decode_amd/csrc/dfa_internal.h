@@ -42,7 +42,11 @@ struct CombineParams {
   int32_t batch, hq, flows, n_splits;
 };
 
-enum : int32_t { kEpiNone = 0, kEpiResidual = 1, kEpiSwiglu = 2, kEpiResidualCoupled = 3, kEpiKvAppend = 4 };
+enum : int32_t { kEpiNone = 0, kEpiResidual = 1, kEpiSwiglu = 2, kEpiResidualCoupled = 3, kEpiKvAppend = 4,
+                 // layer-internal: rows [Wq; Wk; Wv]; columns [0, q_cols) are both flows' queries
+                 // (y1/y2 [batch, q_cols]), the next kv_cols the primary's keys, then its values
+                 // (appended to the cache). Split-K only (the finalize sees keys and values together).
+                 kEpiQkv = 5 };
 
 struct GemvParams {
   const uint16_t* w;   // tiled [n/16][k/8][16][8]
@@ -57,6 +61,10 @@ struct GemvParams {
   float* part;         // [k_split][mats][m_pad][n]
   int32_t batch, n, k, flows, cbf, m_pad, k_split, k_range, pair, x_exact, epilogue;
   int32_t rows_per_wg;  // weight rows per workgroup: 64 or 128
+  const uint16_t* w_seg1;  // rows [seg1_row, seg2_row) come from w_seg1, rows [seg2_row, n) from
+  const uint16_t* w_seg2;  // w_seg2 (each tiled on its own); seg1_row = seg2_row = n: one matrix
+  int32_t seg1_row, seg2_row;
+  int32_t q_cols, kv_cols;  // kEpiQkv
   uint16_t* kv_k;      // KV append target
   uint16_t* kv_v;
   const int32_t* kv_table;

@@ -91,6 +91,28 @@ __device__ __forceinline__ void store4(float* dst, const float (&v)[4]) {
   *(float4*)dst = make_float4(v[0], v[1], v[2], v[3]);
 }
 
+// Writes the primary flow's key k[0..3] and value v[0..3] for kv columns
+// c0..c0+3 (kv head c0 / head_dim) at position ctx_lens[s] of sequence s,
+// rounded to bf16.
+__device__ __forceinline__ void kv_append(const GemvParams& p, int s, int c0, const float (&k)[4], const float (&v)[4]) {
+  const int bs = 1 << p.kv_bs_log2;
+  int pos = p.kv_ctx[s];
+  pos = pos < 0 ? 0 : (pos >= p.kv_max_blocks * bs ? p.kv_max_blocks * bs - 1 : pos);
+  int blk = p.kv_table[(size_t)s * p.kv_max_blocks + (pos >> p.kv_bs_log2)];
+  blk = blk < 0 ? 0 : (blk >= p.kv_num_blocks ? p.kv_num_blocks - 1 : blk);
+  const int g = c0 / p.kv_head_dim, d = c0 - g * p.kv_head_dim, slot = pos & (bs - 1);
+  const size_t head = (size_t)blk * p.kv_hkv * p.kv_head_dim * bs + (size_t)g * p.kv_head_dim * bs;
+  const size_t tile = head + (size_t)(slot >> 4) * p.kv_head_dim * 16;
+  // keys [bs/16][D/8][16][8]: dims d..d+3 are consecutive inside one 8-dim group
+  uint2 kb;
+  kb.x = (uint32_t)bf16_rne(k[0]) | ((uint32_t)bf16_rne(k[1]) << 16);
+  kb.y = (uint32_t)bf16_rne(k[2]) | ((uint32_t)bf16_rne(k[3]) << 16);
+  *(uint2*)(p.kv_k + tile + (size_t)(d >> 3) * 128 + (slot & 15) * 8 + (d & 7)) = kb;
+  // values [bs/16][D][16]: one element per dim
+#pragma unroll
+  for (int j = 0; j < 4; ++j) p.kv_v[tile + (size_t)(d + j) * 16 + (slot & 15)] = bf16_rne(v[j]);
+}
+
 // Epilogue of one sequence s and four consecutive columns n0..n0+3, from the
 // sums y[flow][matrix][j] of both flows (flow 2 unused with one flow).
 __device__ __forceinline__ void apply_epilogue(const GemvParams& p, int s, int n0, const float (&y)[2][2][4]) {
@@ -141,28 +163,12 @@ __device__ __forceinline__ void apply_epilogue(const GemvParams& p, int s, int n
       }
       break;
     }
-    case kEpiKvAppend: {
+    case kEpiKvAppend:
       // primary only: k = rows n of W, v = rows n of W2, appended at position ctx_lens[s]
       if (p.y1) store4(p.y1 + o, y[0][0]);
       if (p.y2) store4(p.y2 + o, y[0][1]);
-      const int bs = 1 << p.kv_bs_log2;
-      int pos = p.kv_ctx[s];
-      pos = pos < 0 ? 0 : (pos >= p.kv_max_blocks * bs ? p.kv_max_blocks * bs - 1 : pos);
-      int blk = p.kv_table[(size_t)s * p.kv_max_blocks + (pos >> p.kv_bs_log2)];
-      blk = blk < 0 ? 0 : (blk >= p.kv_num_blocks ? p.kv_num_blocks - 1 : blk);
-      const int g = n0 / p.kv_head_dim, d = n0 - g * p.kv_head_dim, slot = pos & (bs - 1);
-      const size_t head = (size_t)blk * p.kv_hkv * p.kv_head_dim * bs + (size_t)g * p.kv_head_dim * bs;
-      const size_t tile = head + (size_t)(slot >> 4) * p.kv_head_dim * 16;
-      // keys [bs/16][D/8][16][8]: dims d..d+3 are consecutive inside one 8-dim group
-      uint2 kb;
-      kb.x = (uint32_t)bf16_rne(y[0][0][0]) | ((uint32_t)bf16_rne(y[0][0][1]) << 16);
-      kb.y = (uint32_t)bf16_rne(y[0][0][2]) | ((uint32_t)bf16_rne(y[0][0][3]) << 16);
-      *(uint2*)(p.kv_k + tile + (size_t)(d >> 3) * 128 + (slot & 15) * 8 + (d & 7)) = kb;
-      // values [bs/16][D][16]: one element per dim
-#pragma unroll
-      for (int j = 0; j < 4; ++j) p.kv_v[tile + (size_t)(d + j) * 16 + (slot & 15)] = bf16_rne(y[0][1][j]);
+      kv_append(p, s, n0, y[0][0], y[0][1]);
       break;
-    }
   }
 }
 
@@ -263,12 +269,17 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvParams p) {
   struct WStage {
     bf16x8 a[MATS][kHalfSteps];
   };
+  // this wave's tile within its matrix (several matrices can share one launch, by row range)
+  const int row0 = tile * 16;
+  const int seg = row0 < p.seg1_row ? 0 : (row0 < p.seg2_row ? 1 : 2);
+  const uint16_t* const wmat = seg == 0 ? p.w : (seg == 1 ? p.w_seg1 : p.w_seg2);
+  const int tile_in = (row0 - (seg == 0 ? 0 : (seg == 1 ? p.seg1_row : p.seg2_row))) / 16;
   auto fetch_w = [&](int st, WStage& w) __attribute__((always_inline)) {
     const int kg0 = (k_begin + st * kStage) / 8 + wg * kHalfSteps * 4;
-    const size_t base = (((size_t)tile * kg_total + kg0 + grp) * 16 + col) * 8;
+    const size_t base = (((size_t)tile_in * kg_total + kg0 + grp) * 16 + col) * 8;
 #pragma unroll
     for (int k2 = 0; k2 < kHalfSteps; ++k2) {
-      w.a[0][k2] = __builtin_nontemporal_load((const bf16x8*)(p.w + base + (size_t)k2 * 4 * 16 * 8));
+      w.a[0][k2] = __builtin_nontemporal_load((const bf16x8*)(wmat + base + (size_t)k2 * 4 * 16 * 8));
       if (PAIR) w.a[MATS - 1][k2] = __builtin_nontemporal_load((const bf16x8*)(p.w2 + base + (size_t)k2 * 4 * 16 * 8));
     }
   };
@@ -408,15 +419,35 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvParams p) {
 // issued before the first add; KS == 0: any number, four loads at a time.
 constexpr int kFinalizeThreads = 256;
 
+// Sum over the k-splits (fixed order) of partial row m, matrix mat, columns n0..n0+3.
+template <int KS>
+__device__ __forceinline__ void sum_splits(const GemvParams& p, int mats, int mat, size_t m, int n0, float (&y)[4]) {
+  const size_t mat_stride = (size_t)p.m_pad * p.n;
+  const float* src = p.part + mat * mat_stride + m * p.n + n0;
+  if (KS > 0) {
+    float4 v[KS > 0 ? KS : 1];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) v[ks] = *(const float4*)(src + (size_t)ks * mats * mat_stride);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      y[0] += v[ks].x; y[1] += v[ks].y; y[2] += v[ks].z; y[3] += v[ks].w;
+    }
+  } else {
+#pragma unroll 4
+    for (int ks = 0; ks < p.k_split; ++ks) {
+      const float4 v = *(const float4*)(src + (size_t)ks * mats * mat_stride);
+      y[0] += v.x; y[1] += v.y; y[2] += v.z; y[3] += v.w;
+    }
+  }
+}
+
 template <int KS>
 __global__ __launch_bounds__(kFinalizeThreads) void gemv_finalize_kernel(GemvParams p) {
   const int groups = p.n / 4;
   const int item = blockIdx.x * kFinalizeThreads + threadIdx.x;
   if (item >= p.batch * groups) return;
   const int s = item / groups, n0 = (item - s * groups) * 4;
-  const size_t mat_stride = (size_t)p.m_pad * p.n;
   const int mats = p.pair ? 2 : 1;
-  const int nks = KS > 0 ? KS : p.k_split;
   float y[2][2][4];
 #pragma unroll
   for (int f = 0; f < 2; ++f)
@@ -424,6 +455,20 @@ __global__ __launch_bounds__(kFinalizeThreads) void gemv_finalize_kernel(GemvPar
     for (int mat = 0; mat < 2; ++mat)
 #pragma unroll
       for (int j = 0; j < 4; ++j) y[f][mat][j] = 0.f;
+  if (p.epilogue == kEpiQkv) {
+    if (n0 < p.q_cols) {  // both flows' queries
+      sum_splits<KS>(p, 1, 0, (size_t)s, n0, y[0][0]);
+      sum_splits<KS>(p, 1, 0, (size_t)(p.cbf * 16 + s), n0, y[1][0]);
+      const size_t o = (size_t)s * p.q_cols + n0;
+      store4(p.y1 + o, y[0][0]);
+      store4(p.y2 + o, y[1][0]);
+    } else if (n0 < p.q_cols + p.kv_cols) {  // the primary's key and value of the same kv columns
+      sum_splits<KS>(p, 1, 0, (size_t)s, n0, y[0][0]);
+      sum_splits<KS>(p, 1, 0, (size_t)s, n0 + p.kv_cols, y[0][1]);
+      kv_append(p, s, n0 - p.q_cols, y[0][0], y[0][1]);
+    }
+    return;
+  }
 #pragma unroll
   for (int f = 0; f < 2; ++f) {
     if (f >= p.flows) break;
@@ -431,22 +476,7 @@ __global__ __launch_bounds__(kFinalizeThreads) void gemv_finalize_kernel(GemvPar
 #pragma unroll
     for (int mat = 0; mat < 2; ++mat) {
       if (mat >= mats) break;
-      const float* src = p.part + mat * mat_stride + m * p.n + n0;
-      if (KS > 0) {
-        float4 v[KS > 0 ? KS : 1];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) v[ks] = *(const float4*)(src + (size_t)ks * mats * mat_stride);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          y[f][mat][0] += v[ks].x; y[f][mat][1] += v[ks].y; y[f][mat][2] += v[ks].z; y[f][mat][3] += v[ks].w;
-        }
-      } else {
-#pragma unroll 4
-        for (int ks = 0; ks < nks; ++ks) {
-          const float4 v = *(const float4*)(src + (size_t)ks * mats * mat_stride);
-          y[f][mat][0] += v.x; y[f][mat][1] += v.y; y[f][mat][2] += v.z; y[f][mat][3] += v.w;
-        }
-      }
+      sum_splits<KS>(p, mats, mat, m, n0, y[f][mat]);
     }
   }
   apply_epilogue(p, s, n0, y);

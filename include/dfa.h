@@ -267,9 +267,12 @@ DFA_API dfa_status dfa_pack_weight(const uint16_t* w, uint16_t* w_tiled, int32_t
  *     h_f = x_f + o_f Wo^T
  *     z_1 = silu(h_1 Wg^T) * (h_1 Wu^T),  z_2 = silu(h_2 Wg^T) * (h_2 Wu^T) + b * z_1
  *     out_1 = h_1 + z_1 Wd^T,             out_2 = h_2 + z_2 Wd^T + c * (z_1 Wd^T)
- * Each GEMV is one launch plus, when its plan splits k, a reduction launch
- * (at the benchmark shape: 10 launches); every weight is read once for both
- * flows. The caller advances ctx_lens afterwards. Requirements: those of
+ * The query, key and value projections run as one GEMV over the rows
+ * [Wq; Wk; Wv] (the matrices stay separate in memory) whose split-K reduction
+ * stores the queries and appends the keys and values; each other GEMV is one
+ * launch plus, when its plan splits k, a reduction launch (at the benchmark
+ * shape: 8 launches). Every weight is read once for both flows. The caller
+ * advances ctx_lens afterwards. Requirements: those of
  * dfa_decode_attn (max_ctx_len >= every ctx_lens[b] + 1) and of dfa_dual_gemv
  * (batch <= 32; hidden, mlp, num_q_heads * head_dim and num_kv_heads *
  * head_dim multiples of 128). x1, x2, out1, out2: float32 [batch, hidden].

@@ -161,7 +161,11 @@ def bench_layer(args):
     def step():  # the cache slot at ctx_lens is rewritten with the same values every step
         dfa.dfa_decode_layer(desc, wts, dev["x1"], dev["x2"], dev["k_cache"], dev["v_cache"], dev["block_table"],
                              dev["ctx_lens"], out1, out2, ws, stream)
-    for _ in range(args.warmup):
+    # A step touches ~1 GB of weights and cache that nothing touched since upload; its first
+    # passes run ~10% slower (measured: 241 us per step after 5 warm-up steps, 219 after 500),
+    # so the layer warms up for at least 200 steps, as a serving loop would be.
+    warmup = max(args.warmup, 200)
+    for _ in range(warmup):
         step()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -176,7 +180,7 @@ def bench_layer(args):
     log(f"layer step {ms * 1e3:.1f} us, {nbytes / 1e6:.0f} MB -> {gbps:.0f} GB/s")
     print(json.dumps({"metric": "dual-flow decode layer step: tokens/s (both flows) + achieved HBM GB/s vs peak",
                       "value": 2 * cfg.batch / (ms * 1e-3), "unit": "tokens/s (both flows)", "n_gpus": 1,
-                      "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+                      "steps": args.steps, "warmup": warmup, "ms_per_step": ms, "higher_is_better": True,
                       "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
                       "config": {"workload": "c5: one dual-flow decode layer step, batch 32, hidden 4096, 32/8 heads "
                                              "of 128, SwiGLU MLP 14336, 4096 cached positions",

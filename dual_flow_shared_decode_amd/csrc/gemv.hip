@@ -21,9 +21,12 @@
 // s % 16 (each flow padded to CBF*16 rows), so the two flows of a sequence end
 // up in the same lane and register.
 //
-// Workgroup = 8 waves = 64 weight rows (four 16-row tiles, of each matrix) x
-// one k-range (split-K); two wave groups split the k-steps of every stage,
-// so each SIMD runs two waves that share the stage's B operands. The k-range
+// Workgroup = 8 waves = 64 weight rows (four 16-row tiles, of each matrix;
+// two wave groups split the k-steps of every stage, so each SIMD runs two
+// waves that share the stage's B operands) or 128 rows (eight tiles, one wave
+// each) x one k-range (split-K). A tile takes its weights from one of up to
+// three matrices by row range, so one launch can cover stacked matrices
+// (the layer's [Wq; Wk; Wv]). The k-range
 // is streamed in 128-column stages, three in flight: a stage's weights (in
 // registers) and raw activations (in registers, first touched when they are
 // converted) are fetched together, and per stage the workgroup converts the

@@ -36,6 +36,14 @@ SMALL = {
                               ctx_lens=(64, 200)), 2008),
     "f32_d128_g4": (W.AttnConfig("f32g4", batch=2, num_q_heads=8, num_kv_heads=2, head_dim=128, dtype="f32",
                                  ctx_lens=(129, 700), block_size=64, shuffle_blocks=True), 2009),
+    # 16 query rows per workgroup (8 heads x 2 flows) at head_dim 64, and with float32 queries
+    "d64_rows16": (W.AttnConfig("d64r16", batch=2, num_q_heads=32, num_kv_heads=4, head_dim=64, dtype="bf16",
+                                ctx_lens=(513, 96), block_size=32, shuffle_blocks=True), 2015),
+    "f32q_rows16": (W.AttnConfig("f32qr16", batch=2, num_q_heads=16, num_kv_heads=2, head_dim=128, dtype="bf16",
+                                 ctx_lens=(1025, 40), capacity=2048, q_dtype="f32"), 2016),
+    # more than 64 sequences: one split each, taken in batch order (no length ranking)
+    "batch70": (W.AttnConfig("b70", batch=70, num_q_heads=8, num_kv_heads=4, head_dim=128, dtype="bf16",
+                             ctx_range=(1, 300), block_size=16, shuffle_blocks=True), 2017),
 }
 _CASES = {}
 _REFS = {}

@@ -137,3 +137,28 @@ def test_stream_read_validation():
     with pytest.raises(dfa.DfaError):
         _lib._check(_lib.lib().dfa_stream_read(None, 1024, FAKE, None))
     assert dfa.dfa_stream_read_sink_bytes() > 0
+
+
+def gemv_desc(**kw):
+    d = dict(batch=32, n=4096, k=4096, num_flows=2, epilogue=0, x_exact_bf16=0, k_split=0, rows_per_wg=0)
+    d.update(kw)
+    return dfa.GemvDesc(**d)
+
+
+def test_gemv_plans():
+    """The library's GEMV plans at the layer's shapes (batch 32, two flows: 64 padded rows)."""
+    rows = 2 * 32
+    # 4096 x 4096: 64-row workgroups, 64 row groups -> 4 k-splits
+    assert dfa.dfa_dual_gemv_workspace_size(gemv_desc()) == 4 * rows * 4096 * 4
+    # 4096 x 14336 (MLP down): 128-row workgroups, 32 row groups -> 8 k-splits
+    assert dfa.dfa_dual_gemv_workspace_size(gemv_desc(k=14336)) == 8 * rows * 4096 * 4
+    # forced 64 rows: 64 row groups -> 4 k-splits
+    assert dfa.dfa_dual_gemv_workspace_size(gemv_desc(k=14336, rows_per_wg=64)) == 4 * rows * 4096 * 4
+    # 14336 x 4096 SwiGLU pair: 224 row groups of 64 rows run unsplit (no workspace)
+    assert dfa.dfa_dual_gemv_workspace_size(gemv_desc(n=14336, epilogue=dfa.DFA_EPI_SWIGLU)) == 0
+    # KV append, one flow (32 padded rows), 1024 columns: 16 row groups -> 16 k-splits of two matrices
+    assert dfa.dfa_dual_gemv_workspace_size(gemv_desc(n=1024, num_flows=1, epilogue=dfa.DFA_EPI_KV_APPEND)) == \
+        16 * 2 * 32 * 1024 * 4
+    # invalid: rows_per_wg not 0/64/128, or 128 with n % 128 != 0
+    assert dfa.dfa_dual_gemv_workspace_size(gemv_desc(rows_per_wg=96)) == 0
+    assert dfa.dfa_dual_gemv_workspace_size(gemv_desc(n=192, rows_per_wg=128)) == 0

@@ -252,10 +252,13 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(AttnParams p) {
   for (int db = 0; db < DB; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // One chunk: scores, online softmax, weighted values. The running max of a
-  // row moves only when a chunk's max exceeds it by more than kLazyRescale
-  // (base-2 units; a wave-wide vote), so the weights 2^(s - m_run) stay below
-  // 2^kLazyRescale and most chunks skip rescaling the accumulators. The final
-  // (O, m, l) of a row describe the same softmax whatever m_run ended as.
+  // row moves only when the chunk's max of that row exceeds it by more than
+  // kLazyRescale (base-2 units), so the weights 2^(s - m_run) stay below
+  // 2^kLazyRescale and most chunks skip rescaling the accumulators (a
+  // wave-wide vote skips the whole step when no row needs it). The decision
+  // is the row's own -- other rows, the other flow's included, change neither
+  // its values nor their rounding. The final (O, m, l) of a row describe the
+  // same softmax whatever m_run ended as.
   auto process = [&](Chunk<D>& cur, int c) __attribute__((always_inline)) {
     const int t0 = r.start + 32 * c;
     f32x4 sv[2];
@@ -302,9 +305,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(AttnParams p) {
     for (int j = 1; j < 8; ++j) cmax = fmaxf(cmax, sc[j]);
     cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
     cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-    if (__builtin_amdgcn_ballot_w64(cmax > m_run + kLazyRescale) != 0) {
-      const float m_new = fmaxf(m_run, cmax);
-      const float alpha = fast_exp2(m_run - m_new);
+    const bool moves = cmax > m_run + kLazyRescale;  // the same in every lane of a row
+    if (__builtin_amdgcn_ballot_w64(moves) != 0) {
+      const float m_new = moves ? cmax : m_run;
+      const float alpha = moves ? fast_exp2(m_run - m_new) : 1.f;  // 1: exact, the row is untouched
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db) oacc[db] *= alpha;

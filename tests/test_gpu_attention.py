@@ -113,11 +113,16 @@ def test_primary_independent_of_aux_inputs():
     t = upload_attn_case(case)
     say("case primary independence")
     o1a, o2a = run_attn(case, tensors=t)
-    t["q2"] = torch.randn(t["q2"].shape, device="cuda").to(torch.bfloat16).view(torch.int16)
-    t["a"] = torch.randn_like(t["a"])
-    o1b, o2b = run_attn(case, tensors=t)
-    assert np.array_equal(o1a, o1b)
-    assert not np.array_equal(o2a, o2b)
+    gen = torch.Generator(device="cpu").manual_seed(77)
+    # scales 1 and 16: large auxiliary scores move the auxiliary rows' running max on chunks
+    # where the primary rows keep theirs; the primary must stay bit for bit the same
+    for scale in (1.0, 16.0):
+        q2 = torch.randn(t["q2"].shape, generator=gen) * scale
+        t["q2"] = q2.to(torch.bfloat16).view(torch.int16).cuda()
+        t["a"] = (torch.randn(t["a"].shape, generator=gen) * scale).cuda()
+        o1b, o2b = run_attn(case, tensors=t)
+        assert np.array_equal(o1a, o1b), f"aux scale {scale}"
+        assert not np.array_equal(o2a, o2b)
 
 
 def test_cache_is_never_written():

@@ -20,7 +20,7 @@ of the split kernel against the 8 TB/s peak, the measured stream-read ceiling,
 the auxiliary flow's increment over a one-flow run of the same kernel, and the
 CPU oracle's rate on a bounded sample (context only).
 
-    python bench.py [--steps K] [--warmup W] [--config c2|c3|c4]
+    python bench.py [--steps K] [--warmup W] [--config c2|c3|c4|c5|head]
 """
 import argparse
 import hashlib
@@ -189,13 +189,89 @@ def bench_layer(args):
                       "algorithmic_bytes_per_step": nbytes}), flush=True)
 
 
+def bench_head(args):
+    """One output-head step of the head workload (batch 32, hidden 4096, vocabulary 32000): both flows'
+    logits from one read of the shared vocabulary matrix (dfa_dual_gemv), then the mixture of their
+    distributions and a sampled and a greedy token per sequence (dfa_mixture_sample)."""
+    import numpy as np
+    import torch
+
+    import dual_flow_shared_decode_amd as dfa
+    import workloads as W
+    from workloads.device import to_device
+
+    cfg = W.HEAD
+    log("generating head inputs")
+    h1, h2, w_bits, u = W.make_head_case(cfg, W.SEEDS["head"])
+    dev = to_device(w_bits)
+    # two copies of the 262 MB matrix, alternated between steps: no step finds it in the last-level cache
+    wts = [torch.empty_like(dev) for _ in range(2)]
+    for wt in wts:
+        dfa.dfa_pack_weight(dev, wt, cfg.vocab, cfg.hidden)
+    del dev
+    x1, x2, tu = to_device(h1), to_device(h2), to_device(u)
+    gd = dfa.GemvDesc(batch=cfg.batch, n=cfg.vocab, k=cfg.hidden, num_flows=2, epilogue=dfa.DFA_EPI_NONE,
+                      x_exact_bf16=1, k_split=0, rows_per_wg=0)
+    gws = torch.empty(max(dfa.dfa_dual_gemv_workspace_size(gd) // 4, 4), device="cuda")
+    md = dfa.MixtureDesc(batch=cfg.batch, vocab=cfg.vocab)
+    mws = torch.empty(dfa.dfa_mixture_workspace_size(md) // 4, device="cuda")
+    y1 = torch.empty((cfg.batch, cfg.vocab), device="cuda")
+    y2 = torch.empty_like(y1)
+    tok = torch.empty(cfg.batch, dtype=torch.int32, device="cuda")
+    gr = torch.empty_like(tok)
+    al = torch.empty(cfg.batch, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def mix():
+        dfa.dfa_mixture_sample(md, y1, y2, tu, tok, gr, al, None, mws, stream)
+
+    def step(i):
+        dfa.dfa_dual_gemv(gd, wts[i % 2], None, x1, x2, None, None, None, y1, y2, None, gws, stream)
+        mix()
+
+    def timed(fn, steps, warmup):
+        for i in range(warmup):
+            fn(i)
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(steps):
+            fn(i)
+        end.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / steps
+
+    warmup = max(args.warmup, 100)
+    ms = timed(step, args.steps, warmup)
+    mix_ms = timed(lambda i: mix(), args.steps, 10)
+    w_bytes = 2 * cfg.vocab * cfg.hidden
+    logits = 4 * cfg.batch * cfg.vocab
+    # the weight once, both flows' hidden states in, both flows' logits out and back in, the tokens out
+    nbytes = w_bytes + 2 * 4 * cfg.batch * cfg.hidden + 2 * logits + 2 * logits + 12 * cfg.batch
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    mix_bytes = 2 * logits + 2 * 4 * cfg.batch  # the mixture's own minimum: both logit rows once
+    log(f"head step {ms * 1e3:.1f} us ({nbytes / 1e6:.0f} MB -> {gbps:.0f} GB/s); mixture alone "
+        f"{mix_ms * 1e3:.1f} us")
+    print(json.dumps({"metric": "dual-flow output head + mixture sampling: tokens/s + achieved HBM GB/s vs peak",
+                      "value": cfg.batch / (ms * 1e-3), "unit": "sampled tokens/s", "n_gpus": 1,
+                      "steps": args.steps, "warmup": warmup, "ms_per_step": ms, "higher_is_better": True,
+                      "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+                      "config": {"workload": "head: both flows' logits over a 32000-token vocabulary from hidden "
+                                             "4096 (shared bf16 matrix), mixture, sampled and greedy tokens, "
+                                             "batch 32", "batch": cfg.batch, "vocab": cfg.vocab},
+                      "achieved_gbps": gbps, "hbm_peak_gbps": HBM_PEAK_GBPS, "frac_of_peak": gbps / HBM_PEAK_GBPS,
+                      "algorithmic_bytes_per_step": nbytes, "mixture_us": mix_ms * 1e3,
+                      "mixture_gbps": mix_bytes / (mix_ms * 1e-3) / 1e9}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="c2", choices=["c2", "c3", "c4", "c5"],
-                    help="c2 (default): the attention workload the metric is quoted on; c5: a whole layer step")
+    ap.add_argument("--config", default="c2", choices=["c2", "c3", "c4", "c5", "head"],
+                    help="c2 (default): the attention workload the metric is quoted on; c5: a whole layer step; "
+                         "head: the dual output head and mixture sampling")
     ap.add_argument("--split", type=int, default=0, help="positions per split (0: library choice)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -219,6 +295,9 @@ def main():
     torch.cuda.set_device(0)
     if args.config == "c5":
         bench_layer(args)
+        return
+    if args.config == "head":
+        bench_head(args)
         return
     cfg = W.ATTN_CONFIGS[args.config]
     log(f"generating {cfg.name} inputs")

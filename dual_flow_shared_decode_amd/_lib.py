@@ -21,6 +21,7 @@ EXPORTS = ["dfa_decode_attn_split_len", "dfa_decode_attn_num_splits", "dfa_decod
            "dfa_decode_attn", "dfa_decode_attn_timed", "dfa_decode_attn_partials", "dfa_combine",
            "dfa_dual_gemv_workspace_size", "dfa_dual_gemv", "dfa_pack_weight",
            "dfa_decode_layer_workspace_size", "dfa_decode_layer",
+           "dfa_mixture_workspace_size", "dfa_mixture_sample",
            "dfa_status_string", "dfa_last_error", "dfa_version", "dfa_stream_read", "dfa_stream_read_sink_bytes"]
 
 DFA_EPI_NONE, DFA_EPI_RESIDUAL, DFA_EPI_SWIGLU, DFA_EPI_RESIDUAL_COUPLED, DFA_EPI_KV_APPEND = range(5)
@@ -74,6 +75,12 @@ class LayerWeights(ctypes.Structure):
     _fields_ = [(f, ctypes.c_void_p) for f in ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down", "a", "b", "c")]
 
 
+class MixtureDesc(ctypes.Structure):
+    """Mirror of dfa_mixture_desc."""
+
+    _fields_ = [("batch", ctypes.c_int32), ("vocab", ctypes.c_int32)]
+
+
 class KernelEvents(ctypes.Structure):
     """Mirror of dfa_kernel_events (hipEvent_t handles)."""
 
@@ -108,6 +115,9 @@ def lib() -> ctypes.CDLL:
             "dfa_decode_layer_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(LayerDesc)]),
             "dfa_decode_layer": (ctypes.c_int, [ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerWeights), _P, _P, _P,
                                                 _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+            "dfa_mixture_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(MixtureDesc)]),
+            "dfa_mixture_sample": (ctypes.c_int, [ctypes.POINTER(MixtureDesc), _P, _P, _P, _P, _P, _P, _P, _P,
+                                                  ctypes.c_size_t, _P]),
             "dfa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
             "dfa_last_error": (ctypes.c_char_p, []),
             "dfa_version": (ctypes.c_int32, []),
@@ -248,6 +258,17 @@ def dfa_decode_layer(desc, weights, x1, x2, k_cache, v_cache, block_table, ctx_l
     _check(lib().dfa_decode_layer(ctypes.byref(desc), ctypes.byref(weights), _ptr(x1), _ptr(x2), _ptr(k_cache),
                                   _ptr(v_cache), _ptr(block_table), _ptr(ctx_lens), _ptr(out1), _ptr(out2),
                                   _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def dfa_mixture_workspace_size(desc: MixtureDesc) -> int:
+    return int(lib().dfa_mixture_workspace_size(ctypes.byref(desc)))
+
+
+def dfa_mixture_sample(desc, logits1, logits2, u, token, greedy, alpha, p_mix, workspace, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().dfa_mixture_sample(ctypes.byref(desc), _ptr(logits1), _ptr(logits2), _ptr(u), _ptr(token),
+                                    _ptr(greedy), _ptr(alpha), _ptr(p_mix), _ptr(workspace), ws_bytes,
+                                    _stream(stream)))
 
 
 def dfa_stream_read(buf, sink, stream=None):

@@ -233,13 +233,16 @@ dfa_status validate_gemv(const dfa_gemv_desc* d, GemvPlan* plan) {
   pl.m_pad = d->num_flows * pl.cbf * 16;
   const int64_t chunks = d->k / int64_t(dfa::gemv_chunk());
   // Library choice of the workgroup's rows (measured on MI355X, batch 32, two
-  // flows): 64, unless the matrix is large (at least 48 Mi elements) and too
-  // narrow to fill the chip unsplit at 64 rows -- then 128, so that the
-  // activations a workgroup loads per stage serve twice the weight rows and
-  // twice the weight bytes are in flight (4096 x 14336: 37.5 -> 33.4 us; a
-  // 14336-row matrix runs unsplit at 64 rows and is faster so).
+  // flows): 128 for a large matrix (at least 48 Mi elements) that is either too
+  // narrow to fill the chip unsplit at 64 rows or wide enough to fill it
+  // unsplit at 128 -- the activations a workgroup loads per stage then serve
+  // twice the weight rows and twice the weight bytes are in flight
+  // (4096 x 14336: 37.5 -> 33.4 us; 32000 x 4096: 68.3 -> 49.1 us); else 64
+  // (a 14336-row matrix runs unsplit at 64 rows and is faster so than split
+  // at 128).
   const bool big = int64_t(d->n) * d->k >= (int64_t(48) << 20);
-  pl.rows_per_wg = d->rows_per_wg > 0 ? d->rows_per_wg : ((big && d->n % 128 == 0 && d->n / 64 < 192) ? 128 : 64);
+  const bool wide128 = d->n % 128 == 0 && (d->n / 64 < 192 || d->n / 128 >= 192);
+  pl.rows_per_wg = d->rows_per_wg > 0 ? d->rows_per_wg : ((big && wide128) ? 128 : 64);
   const int64_t row_groups = d->n / pl.rows_per_wg;
   // About one workgroup per compute unit (at most 256); a matrix with at
   // least 192 row groups runs unsplit, so its epilogue needs no second launch.
@@ -513,6 +516,54 @@ dfa_status dfa_decode_layer(const dfa_layer_desc* d, const dfa_layer_weights* w,
     if (st != DFA_OK) return st;
     // 6. down projection, MLP-output coupling c, residual
     return gemv_impl(&lp.mlp_out, w->w_down, nullptr, z1, z2, w->c, h1, h2, out1, out2, nullptr, gws, gws_bytes, hs);
+  } catch (...) {
+    return fail(DFA_ERR_HIP, "unexpected host exception");
+  }
+}
+
+static dfa_status validate_mixture(const dfa_mixture_desc* d) {
+  if (!d) return fail(DFA_ERR_NULL, "desc is NULL");
+  if (d->batch < 1 || d->batch > 65535) return fail(DFA_ERR_SHAPE, "batch must be in [1, 65535]");
+  if (d->vocab < 4 || d->vocab % 4 != 0 || d->vocab > dfa::kMixChunk * dfa::kMixMaxChunks)
+    return fail(DFA_ERR_SHAPE, "vocab must be a positive multiple of 4, at most 2^20");
+  return DFA_OK;
+}
+
+size_t dfa_mixture_workspace_size(const dfa_mixture_desc* d) {
+  if (validate_mixture(d) != DFA_OK) return 0;
+  // per (sequence, chunk): softmax statistics (kMixRec floats), then mass and maximum (4 words)
+  return size_t(d->batch) * dfa::mixture_chunks(d->vocab) * (dfa::kMixRec * sizeof(float) + 4 * sizeof(uint32_t));
+}
+
+dfa_status dfa_mixture_sample(const dfa_mixture_desc* d, const float* logits1, const float* logits2,
+                              const float* u, int32_t* token, int32_t* greedy, float* alpha, float* p_mix,
+                              void* workspace, size_t ws_bytes, void* stream) {
+  try {
+    dfa_status st = validate_mixture(d);
+    if (st != DFA_OK) return st;
+    if (!logits1 || !logits2 || !u || !token || !greedy || !alpha)
+      return fail(DFA_ERR_NULL, "logits1, logits2, u, token, greedy and alpha are required");
+    if (!aligned16(logits1) || !aligned16(logits2) || (p_mix && !aligned16(p_mix)))
+      return fail(DFA_ERR_ALIGNMENT, "logits and p_mix must be 16-byte aligned");
+    const size_t need = dfa_mixture_workspace_size(d);
+    if (!workspace || ws_bytes < need) return fail(DFA_ERR_WORKSPACE, "workspace smaller than dfa_mixture_workspace_size()");
+    if (!aligned16(workspace)) return fail(DFA_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
+    dfa::MixParams p{};
+    p.logits1 = logits1;
+    p.logits2 = logits2;
+    p.u = u;
+    p.token = token;
+    p.greedy = greedy;
+    p.alpha = alpha;
+    p.p_mix = p_mix;
+    p.batch = d->batch;
+    p.vocab = d->vocab;
+    p.chunks = int32_t(dfa::mixture_chunks(d->vocab));
+    p.rec = static_cast<float*>(workspace);
+    p.crec = reinterpret_cast<uint32_t*>(p.rec + size_t(p.batch) * p.chunks * dfa::kMixRec);
+    const hipError_t e = dfa::launch_mixture(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(DFA_ERR_HIP, std::string("mixture launch: ") + hipGetErrorString(e));
+    return DFA_OK;
   } catch (...) {
     return fail(DFA_ERR_HIP, "unexpected host exception");
   }

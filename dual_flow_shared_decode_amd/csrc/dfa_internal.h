@@ -72,6 +72,25 @@ struct GemvParams {
   int32_t kv_hkv, kv_head_dim, kv_bs_log2, kv_max_blocks, kv_num_blocks;
 };
 
+// Mixture decoding: the vocabulary is cut into chunks of kMixChunk tokens;
+// at most kMixMaxChunks chunks (one per thread of the pick kernel).
+constexpr int kMixChunk = 4096;
+constexpr int kMixMaxChunks = 256;
+constexpr int kMixRec = 8;  // floats per chunk-statistics record (5 used, 32-byte aligned)
+
+struct MixParams {
+  const float* logits1;  // [batch, vocab]
+  const float* logits2;
+  const float* u;        // [batch] uniforms in [0, 1)
+  int32_t* token;        // [batch] inverse-CDF draw
+  int32_t* greedy;       // [batch] first most likely token
+  float* alpha;          // [batch]
+  float* p_mix;          // [batch, vocab] or null
+  float* rec;            // workspace: [batch][chunks][kMixRec] softmax statistics
+  uint32_t* crec;        // workspace: [batch][chunks][4] mass (2 words), first maximum (value, token)
+  int32_t batch, vocab, chunks;
+};
+
 // Optional events recorded by the runtime at the start and end of a kernel's
 // own dispatch (no extra commands on the stream).
 struct KernelEvents {
@@ -87,6 +106,8 @@ hipError_t launch_gemv(const GemvParams& p, hipStream_t s);
 hipError_t launch_gemv_finalize(const GemvParams& p, hipStream_t s);
 hipError_t launch_pack_weight(const uint16_t* w, uint16_t* wt, int n, int k, hipStream_t s);
 size_t gemv_chunk();
+hipError_t launch_mixture(const MixParams& p, hipStream_t s);
+size_t mixture_chunks(int vocab);
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s);
 size_t stream_read_threads();
 

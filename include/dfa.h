@@ -305,6 +305,43 @@ DFA_API dfa_status dfa_decode_layer(const dfa_layer_desc* desc, const dfa_layer_
                                     const int32_t* block_table, const int32_t* ctx_lens, float* out1,
                                     float* out2, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * ------------------------------------------------------ mixture decoding
+ * Next token from the mixture of the two flows' distributions ("Mecanismos
+ * Chave", mixture objective): with p_f = softmax(logits_f) over the vocabulary,
+ *     c = sum_v p_1(v)^2           (the primary's collision probability)
+ *     alpha = (1 + c) / 2          (this library's reading: the primary keeps at
+ *                                   least half of the weight, more when confident)
+ *     p_mix = alpha p_1 + (1 - alpha) p_2.
+ * For each sequence b, with the caller's uniform u[b] (clamped to [0, 1)):
+ *     token[b]  = the smallest v whose cumulative p_mix mass exceeds u[b] times
+ *                 the total mass (inverse CDF);
+ *     greedy[b] = the smallest v with the largest p_mix(v);
+ *     alpha[b]  = alpha.
+ * logits1 (primary), logits2 (auxiliary): float32 [batch, vocab], row-major,
+ * 16-byte aligned, finite. p_mix (optional, NULL to skip): float32
+ * [batch, vocab], receives the mixture. u: float32 [batch]. token, greedy:
+ * int32 [batch]; alpha: float32 [batch]. All device memory owned by the
+ * caller; results independent of timing.
+ * Masses are summed as integers (p_mix scaled by 2^35, truncated), so the
+ * search is exact and independent of summation order; a token with less than
+ * 2^-35 of mass is never drawn. Three launches on `stream`.
+ * Limits: batch 1..65535; vocab a multiple of 4 in [4, 2^20]. The workspace
+ * (dfa_mixture_workspace_size bytes, 16-byte aligned) holds per-chunk records;
+ * its contents on entry do not matter.
+ */
+typedef struct dfa_mixture_desc {
+  int32_t batch;
+  int32_t vocab;
+} dfa_mixture_desc;
+
+/* Workspace bytes of dfa_mixture_sample for `desc` (0 if invalid). */
+DFA_API size_t dfa_mixture_workspace_size(const dfa_mixture_desc* desc);
+
+DFA_API dfa_status dfa_mixture_sample(const dfa_mixture_desc* desc, const float* logits1, const float* logits2,
+                                      const float* u, int32_t* token, int32_t* greedy, float* alpha, float* p_mix,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
 /* Short fixed description of a status code. Never NULL. */
 DFA_API const char* dfa_status_string(dfa_status status);
 

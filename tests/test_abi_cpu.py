@@ -159,6 +159,40 @@ def test_gemv_plans():
     # KV append, one flow (32 padded rows), 1024 columns: 16 row groups -> 16 k-splits of two matrices
     assert dfa.dfa_dual_gemv_workspace_size(gemv_desc(n=1024, num_flows=1, epilogue=dfa.DFA_EPI_KV_APPEND)) == \
         16 * 2 * 32 * 1024 * 4
+    # 32000 x 4096 (output head over the vocabulary): 250 row groups of 128 rows, unsplit
+    assert dfa.dfa_dual_gemv_workspace_size(gemv_desc(n=32000)) == 0
+    assert dfa.dfa_dual_gemv_workspace_size(gemv_desc(n=32000, rows_per_wg=64, k_split=2)) == 2 * rows * 32000 * 4
     # invalid: rows_per_wg not 0/64/128, or 128 with n % 128 != 0
     assert dfa.dfa_dual_gemv_workspace_size(gemv_desc(rows_per_wg=96)) == 0
     assert dfa.dfa_dual_gemv_workspace_size(gemv_desc(n=192, rows_per_wg=128)) == 0
+
+
+def test_mixture_workspace_and_validation():
+    d = dfa.MixtureDesc(batch=32, vocab=32000)
+    # per (sequence, chunk of 4096 tokens): 8 floats of softmax statistics and 4 words of mass and maximum
+    assert dfa.dfa_mixture_workspace_size(d) == 32 * 8 * (32 + 16)
+    assert dfa.dfa_mixture_workspace_size(dfa.MixtureDesc(batch=1, vocab=1 << 20)) == 256 * 48
+    for bad in (dict(batch=0, vocab=32000), dict(batch=65536, vocab=32000), dict(batch=1, vocab=0),
+                dict(batch=1, vocab=30), dict(batch=1, vocab=2), dict(batch=1, vocab=(1 << 20) + 4)):
+        assert dfa.dfa_mixture_workspace_size(dfa.MixtureDesc(**bad)) == 0
+        with pytest.raises(dfa.DfaError) as e:
+            _lib._check(_lib.lib().dfa_mixture_sample(ctypes.byref(dfa.MixtureDesc(**bad)), FAKE, FAKE, FAKE, FAKE,
+                                                      FAKE, FAKE, None, FAKE, 1 << 20, None))
+        assert _lib.STATUS[e.value.status] == "DFA_ERR_SHAPE"
+    need = dfa.dfa_mixture_workspace_size(d)
+
+    def call(**kw):
+        p = dict(l1=FAKE, l2=FAKE, u=FAKE, tok=FAKE, gr=FAKE, al=FAKE, pm=None, ws=FAKE, nb=need)
+        p.update(kw)
+        with pytest.raises(dfa.DfaError) as e:
+            _lib._check(_lib.lib().dfa_mixture_sample(ctypes.byref(d), p["l1"], p["l2"], p["u"], p["tok"], p["gr"],
+                                                      p["al"], p["pm"], p["ws"], p["nb"], None))
+        return _lib.STATUS[e.value.status]
+
+    for name in ("l1", "l2", "u", "tok", "gr", "al"):
+        assert call(**{name: None}, nb=0) == "DFA_ERR_NULL", name
+    assert call(nb=need - 4) == "DFA_ERR_WORKSPACE"
+    assert call(ws=None) == "DFA_ERR_WORKSPACE"
+    for name in ("l1", "l2", "pm"):
+        assert call(**{name: FAKE + 4}, nb=need - 4) == "DFA_ERR_ALIGNMENT", name
+    assert call(ws=FAKE + 4) == "DFA_ERR_ALIGNMENT"

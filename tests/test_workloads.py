@@ -81,3 +81,15 @@ def test_layer_case_shapes():
     assert case.w["wd"].shape == (64, 96)
     assert np.array_equal(W.bf16_bits_to_f32(W.f32_to_bf16_bits(case.x1)), case.x1)
     assert case.k_cache.shape == (2, 2, 2, 2, 16, 8) and case.v_cache.shape == (2, 2, 2, 16, 16)
+
+
+def test_output_head_inputs_are_deterministic():
+    cfg = W.MIX.replace(batch=5, vocab=64)
+    a, b = W.make_mixture_case(cfg, 3), W.make_mixture_case(cfg, 3)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    assert a[0].dtype == np.float32 and a[0].shape == (5, 64) and np.all((a[2] >= 0) & (a[2] < 1))
+    assert not np.array_equal(a[0], a[1])  # the flows draw from separate streams
+    h1, h2, w, u = W.make_head_case(W.HEAD.replace(batch=2, hidden=16, vocab=32), 4)
+    assert w.dtype == np.uint16 and w.shape == (32, 16)
+    assert np.array_equal(W.bf16_bits_to_f32(W.f32_to_bf16_bits(h1)), h1)  # exact bf16 values

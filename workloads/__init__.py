@@ -39,7 +39,8 @@ BF16_NAN_BITS = np.uint16(0x7FC0)
 # Tags separating the random streams of different tensors.
 _TAG = {"q1": 1, "q2": 2, "a": 3, "k": 4, "v": 5, "peak": 6, "len": 7, "perm": 8,
         "x1": 11, "x2": 12, "wq": 13, "wk": 14, "wv": 15, "wo": 16, "wg": 17,
-        "wu": 18, "wd": 19, "b": 20, "c": 21}
+        "wu": 18, "wd": 19, "b": 20, "c": 21, "l1": 22, "l2": 23, "u": 24, "lpeak": 25, "wlm": 26,
+        "h1": 27, "h2": 28}
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -124,7 +125,7 @@ C3 = AttnConfig("c3", batch=64, num_q_heads=64, num_kv_heads=8, head_dim=128, dt
 C4 = AttnConfig("c4", batch=4, num_q_heads=32, num_kv_heads=8, head_dim=128, dtype="bf16",
                 ctx_lens=(131072,) * 4, peaky_fraction=0.01, peaky_factor=8.0)
 ATTN_CONFIGS = {"c1": C1, "c2": C2, "c3": C3, "c4": C4}
-SEEDS = {"c1": 1001, "c2": 1002, "c3": 1003, "c4": 1004, "c5": 1005}
+SEEDS = {"c1": 1001, "c2": 1002, "c3": 1003, "c4": 1004, "c5": 1005, "head": 1006, "mix": 1007}
 
 
 def draw_ctx_lens(cfg: AttnConfig, seed: int) -> np.ndarray:
@@ -343,3 +344,72 @@ def permute_blocks(k_cache, v_cache, block_table, seed: int):
     v2[perm] = v_cache
     t2 = np.where(block_table >= 0, perm[np.maximum(block_table, 0)], -1).astype(np.int32)
     return k2, v2, t2
+
+
+# --------------------------------------------------------------------------
+# Output-head workloads
+# --------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class MixConfig:
+    """Next-token logits of both flows for a batch of sequences.
+
+    Logits are normal draws with standard deviation ``std``; in a fraction
+    ``peak_rows`` of the sequences, ``peak_tokens`` random tokens of each
+    flow's row get ``peak_boost`` added (a confident distribution)."""
+
+    name: str
+    batch: int
+    vocab: int
+    std: float = 2.0
+    peak_rows: float = 0.5
+    peak_tokens: int = 4
+    peak_boost: float = 12.0
+
+    def replace(self, **kw) -> "MixConfig":
+        return dataclasses.replace(self, **kw)
+
+
+def make_mixture_case(cfg: MixConfig, seed: int):
+    """(logits1, logits2, u): float32 [batch, vocab] twice and float32 [batch] in [0, 1)."""
+    l1 = _normal(seed, "l1", (), (cfg.batch, cfg.vocab), cfg.std)
+    l2 = _normal(seed, "l2", (), (cfg.batch, cfg.vocab), cfg.std)
+    rng = _rng(seed, "lpeak")
+    for b in range(cfg.batch):
+        if rng.random() < cfg.peak_rows:
+            for row in (l1, l2):
+                row[b, rng.choice(cfg.vocab, size=min(cfg.peak_tokens, cfg.vocab), replace=False)] += \
+                    np.float32(cfg.peak_boost)
+    u = _rng(seed, "u").random(cfg.batch, dtype=np.float32)
+    return l1, l2, u
+
+
+@dataclass(frozen=True)
+class HeadConfig:
+    """Shared output head: both flows' final hidden states times one vocabulary matrix."""
+
+    name: str
+    batch: int
+    hidden: int
+    vocab: int
+    x_std: float = 1.0
+    w_std: float = 0.02
+
+    def replace(self, **kw) -> "HeadConfig":
+        return dataclasses.replace(self, **kw)
+
+
+# The output head after the C5 layer: batch 32, hidden 4096, weights ~ N(0, 0.02). The pages
+# name no vocabulary; 32000 tokens is the size used with hidden 4096 by the common 7B models.
+HEAD = HeadConfig("head", batch=32, hidden=4096, vocab=32000)
+MIX = MixConfig("mix", batch=32, vocab=32000)
+
+
+def make_head_case(cfg: HeadConfig, seed: int):
+    """(h1, h2, w_bits, u): hidden states float32 [batch, hidden] (exact bf16 values), the
+    vocabulary matrix as bf16 bits [vocab, hidden] (row-major), uniforms float32 [batch]."""
+    h1 = bf16_bits_to_f32(f32_to_bf16_bits(_normal(seed, "h1", (), (cfg.batch, cfg.hidden), cfg.x_std)))
+    h2 = bf16_bits_to_f32(f32_to_bf16_bits(_normal(seed, "h2", (), (cfg.batch, cfg.hidden), cfg.x_std)))
+    w = f32_to_bf16_bits(_normal(seed, "wlm", (), (cfg.vocab, cfg.hidden), cfg.w_std))
+    u = _rng(seed, "u").random(cfg.batch, dtype=np.float32)
+    return h1, h2, w, u

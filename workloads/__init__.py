@@ -40,7 +40,8 @@ BF16_NAN_BITS = np.uint16(0x7FC0)
 _TAG = {"q1": 1, "q2": 2, "a": 3, "k": 4, "v": 5, "peak": 6, "len": 7, "perm": 8,
         "x1": 11, "x2": 12, "wq": 13, "wk": 14, "wv": 15, "wo": 16, "wg": 17,
         "wu": 18, "wd": 19, "b": 20, "c": 21, "l1": 22, "l2": 23, "u": 24, "lpeak": 25, "wlm": 26,
-        "h1": 27, "h2": 28}
+        "h1": 27, "h2": 28, "mh1": 29, "mh2": 30, "mg": 31, "mu": 32, "md": 33, "mr": 34, "mb": 35, "mc": 36,
+        "mres1": 37, "mres2": 38}
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -125,7 +126,7 @@ C3 = AttnConfig("c3", batch=64, num_q_heads=64, num_kv_heads=8, head_dim=128, dt
 C4 = AttnConfig("c4", batch=4, num_q_heads=32, num_kv_heads=8, head_dim=128, dtype="bf16",
                 ctx_lens=(131072,) * 4, peaky_fraction=0.01, peaky_factor=8.0)
 ATTN_CONFIGS = {"c1": C1, "c2": C2, "c3": C3, "c4": C4}
-SEEDS = {"c1": 1001, "c2": 1002, "c3": 1003, "c4": 1004, "c5": 1005, "head": 1006, "mix": 1007}
+SEEDS = {"c1": 1001, "c2": 1002, "c3": 1003, "c4": 1004, "c5": 1005, "head": 1006, "mix": 1007, "moe": 1008}
 
 
 def draw_ctx_lens(cfg: AttnConfig, seed: int) -> np.ndarray:
@@ -413,3 +414,65 @@ def make_head_case(cfg: HeadConfig, seed: int):
     w = f32_to_bf16_bits(_normal(seed, "wlm", (), (cfg.vocab, cfg.hidden), cfg.w_std))
     u = _rng(seed, "u").random(cfg.batch, dtype=np.float32)
     return h1, h2, w, u
+
+
+# --------------------------------------------------------------------------
+# Mixture-of-experts workloads
+# --------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class MoeConfig:
+    """A SwiGLU mixture-of-experts FFN at one decode step: `experts` experts of width `mlp`, a
+    shared router, primary fan-out k1 and auxiliary fan-out k2 (k1 <= k2)."""
+
+    name: str
+    batch: int
+    hidden: int
+    mlp: int
+    experts: int
+    k1: int
+    k2: int
+    w_std: float = 0.02
+    x_std: float = 1.0
+    coupling_std: float = 0.1
+
+    def replace(self, **kw) -> "MoeConfig":
+        return dataclasses.replace(self, **kw)
+
+
+# The MoE FFN after the C5 attention block: batch 32, hidden 4096, weights ~ N(0, 0.02); 64
+# experts of width 1024 with the primary taking its top 4 and the auxiliary flow the top 8 of the
+# primary's ranking. The pages name no expert configuration.
+MOE = MoeConfig("moe", batch=32, hidden=4096, mlp=1024, experts=64, k1=4, k2=8)
+
+
+@dataclass
+class MoeCase:
+    cfg: MoeConfig
+    h1: np.ndarray    # float32 [B, hidden], exact bf16 values (the FFN inputs)
+    h2: np.ndarray
+    res1: np.ndarray  # float32 [B, hidden] (residual stream added to the FFN output)
+    res2: np.ndarray
+    wg: np.ndarray    # bf16 bits [E, mlp, hidden]
+    wu: np.ndarray    # bf16 bits [E, mlp, hidden]
+    wd: np.ndarray    # bf16 bits [E, hidden, mlp]
+    wr: np.ndarray    # bf16 bits [E, hidden] router
+    b: np.ndarray     # float32 [mlp]
+    c: np.ndarray     # float32 [hidden]
+
+
+def make_moe_case(cfg: MoeConfig, seed: int) -> MoeCase:
+    """All inputs of one MoE FFN step (router logits are h_f Wr^T, computed by the consumer)."""
+    def acts(tag):
+        return bf16_bits_to_f32(f32_to_bf16_bits(_normal(seed, tag, (), (cfg.batch, cfg.hidden), cfg.x_std)))
+    wg = np.stack([f32_to_bf16_bits(_normal(seed, "mg", (e,), (cfg.mlp, cfg.hidden), cfg.w_std))
+                   for e in range(cfg.experts)])
+    wu = np.stack([f32_to_bf16_bits(_normal(seed, "mu", (e,), (cfg.mlp, cfg.hidden), cfg.w_std))
+                   for e in range(cfg.experts)])
+    wd = np.stack([f32_to_bf16_bits(_normal(seed, "md", (e,), (cfg.hidden, cfg.mlp), cfg.w_std))
+                   for e in range(cfg.experts)])
+    wr = f32_to_bf16_bits(_normal(seed, "mr", (), (cfg.experts, cfg.hidden), cfg.w_std))
+    return MoeCase(cfg, acts("mh1"), acts("mh2"), _normal(seed, "mres1", (), (cfg.batch, cfg.hidden)),
+                   _normal(seed, "mres2", (), (cfg.batch, cfg.hidden)), wg, wu, wd, wr,
+                   _normal(seed, "mb", (), (cfg.mlp,), cfg.coupling_std),
+                   _normal(seed, "mc", (), (cfg.hidden,), cfg.coupling_std))

@@ -20,7 +20,7 @@ of the split kernel against the 8 TB/s peak, the measured stream-read ceiling,
 the auxiliary flow's increment over a one-flow run of the same kernel, and the
 CPU oracle's rate on a bounded sample (context only).
 
-    python bench.py [--steps K] [--warmup W] [--config c2|c3|c4|c5|head]
+    python bench.py [--steps K] [--warmup W] [--config c2|c3|c4|c5|head|moe]
 """
 import argparse
 import hashlib
@@ -264,14 +264,108 @@ def bench_head(args):
                       "mixture_gbps": mix_bytes / (mix_ms * 1e-3) / 1e9}), flush=True)
 
 
+def bench_moe(args):
+    """One mixture-of-experts FFN step with router replay (batch 32, hidden 4096, 64 experts of width
+    1024, primary fan-out 4, auxiliary fan-out 8): both flows' router logits from one read of the
+    shared router (dfa_dual_gemv), the selection and mixing weights (dfa_moe_route), and the experts
+    (dfa_moe_ffn: grouped gate/up and down GEMVs, each selected expert read once for both flows, and
+    the weighted combination)."""
+    import numpy as np
+    import torch
+
+    import dual_flow_shared_decode_amd as dfa
+    import workloads as W
+    from workloads.device import to_device
+
+    cfg = W.MOE
+    log("generating moe inputs")
+    case = W.make_moe_case(cfg, W.SEEDS["moe"])
+
+    def pack(bits):
+        ne, n, k = bits.shape
+        src = to_device(bits)
+        dst = torch.empty_like(src)
+        for e in range(ne):
+            dfa.dfa_pack_weight(src[e], dst[e], n, k)
+        return dst
+    wg, wu, wd = pack(case.wg), pack(case.wu), pack(case.wd)
+    wr = pack(case.wr[None])[0]
+    h1, h2, res1, res2 = (to_device(x) for x in (case.h1, case.h2, case.res1, case.res2))
+    bvec, cvec = to_device(case.b), to_device(case.c)
+    rd = dfa.GemvDesc(batch=cfg.batch, n=cfg.experts, k=cfg.hidden, num_flows=2, epilogue=dfa.DFA_EPI_NONE,
+                      x_exact_bf16=1, k_split=0, rows_per_wg=0)
+    rws = torch.empty(max(dfa.dfa_dual_gemv_workspace_size(rd) // 4, 4), device="cuda")
+    r1 = torch.empty((cfg.batch, cfg.experts), device="cuda")
+    r2 = torch.empty_like(r1)
+    out1 = torch.empty((cfg.batch, cfg.hidden), device="cuda")
+    out2 = torch.empty_like(out1)
+    stream = torch.cuda.current_stream()
+
+    def make(k2):
+        d = dfa.MoeDesc(batch=cfg.batch, hidden=cfg.hidden, mlp=cfg.mlp, num_experts=cfg.experts, k1=cfg.k1, k2=k2,
+                        x_exact_bf16=1)
+        routing = torch.empty(dfa.dfa_moe_routing_size(d) // 4, dtype=torch.int32, device="cuda")
+        ws = torch.empty(dfa.dfa_moe_workspace_size(d) // 4, device="cuda")
+
+        def step():
+            dfa.dfa_dual_gemv(rd, wr, None, h1, h2, None, None, None, r1, r2, None, rws, stream)
+            dfa.dfa_moe_route(d, r1, r2, routing, stream)
+            dfa.dfa_moe_ffn(d, wg, wu, wd, bvec, cvec, h1, h2, res1, res2, routing, out1, out2, ws, stream)
+        return d, routing, step
+
+    def timed(step, steps, warmup):
+        for _ in range(warmup):
+            step()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(steps):
+            step()
+        end.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / steps
+
+    def distinct(d, routing, k):  # experts the step reads: the union of the first k of every row
+        sel = routing.cpu().numpy()[:cfg.batch * d.k2].reshape(cfg.batch, d.k2)
+        return len(np.unique(sel[:, :k]))
+
+    warmup = max(args.warmup, 20)
+    d, routing, step = make(cfg.k2)
+    ms = timed(step, args.steps, warmup)
+    used = distinct(d, routing, cfg.k2)
+    used_primary = distinct(d, routing, cfg.k1)
+    d_eq, routing_eq, step_eq = make(cfg.k1)
+    ms_eq = timed(step_eq, args.steps, warmup)
+    expert_bytes = 3 * cfg.hidden * cfg.mlp * 2
+    act = 4 * cfg.batch * cfg.hidden * 2 * 3  # h in (router and experts' first read), res in, out
+    inter = 4 * cfg.batch * cfg.k2 * 2 * (cfg.mlp + cfg.hidden) * 2  # intermediates and expert outputs, out and in
+    nbytes = used * expert_bytes + 2 * cfg.experts * cfg.hidden + act + inter
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    log(f"moe step {ms * 1e3:.1f} us: {used} of {cfg.experts} experts read ({used_primary} for the primary's "
+        f"fan-out alone), {nbytes / 1e6:.0f} MB -> {gbps:.0f} GB/s; with k2 = k1 = {cfg.k1}: {ms_eq * 1e3:.1f} us")
+    print(json.dumps({"metric": "dual-flow MoE FFN step (router replay): tokens/s (both flows) + achieved HBM GB/s",
+                      "value": 2 * cfg.batch / (ms * 1e-3), "unit": "tokens/s (both flows)", "n_gpus": 1,
+                      "steps": args.steps, "warmup": warmup, "ms_per_step": ms, "higher_is_better": True,
+                      "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+                      "config": {"workload": "moe: SwiGLU mixture-of-experts FFN with router replay, batch 32, "
+                                             "hidden 4096, 64 experts of width 1024, primary fan-out 4, auxiliary "
+                                             "fan-out 8", "batch": cfg.batch, "experts": cfg.experts,
+                                 "k1": cfg.k1, "k2": cfg.k2},
+                      "achieved_gbps": gbps, "hbm_peak_gbps": HBM_PEAK_GBPS, "frac_of_peak": gbps / HBM_PEAK_GBPS,
+                      "algorithmic_bytes_per_step": nbytes, "experts_read": used,
+                      "experts_read_primary_fanout": used_primary,
+                      "ms_per_step_aux_fanout_equal_to_primary": ms_eq,
+                      "aux_fanout_increment": ms / ms_eq - 1.0}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="c2", choices=["c2", "c3", "c4", "c5", "head"],
+    ap.add_argument("--config", default="c2", choices=["c2", "c3", "c4", "c5", "head", "moe"],
                     help="c2 (default): the attention workload the metric is quoted on; c5: a whole layer step; "
-                         "head: the dual output head and mixture sampling")
+                         "head: the dual output head and mixture sampling; moe: the MoE FFN with router replay")
     ap.add_argument("--split", type=int, default=0, help="positions per split (0: library choice)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -298,6 +392,9 @@ def main():
         return
     if args.config == "head":
         bench_head(args)
+        return
+    if args.config == "moe":
+        bench_moe(args)
         return
     cfg = W.ATTN_CONFIGS[args.config]
     log(f"generating {cfg.name} inputs")

@@ -22,6 +22,7 @@ EXPORTS = ["dfa_decode_attn_split_len", "dfa_decode_attn_num_splits", "dfa_decod
            "dfa_dual_gemv_workspace_size", "dfa_dual_gemv", "dfa_pack_weight",
            "dfa_decode_layer_workspace_size", "dfa_decode_layer",
            "dfa_mixture_workspace_size", "dfa_mixture_sample",
+           "dfa_moe_routing_size", "dfa_moe_route", "dfa_moe_workspace_size", "dfa_moe_ffn",
            "dfa_status_string", "dfa_last_error", "dfa_version", "dfa_stream_read", "dfa_stream_read_sink_bytes"]
 
 DFA_EPI_NONE, DFA_EPI_RESIDUAL, DFA_EPI_SWIGLU, DFA_EPI_RESIDUAL_COUPLED, DFA_EPI_KV_APPEND = range(5)
@@ -81,6 +82,12 @@ class MixtureDesc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("vocab", ctypes.c_int32)]
 
 
+class MoeDesc(ctypes.Structure):
+    """Mirror of dfa_moe_desc."""
+
+    _fields_ = [(f, ctypes.c_int32) for f in ("batch", "hidden", "mlp", "num_experts", "k1", "k2", "x_exact_bf16")]
+
+
 class KernelEvents(ctypes.Structure):
     """Mirror of dfa_kernel_events (hipEvent_t handles)."""
 
@@ -118,6 +125,11 @@ def lib() -> ctypes.CDLL:
             "dfa_mixture_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(MixtureDesc)]),
             "dfa_mixture_sample": (ctypes.c_int, [ctypes.POINTER(MixtureDesc), _P, _P, _P, _P, _P, _P, _P, _P,
                                                   ctypes.c_size_t, _P]),
+            "dfa_moe_routing_size": (ctypes.c_size_t, [ctypes.POINTER(MoeDesc)]),
+            "dfa_moe_route": (ctypes.c_int, [ctypes.POINTER(MoeDesc), _P, _P, _P, ctypes.c_size_t, _P]),
+            "dfa_moe_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(MoeDesc)]),
+            "dfa_moe_ffn": (ctypes.c_int, [ctypes.POINTER(MoeDesc), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                           _P, ctypes.c_size_t, _P]),
             "dfa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
             "dfa_last_error": (ctypes.c_char_p, []),
             "dfa_version": (ctypes.c_int32, []),
@@ -269,6 +281,29 @@ def dfa_mixture_sample(desc, logits1, logits2, u, token, greedy, alpha, p_mix, w
     _check(lib().dfa_mixture_sample(ctypes.byref(desc), _ptr(logits1), _ptr(logits2), _ptr(u), _ptr(token),
                                     _ptr(greedy), _ptr(alpha), _ptr(p_mix), _ptr(workspace), ws_bytes,
                                     _stream(stream)))
+
+
+def dfa_moe_routing_size(desc: MoeDesc) -> int:
+    return int(lib().dfa_moe_routing_size(ctypes.byref(desc)))
+
+
+def dfa_moe_workspace_size(desc: MoeDesc) -> int:
+    return int(lib().dfa_moe_workspace_size(ctypes.byref(desc)))
+
+
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def dfa_moe_route(desc, r1, r2, routing, stream=None):
+    _check(lib().dfa_moe_route(ctypes.byref(desc), _ptr(r1), _ptr(r2), _ptr(routing), _nbytes(routing),
+                               _stream(stream)))
+
+
+def dfa_moe_ffn(desc, w_gate, w_up, w_down, b, c, h1, h2, res1, res2, routing, out1, out2, workspace, stream=None):
+    _check(lib().dfa_moe_ffn(ctypes.byref(desc), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(b), _ptr(c), _ptr(h1),
+                             _ptr(h2), _ptr(res1), _ptr(res2), _ptr(routing), _ptr(out1), _ptr(out2), _ptr(workspace),
+                             _nbytes(workspace), _stream(stream)))
 
 
 def dfa_stream_read(buf, sink, stream=None):

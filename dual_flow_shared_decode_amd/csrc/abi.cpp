@@ -569,6 +569,171 @@ dfa_status dfa_mixture_sample(const dfa_mixture_desc* d, const float* logits1, c
   }
 }
 
+static dfa_status validate_moe(const dfa_moe_desc* d) {
+  if (!d) return fail(DFA_ERR_NULL, "desc is NULL");
+  if (d->batch < 1 || d->batch > 32) return fail(DFA_ERR_SHAPE, "batch must be in [1, 32]");
+  if (d->hidden < 128 || d->hidden % 128 != 0 || d->mlp < 128 || d->mlp % 128 != 0)
+    return fail(DFA_ERR_SHAPE, "hidden and mlp must be positive multiples of 128");
+  if (d->num_experts < 1 || d->num_experts > dfa::kMoeMaxExperts)
+    return fail(DFA_ERR_SHAPE, "num_experts must be in [1, 1024]");
+  if (d->k1 < 1 || d->k1 > d->k2 || d->k2 > d->num_experts || d->k2 > dfa::kMoeMaxK)
+    return fail(DFA_ERR_SHAPE, "fan-outs must satisfy 1 <= k1 <= k2 <= min(num_experts, 32)");
+  return DFA_OK;
+}
+
+// Weight rows per workgroup of the grouped expert GEMVs.
+constexpr int kMoeRowsUp = 128;
+constexpr int kMoeRowsDown = 128;
+
+// Routing buffer: int32 sel [batch][k2], then float g1 [batch][k1], then float g2 [batch][k2],
+// each section starting on a 16-byte boundary.
+struct MoeRouting {
+  size_t g1_off, g2_off, bytes;
+};
+static MoeRouting moe_routing_layout(const dfa_moe_desc* d) {
+  auto up16 = [](size_t x) { return (x + 15) & ~size_t(15); };
+  MoeRouting r;
+  r.g1_off = up16(size_t(d->batch) * d->k2 * sizeof(int32_t));
+  r.g2_off = r.g1_off + up16(size_t(d->batch) * d->k1 * sizeof(float));
+  r.bytes = r.g2_off + up16(size_t(d->batch) * d->k2 * sizeof(float));
+  return r;
+}
+
+size_t dfa_moe_routing_size(const dfa_moe_desc* d) {
+  if (validate_moe(d) != DFA_OK) return 0;
+  return moe_routing_layout(d).bytes;
+}
+
+size_t dfa_moe_workspace_size(const dfa_moe_desc* d) {
+  if (validate_moe(d) != DFA_OK) return 0;
+  // both flows' expert intermediates [batch][k2][2][mlp], then expert outputs [batch][k2][2][hidden]
+  return size_t(d->batch) * d->k2 * 2 * (size_t(d->mlp) + d->hidden) * sizeof(float);
+}
+
+dfa_status dfa_moe_route(const dfa_moe_desc* d, const float* r1, const float* r2, void* routing,
+                         size_t routing_bytes, void* stream) {
+  try {
+    dfa_status st = validate_moe(d);
+    if (st != DFA_OK) return st;
+    if (!r1 || !r2 || !routing) return fail(DFA_ERR_NULL, "r1, r2 and routing are required");
+    if (!aligned16(r1) || !aligned16(r2) || !aligned16(routing))
+      return fail(DFA_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
+    const MoeRouting lay = moe_routing_layout(d);
+    if (routing_bytes < lay.bytes) return fail(DFA_ERR_WORKSPACE, "routing smaller than dfa_moe_routing_size()");
+    char* base = static_cast<char*>(routing);
+    dfa::MoeRouteParams p{};
+    p.r1 = r1;
+    p.r2 = r2;
+    p.sel = reinterpret_cast<int32_t*>(base);
+    p.g1 = reinterpret_cast<float*>(base + lay.g1_off);
+    p.g2 = reinterpret_cast<float*>(base + lay.g2_off);
+    p.batch = d->batch;
+    p.experts = d->num_experts;
+    p.k1 = d->k1;
+    p.k2 = d->k2;
+    const hipError_t e = dfa::launch_moe_route(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(DFA_ERR_HIP, std::string("moe route launch: ") + hipGetErrorString(e));
+    return DFA_OK;
+  } catch (...) {
+    return fail(DFA_ERR_HIP, "unexpected host exception");
+  }
+}
+
+dfa_status dfa_moe_ffn(const dfa_moe_desc* d, const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
+                       const float* b, const float* c, const float* h1, const float* h2, const float* res1,
+                       const float* res2, const void* routing, float* out1, float* out2, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  try {
+    dfa_status st = validate_moe(d);
+    if (st != DFA_OK) return st;
+    if (!w_gate || !w_up || !w_down || !h1 || !h2 || !routing || !out1 || !out2)
+      return fail(DFA_ERR_NULL, "weights, h1, h2, routing, out1 and out2 are required");
+    const void* ptrs[] = {w_gate, w_up, w_down, b, c, h1, h2, res1, res2, routing, out1, out2, workspace};
+    for (const void* q : ptrs)
+      if (q && !aligned16(q)) return fail(DFA_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
+    const size_t need = dfa_moe_workspace_size(d);
+    if (!workspace || workspace_bytes < need) return fail(DFA_ERR_WORKSPACE, "workspace smaller than dfa_moe_workspace_size()");
+    const MoeRouting lay = moe_routing_layout(d);
+    const char* rb = static_cast<const char*>(routing);
+    const int32_t* sel = reinterpret_cast<const int32_t*>(rb);
+    float* z = static_cast<float*>(workspace);
+    float* y = z + size_t(d->batch) * d->k2 * 2 * d->mlp;
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+
+    // gate and up projections of every selected expert, SwiGLU and b in the epilogue
+    dfa::GemvParams g{};
+    g.batch = d->batch;
+    g.flows = 2;
+    g.cbf = (d->batch + 15) / 16;
+    g.m_pad = 2 * g.cbf * 16;
+    g.k_split = 1;
+    g.moe_sel = sel;
+    g.moe_k1 = d->k1;
+    g.moe_k2 = d->k2;
+    g.moe_experts = d->num_experts;
+    dfa::GemvParams up = g;
+    up.w = w_gate;
+    up.w2 = w_up;
+    up.x1 = h1;
+    up.x2 = h2;
+    up.couple = b;
+    up.y1 = up.y2 = z;
+    up.n = d->mlp;
+    up.k = d->hidden;
+    up.k_range = d->hidden;
+    up.pair = 1;
+    up.x_exact = d->x_exact_bf16 != 0;
+    up.epilogue = dfa::kEpiSwiglu;
+    up.w_seg1 = up.w_seg2 = w_gate;
+    up.seg1_row = up.seg2_row = d->mlp;
+    up.moe_wstride = int64_t(d->mlp) * d->hidden;
+    up.rows_per_wg = d->mlp % kMoeRowsUp == 0 ? kMoeRowsUp : 64;
+    up.moe_rgs = d->mlp / up.rows_per_wg;
+    up.moe_row_s = 1;
+    hipError_t e = dfa::launch_gemv(up, hs);
+    if (e != hipSuccess) return fail(DFA_ERR_HIP, std::string("moe gate/up launch: ") + hipGetErrorString(e));
+    // down projection of every selected expert, from the intermediates [batch][k2][2][mlp]
+    dfa::GemvParams dn = g;
+    dn.w = w_down;
+    dn.x1 = dn.x2 = z;
+    dn.y1 = dn.y2 = y;
+    dn.n = d->hidden;
+    dn.k = d->mlp;
+    dn.k_range = d->mlp;
+    dn.pair = 0;
+    dn.x_exact = 0;
+    dn.epilogue = dfa::kEpiNone;
+    dn.w_seg1 = dn.w_seg2 = w_down;
+    dn.seg1_row = dn.seg2_row = d->hidden;
+    dn.moe_wstride = int64_t(d->hidden) * d->mlp;
+    dn.rows_per_wg = d->hidden % kMoeRowsDown == 0 ? kMoeRowsDown : 64;
+    dn.moe_rgs = d->hidden / dn.rows_per_wg;
+    dn.moe_row_s = 2 * d->k2;
+    dn.moe_row_slot = 2;
+    dn.moe_row_f = 1;
+    e = dfa::launch_gemv(dn, hs);
+    if (e != hipSuccess) return fail(DFA_ERR_HIP, std::string("moe down launch: ") + hipGetErrorString(e));
+    dfa::MoeCombineParams cp{};
+    cp.y = y;
+    cp.g1 = reinterpret_cast<const float*>(rb + lay.g1_off);
+    cp.g2 = reinterpret_cast<const float*>(rb + lay.g2_off);
+    cp.res1 = res1;
+    cp.res2 = res2;
+    cp.c = c;
+    cp.out1 = out1;
+    cp.out2 = out2;
+    cp.batch = d->batch;
+    cp.hidden = d->hidden;
+    cp.k1 = d->k1;
+    cp.k2 = d->k2;
+    e = dfa::launch_moe_combine(cp, hs);
+    if (e != hipSuccess) return fail(DFA_ERR_HIP, std::string("moe combine launch: ") + hipGetErrorString(e));
+    return DFA_OK;
+  } catch (...) {
+    return fail(DFA_ERR_HIP, "unexpected host exception");
+  }
+}
+
 dfa_status dfa_pack_weight(const uint16_t* w, uint16_t* w_tiled, int32_t n, int32_t k, void* stream) {
   if (!w || !w_tiled) return fail(DFA_ERR_NULL, "w and w_tiled are required");
   if (n < 16 || n % 16 != 0 || k < 8 || k % 8 != 0) return fail(DFA_ERR_SHAPE, "n must be a multiple of 16, k of 8");

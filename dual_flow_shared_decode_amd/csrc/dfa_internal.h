@@ -65,6 +65,15 @@ struct GemvParams {
   const uint16_t* w_seg2;  // w_seg2 (each tiled on its own); seg1_row = seg2_row = n: one matrix
   int32_t seg1_row, seg2_row;
   int32_t q_cols, kv_cols;  // kEpiQkv
+  // Grouped (mixture-of-experts) launch when moe_sel is set: moe_sel [batch][moe_k2]
+  // experts per sequence in ranking order (the first moe_k1 the primary's); the
+  // matrices of expert e start e * moe_wstride elements after w (and w2);
+  // moe_rgs row groups per expert. Activation row of (sequence s, slot, flow f):
+  // s * moe_row_s + slot * moe_row_slot + f * moe_row_f of x_f. Outputs go to
+  // rows ((s * moe_k2 + slot) * 2 + f) of y1 (= y2).
+  const int32_t* moe_sel;
+  int64_t moe_wstride;
+  int32_t moe_k1, moe_k2, moe_experts, moe_rgs, moe_row_s, moe_row_slot, moe_row_f;
   uint16_t* kv_k;      // KV append target
   uint16_t* kv_v;
   const int32_t* kv_table;
@@ -91,6 +100,31 @@ struct MixParams {
   int32_t batch, vocab, chunks;
 };
 
+// Mixture-of-experts routing and output combination.
+constexpr int kMoeMaxExperts = 1024;
+constexpr int kMoeMaxK = 32;
+
+struct MoeRouteParams {
+  const float* r1;  // [batch, experts] router logits of the primary flow
+  const float* r2;  // [batch, experts] of the auxiliary flow
+  int32_t* sel;     // [batch, k2] experts in ranking order
+  float* g1;        // [batch, k1]
+  float* g2;        // [batch, k2]
+  int32_t batch, experts, k1, k2;
+};
+
+struct MoeCombineParams {
+  const float* y;     // [batch][k2][2][hidden] expert outputs of both flows
+  const float* g1;
+  const float* g2;
+  const float* res1;  // [batch, hidden] or null
+  const float* res2;
+  const float* c;     // [hidden] or null
+  float* out1;
+  float* out2;
+  int32_t batch, hidden, k1, k2;
+};
+
 // Optional events recorded by the runtime at the start and end of a kernel's
 // own dispatch (no extra commands on the stream).
 struct KernelEvents {
@@ -107,6 +141,8 @@ hipError_t launch_gemv_finalize(const GemvParams& p, hipStream_t s);
 hipError_t launch_pack_weight(const uint16_t* w, uint16_t* wt, int n, int k, hipStream_t s);
 size_t gemv_chunk();
 hipError_t launch_mixture(const MixParams& p, hipStream_t s);
+hipError_t launch_moe_route(const MoeRouteParams& p, hipStream_t s);
+hipError_t launch_moe_combine(const MoeCombineParams& p, hipStream_t s);
 size_t mixture_chunks(int vocab);
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s);
 size_t stream_read_threads();

@@ -117,59 +117,60 @@ __device__ __forceinline__ void kv_append(const GemvParams& p, int s, int c0, co
 }
 
 // Epilogue of one sequence s and four consecutive columns n0..n0+3, from the
-// sums y[flow][matrix][j] of both flows (flow 2 unused with one flow).
-__device__ __forceinline__ void apply_epilogue(const GemvParams& p, int s, int n0, const float (&y)[2][2][4]) {
-  const size_t o = (size_t)s * p.n + n0;
+// sums y[flow][matrix][j] of both flows (flow 2 unused with one flow); o1, o2:
+// element offsets of the outputs (and residuals) of the two flows.
+__device__ __forceinline__ void apply_epilogue(const GemvParams& p, int s, size_t o1, size_t o2, int n0,
+                                               const float (&y)[2][2][4]) {
   const bool two = p.flows == 2;
   float r1[4], r2[4];
   switch (p.epilogue) {
     case kEpiNone:
-      store4(p.y1 + o, y[0][0]);
-      if (two) store4(p.y2 + o, y[1][0]);
+      store4(p.y1 + o1, y[0][0]);
+      if (two) store4(p.y2 + o2, y[1][0]);
       break;
     case kEpiResidual: {
-      const float4 a = *(const float4*)(p.res1 + o);
+      const float4 a = *(const float4*)(p.res1 + o1);
       r1[0] = a.x + y[0][0][0]; r1[1] = a.y + y[0][0][1]; r1[2] = a.z + y[0][0][2]; r1[3] = a.w + y[0][0][3];
-      store4(p.y1 + o, r1);
+      store4(p.y1 + o1, r1);
       if (two) {
-        const float4 b = *(const float4*)(p.res2 + o);
+        const float4 b = *(const float4*)(p.res2 + o2);
         r2[0] = b.x + y[1][0][0]; r2[1] = b.y + y[1][0][1]; r2[2] = b.z + y[1][0][2]; r2[3] = b.w + y[1][0][3];
-        store4(p.y2 + o, r2);
+        store4(p.y2 + o2, r2);
       }
       break;
     }
     case kEpiSwiglu: {
 #pragma unroll
       for (int j = 0; j < 4; ++j) r1[j] = silu(y[0][0][j]) * y[0][1][j];
-      store4(p.y1 + o, r1);
+      store4(p.y1 + o1, r1);
       if (two) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float z2 = silu(y[1][0][j]) * y[1][1][j];
           r2[j] = p.couple ? fmaf(p.couple[n0 + j], r1[j], z2) : z2;
         }
-        store4(p.y2 + o, r2);
+        store4(p.y2 + o2, r2);
       }
       break;
     }
     case kEpiResidualCoupled: {
-      const float4 a = *(const float4*)(p.res1 + o);
+      const float4 a = *(const float4*)(p.res1 + o1);
       r1[0] = a.x + y[0][0][0]; r1[1] = a.y + y[0][0][1]; r1[2] = a.z + y[0][0][2]; r1[3] = a.w + y[0][0][3];
-      store4(p.y1 + o, r1);
+      store4(p.y1 + o1, r1);
       if (two) {
-        const float4 b = *(const float4*)(p.res2 + o);
+        const float4 b = *(const float4*)(p.res2 + o2);
         const float bb[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           r2[j] = bb[j] + (p.couple ? fmaf(p.couple[n0 + j], y[0][0][j], y[1][0][j]) : y[1][0][j]);
-        store4(p.y2 + o, r2);
+        store4(p.y2 + o2, r2);
       }
       break;
     }
     case kEpiKvAppend:
       // primary only: k = rows n of W, v = rows n of W2, appended at position ctx_lens[s]
-      if (p.y1) store4(p.y1 + o, y[0][0]);
-      if (p.y2) store4(p.y2 + o, y[0][1]);
+      if (p.y1) store4(p.y1 + o1, y[0][0]);
+      if (p.y2) store4(p.y2 + o1, y[0][1]);
       kv_append(p, s, n0, y[0][0], y[0][1]);
       break;
   }
@@ -185,18 +186,34 @@ struct XStage {
   bool live[kItems];  // false: the group is padding and converts to zeros
 };
 
-template <int NCB>
-__device__ __forceinline__ void fetch_x(const GemvParams& p, int k_begin, int st, XStage<NCB>& xr) {
+// GROUPED: activation column j of a flow is entry j of the workgroup's expert
+// (ent[j] = sequence | slot << 16, cnt entries); its row of x_f is
+// s * moe_row_s + slot * moe_row_slot + f * moe_row_f, and the primary's
+// column is live only where the primary selected the expert (slot < k1).
+template <int NCB, bool GROUPED>
+__device__ __forceinline__ void fetch_x(const GemvParams& p, int k_begin, int st, XStage<NCB>& xr, const int* ent,
+                                        int cnt) {
   const int kc = k_begin + st * kStage;
 #pragma unroll
   for (int it = 0; it < XStage<NCB>::kItems; ++it) {
     const int item = threadIdx.x + it * kGemvThreads;
     const int kg = item % (kStage / 8), m = item / (kStage / 8);
-    const int cb = m >> 4, f = cb / p.cbf, s = (cb - f * p.cbf) * 16 + (m & 15);
-    // groups past the stage (fewer than threads) or past the batch read row 0
-    // of x1, which always exists, and are replaced by zeros
-    const bool live = item < XStage<NCB>::kTotal && s < p.batch;
-    const float4* src = (const float4*)(live ? (f ? p.x2 : p.x1) + (size_t)s * p.k + kc + kg * 8 : p.x1 + kc);
+    const int cb = m >> 4, f = cb / p.cbf, j = (cb - f * p.cbf) * 16 + (m & 15);
+    // groups past the stage (fewer than threads), past the batch or past the
+    // expert's entries read row 0 of x1, which always exists, and are replaced
+    // by zeros
+    bool live;
+    size_t row;
+    if (GROUPED) {
+      const int en = j < cnt ? ent[j] : 0;
+      const int s = en & 0xFFFF, slot = en >> 16;
+      live = item < XStage<NCB>::kTotal && j < cnt && (f == 1 || slot < p.moe_k1);
+      row = (size_t)s * p.moe_row_s + (size_t)slot * p.moe_row_slot + (size_t)f * p.moe_row_f;
+    } else {
+      live = item < XStage<NCB>::kTotal && j < p.batch;
+      row = j;
+    }
+    const float4* src = (const float4*)(live ? (f ? p.x2 : p.x1) + row * p.k + kc + kg * 8 : p.x1 + kc);
     // the values are not touched here: the conversion (put_x) is the first use,
     // so the loads stay in flight until then
     xr.v[it][0] = src[0];
@@ -241,7 +258,12 @@ __device__ __forceinline__ void put_x(const XStage<NCB>& xr, uint16_t* xs) {
 // Wave w works on tile w % 4 with the k-steps of wave group w / 4: group g
 // takes k-steps 2g, 2g + 1 of every stage, so two waves per SIMD share the
 // stage's B operands and each holds half of the weights in flight.
-template <int NCB, bool PAIR, bool LO, int TILES>
+//
+// GROUPED (mixture of experts): grid row index = expert * moe_rgs + row group;
+// the workgroup multiplies its expert's matrices (moe_wstride elements apart)
+// with the rows of the sequences that selected the expert (moe_sel), found
+// here in sequence order, and exits at once if there are none. One k-range.
+template <int NCB, bool PAIR, bool LO, int TILES, bool GROUPED>
 __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvParams p) {
   constexpr int kTiles = TILES;                  // 16-row weight tiles per workgroup (4 or 8)
   constexpr int kGroups = kGemvWaves / kTiles;   // wave groups sharing the tiles (2 or 1)
@@ -267,7 +289,27 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvParams p) {
   // holds the workgroups of one or two of them and its L2 keeps only their
   // activations (measured: within noise of the row-group-first order, the
   // 4096 x 4096 GEMV 16.7 -> 16.0 us).
-  const int rg = blockIdx.y, ks = blockIdx.x;
+  int rg = blockIdx.y, expert = 0, cnt = 0;
+  const int ks = blockIdx.x;
+  __shared__ int ent[GROUPED ? 64 : 1];
+  __shared__ int ent_count;
+  if (GROUPED) {
+    expert = blockIdx.y / p.moe_rgs;
+    rg = blockIdx.y - expert * p.moe_rgs;
+    if (threadIdx.x < 64) {  // wave 0: lane s finds the slot of this expert in sequence s's selection
+      const int s = threadIdx.x;
+      int slot = -1;
+      if (s < p.batch)
+        for (int q = 0; q < p.moe_k2; ++q)
+          if (p.moe_sel[s * p.moe_k2 + q] == expert) slot = q;
+      const unsigned long long mask = __ballot(slot >= 0);
+      if (slot >= 0) ent[__popcll(mask & ((1ull << s) - 1))] = s | (slot << 16);
+      if (s == 0) ent_count = __popcll(mask);
+    }
+    __syncthreads();
+    cnt = ent_count;
+    if (cnt == 0) return;  // workgroup-uniform: no sequence selected this expert
+  }
   const int tile = rg * kTiles + wt;  // this wave's 16-row weight tile
   const int k_begin = ks * p.k_range;
   const int nst = (min(k_begin + p.k_range, p.k) - k_begin) / kStage;
@@ -280,7 +322,9 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvParams p) {
   // this wave's tile within its matrix (several matrices can share one launch, by row range)
   const int row0 = tile * 16;
   const int seg = row0 < p.seg1_row ? 0 : (row0 < p.seg2_row ? 1 : 2);
-  const uint16_t* const wmat = seg == 0 ? p.w : (seg == 1 ? p.w_seg1 : p.w_seg2);
+  const size_t wofs = GROUPED ? (size_t)expert * p.moe_wstride : 0;
+  const uint16_t* const wmat = (seg == 0 ? p.w : (seg == 1 ? p.w_seg1 : p.w_seg2)) + wofs;
+  const uint16_t* const wmat2 = PAIR ? p.w2 + wofs : nullptr;
   const int tile_in = (row0 - (seg == 0 ? 0 : (seg == 1 ? p.seg1_row : p.seg2_row))) / 16;
   auto fetch_w = [&](int st, WStage& w) __attribute__((always_inline)) {
     const int kg0 = (k_begin + st * kStage) / 8 + wg * kHalfSteps * 4;
@@ -288,7 +332,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvParams p) {
 #pragma unroll
     for (int k2 = 0; k2 < kHalfSteps; ++k2) {
       w.a[0][k2] = __builtin_nontemporal_load((const bf16x8*)(wmat + base + (size_t)k2 * 4 * 16 * 8));
-      if (PAIR) w.a[MATS - 1][k2] = __builtin_nontemporal_load((const bf16x8*)(p.w2 + base + (size_t)k2 * 4 * 16 * 8));
+      if (PAIR) w.a[MATS - 1][k2] = __builtin_nontemporal_load((const bf16x8*)(wmat2 + base + (size_t)k2 * 4 * 16 * 8));
     }
   };
 
@@ -305,15 +349,15 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvParams p) {
   WStage w0, w1, w2;  // three separately named buffers stay in registers
   XStage<NCB> x0, x1, x2;
   if (nst > 0) {
-    fetch_x<NCB>(p, k_begin, 0, x0);
+    fetch_x<NCB, GROUPED>(p, k_begin, 0, x0, ent, cnt);
     fetch_w(0, w0);
   }
   if (nst > 1) {
-    fetch_x<NCB>(p, k_begin, 1, x1);
+    fetch_x<NCB, GROUPED>(p, k_begin, 1, x1, ent, cnt);
     fetch_w(1, w1);
   }
   if (nst > 2) {
-    fetch_x<NCB>(p, k_begin, 2, x2);
+    fetch_x<NCB, GROUPED>(p, k_begin, 2, x2, ent, cnt);
     fetch_w(2, w2);
   }
   if (nst > 0) put_x<NCB, NH>(x0, &xs[0][0][0][0][0][0]);
@@ -341,7 +385,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvParams p) {
           for (int mat = 0; mat < MATS; ++mat)
             acc[mat][cb] = mfma(wj.a[mat][k2], xb[k2][cb][h], acc[mat][cb]);
     if (fetch) {
-      fetch_x<NCB>(p, k_begin, st + DEPTH, xj);
+      fetch_x<NCB, GROUPED>(p, k_begin, st + DEPTH, xj, ent, cnt);
       fetch_w(st + DEPTH, wj);
     }
     __syncthreads();
@@ -405,20 +449,29 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvParams p) {
         *(f32x4*)(res + ((size_t)mat * NCB * 16 + cb * 16 + col) * kRowsPerWg + wt * 16 + 4 * grp) = acc[mat][cb];
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < p.batch * (kRowsPerWg / 4); idx += kGemvThreads) {
-    const int s = idx / (kRowsPerWg / 4), c4 = (idx - s * (kRowsPerWg / 4)) * 4;
+  const int rows = GROUPED ? cnt : p.batch;  // activation columns per flow
+  for (int idx = threadIdx.x; idx < rows * (kRowsPerWg / 4); idx += kGemvThreads) {
+    const int j = idx / (kRowsPerWg / 4), c4 = (idx - j * (kRowsPerWg / 4)) * 4;
     float y[2][2][4];
 #pragma unroll
     for (int f = 0; f < 2; ++f)
 #pragma unroll
       for (int mat = 0; mat < 2; ++mat) {
         const bool have = f < p.flows && mat < MATS;
-        const int m = (f * p.cbf + (s >> 4)) * 16 + (s & 15);
+        const int m = (f * p.cbf + (j >> 4)) * 16 + (j & 15);
         const float4 v = have ? *(const float4*)(res + ((size_t)(mat < MATS ? mat : 0) * NCB * 16 + m) * kRowsPerWg + c4)
                               : make_float4(0.f, 0.f, 0.f, 0.f);
         y[f][mat][0] = v.x; y[f][mat][1] = v.y; y[f][mat][2] = v.z; y[f][mat][3] = v.w;
       }
-    apply_epilogue(p, s, rg * kRowsPerWg + c4, y);
+    const int n0 = rg * kRowsPerWg + c4;
+    if (GROUPED) {  // rows (sequence, slot, flow) of the output: [batch][k2][2][n]
+      const int s = ent[j] & 0xFFFF, slot = ent[j] >> 16;
+      const size_t o1 = ((size_t)(s * p.moe_k2 + slot) * 2) * p.n + n0;
+      apply_epilogue(p, s, o1, o1 + p.n, n0, y);
+    } else {
+      const size_t o = (size_t)j * p.n + n0;
+      apply_epilogue(p, j, o, o, n0, y);
+    }
   }
 }
 
@@ -487,19 +540,34 @@ __global__ __launch_bounds__(kFinalizeThreads) void gemv_finalize_kernel(GemvPar
       sum_splits<KS>(p, mats, mat, m, n0, y[f][mat]);
     }
   }
-  apply_epilogue(p, s, n0, y);
+  const size_t o = (size_t)s * p.n + n0;
+  apply_epilogue(p, s, o, o, n0, y);
 }
 
 hipError_t launch_gemv(const GemvParams& p, hipStream_t stream) {
-  const dim3 grid(p.k_split, p.n / p.rows_per_wg), block(kGemvThreads);
   const int ncb = p.flows * p.cbf;
   const bool lo = !p.x_exact;
   const int tiles = p.rows_per_wg / 16;
-#define DFA_GEMV_CASE(NCB_, PAIR_, LO_)                                                               \
-  if (ncb == NCB_ && p.pair == PAIR_ && lo == LO_) {                                                  \
-    if (tiles == 8) hipLaunchKernelGGL((gemv_kernel<NCB_, PAIR_, LO_, 8>), grid, block, 0, stream, p); \
-    else hipLaunchKernelGGL((gemv_kernel<NCB_, PAIR_, LO_, 4>), grid, block, 0, stream, p);            \
-    return hipGetLastError();                                                                         \
+  if (p.moe_sel) {  // grouped: two flows, one k-range
+    if (p.flows != 2 || (tiles != 4 && tiles != 8) || p.k_split != 1) return hipErrorInvalidValue;
+    const dim3 grid(1, (p.n / p.rows_per_wg) * p.moe_experts), block(kGemvThreads);
+#define DFA_GROUPED_CASE(NCB_, PAIR_, LO_)                                                                  \
+  if (ncb == NCB_ && p.pair == PAIR_ && lo == LO_) {                                                        \
+    if (tiles == 8) hipLaunchKernelGGL((gemv_kernel<NCB_, PAIR_, LO_, 8, true>), grid, block, 0, stream, p); \
+    else hipLaunchKernelGGL((gemv_kernel<NCB_, PAIR_, LO_, 4, true>), grid, block, 0, stream, p);            \
+    return hipGetLastError();                                                                               \
+  }
+    DFA_GROUPED_CASE(2, true, false) DFA_GROUPED_CASE(2, true, true) DFA_GROUPED_CASE(2, false, true)
+    DFA_GROUPED_CASE(4, true, false) DFA_GROUPED_CASE(4, true, true) DFA_GROUPED_CASE(4, false, true)
+#undef DFA_GROUPED_CASE
+    return hipErrorInvalidValue;
+  }
+  const dim3 grid(p.k_split, p.n / p.rows_per_wg), block(kGemvThreads);
+#define DFA_GEMV_CASE(NCB_, PAIR_, LO_)                                                                      \
+  if (ncb == NCB_ && p.pair == PAIR_ && lo == LO_) {                                                         \
+    if (tiles == 8) hipLaunchKernelGGL((gemv_kernel<NCB_, PAIR_, LO_, 8, false>), grid, block, 0, stream, p); \
+    else hipLaunchKernelGGL((gemv_kernel<NCB_, PAIR_, LO_, 4, false>), grid, block, 0, stream, p);            \
+    return hipGetLastError();                                                                                \
   }
   DFA_GEMV_CASE(1, false, false) DFA_GEMV_CASE(1, false, true) DFA_GEMV_CASE(1, true, false)
   DFA_GEMV_CASE(1, true, true) DFA_GEMV_CASE(2, false, false) DFA_GEMV_CASE(2, false, true)

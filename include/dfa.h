@@ -342,6 +342,72 @@ DFA_API dfa_status dfa_mixture_sample(const dfa_mixture_desc* desc, const float*
                                       const float* u, int32_t* token, int32_t* greedy, float* alpha, float* p_mix,
                                       void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * ------------------------------------------- mixture-of-experts FFN (router replay)
+ * A SwiGLU mixture-of-experts FFN for both flows at one decode step ("Mecanismos
+ * Chave", router replay: the auxiliary flow reuses the experts the primary
+ * router selected, with its own mixing weights; "Contribuições Principais",
+ * phase-specific MoE allocation: the two flows' expert fan-outs k1 and k2 are
+ * independent). This library's reading, for every sequence s:
+ *     experts ranked by the primary's router logits r1[s] (descending; equal
+ *     logits in index order); S1 = the first k1, S2 = the first k2 (k1 <= k2)
+ *     g1 = softmax of r1[s] over S1,  g2 = softmax of r2[s] over S2
+ *     z_f,e = silu(h_f Wg_e^T) * (h_f Wu_e^T);  z2,e += b * z1,e for e in S1
+ *     m1 = sum_{e in S1} g1(e) z1,e Wd_e^T,  m2 = sum_{e in S2} g2(e) z2,e Wd_e^T
+ *     out1 = res1 + m1,  out2 = res2 + m2 + c * m1
+ * Each selected expert's matrices are read once for every row of both flows
+ * that selected it. The primary flow's outputs never depend on the auxiliary
+ * flow's inputs (h2, r2, res2, b, c).
+ */
+typedef struct dfa_moe_desc {
+  int32_t batch;         /* sequences: 1..32 */
+  int32_t hidden;        /* model width: multiple of 128 */
+  int32_t mlp;           /* expert width: multiple of 128 */
+  int32_t num_experts;   /* 1..1024 */
+  int32_t k1, k2;        /* fan-outs: 1 <= k1 <= k2 <= min(num_experts, 32) */
+  int32_t x_exact_bf16;  /* 1: h1 and h2 hold exact bf16 values */
+} dfa_moe_desc;
+
+/*
+ * Bytes of a routing buffer: int32 sel [batch][k2] (experts in ranking order;
+ * the first k1 of a row are the primary's), then float32 g1 [batch][k1], then
+ * float32 g2 [batch][k2], each section starting on a 16-byte boundary. 0 if
+ * `desc` is invalid. A caller may also fill one itself (distinct experts in
+ * [0, num_experts) per row).
+ */
+DFA_API size_t dfa_moe_routing_size(const dfa_moe_desc* desc);
+
+/*
+ * Router replay: from both flows' router logits r1, r2 (float32
+ * [batch, num_experts], finite), writes the selection and both flows' mixing
+ * weights into `routing` (one launch on `stream`). Equal logits rank in index
+ * order; the mixing weights are summed in ranking order.
+ */
+DFA_API dfa_status dfa_moe_route(const dfa_moe_desc* desc, const float* r1, const float* r2, void* routing,
+                                 size_t routing_bytes, void* stream);
+
+/* Workspace bytes of dfa_moe_ffn: 4 * batch * k2 * 2 * (mlp + hidden); 0 if invalid. */
+DFA_API size_t dfa_moe_workspace_size(const dfa_moe_desc* desc);
+
+/*
+ * The experts and their combination (three launches on `stream`): grouped
+ * gate/up GEMV with SwiGLU and b, grouped down GEMV, and the weighted sums in
+ * ranking order with the residuals and c.
+ *  w_gate, w_up: bf16 [num_experts][mlp, hidden], w_down: bf16
+ *                [num_experts][hidden, mlp]; each expert's matrix tiled by
+ *                dfa_pack_weight, the experts back to back.
+ *  b: float32 [mlp] or NULL (0); c: float32 [hidden] or NULL (0).
+ *  h1, h2: float32 [batch, hidden] FFN inputs; res1, res2: float32
+ *          [batch, hidden] residuals or NULL (0); out1, out2: float32
+ *          [batch, hidden]; routing: as written by dfa_moe_route.
+ * Routing entries outside [0, num_experts) select nothing (their slots then
+ * read unwritten workspace). The workspace's contents on entry do not matter.
+ */
+DFA_API dfa_status dfa_moe_ffn(const dfa_moe_desc* desc, const uint16_t* w_gate, const uint16_t* w_up,
+                               const uint16_t* w_down, const float* b, const float* c, const float* h1,
+                               const float* h2, const float* res1, const float* res2, const void* routing,
+                               float* out1, float* out2, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Short fixed description of a status code. Never NULL. */
 DFA_API const char* dfa_status_string(dfa_status status);
 

@@ -196,3 +196,57 @@ def test_mixture_workspace_and_validation():
     for name in ("l1", "l2", "pm"):
         assert call(**{name: FAKE + 4}, nb=need - 4) == "DFA_ERR_ALIGNMENT", name
     assert call(ws=FAKE + 4) == "DFA_ERR_ALIGNMENT"
+
+
+def moe_desc(**kw):
+    d = dict(batch=32, hidden=4096, mlp=1024, num_experts=64, k1=4, k2=8, x_exact_bf16=1)
+    d.update(kw)
+    return dfa.MoeDesc(**d)
+
+
+def test_moe_sizes_and_validation():
+    d = moe_desc()
+    # sel int32 [32][8] | g1 float [32][4] | g2 float [32][8], 16-byte aligned sections
+    assert dfa.dfa_moe_routing_size(d) == 32 * 8 * 4 + 32 * 4 * 4 + 32 * 8 * 4
+    assert dfa.dfa_moe_routing_size(moe_desc(batch=3, k1=1, k2=3)) == 48 + 16 + 48
+    assert dfa.dfa_moe_workspace_size(d) == 4 * 32 * 8 * 2 * (1024 + 4096)
+    for bad in (dict(batch=0), dict(batch=33), dict(hidden=4000), dict(mlp=64), dict(num_experts=0),
+                dict(num_experts=1025), dict(k1=0), dict(k1=9), dict(k2=65), dict(num_experts=40, k2=33, k1=1)):
+        bd = moe_desc(**bad)
+        assert dfa.dfa_moe_routing_size(bd) == 0 and dfa.dfa_moe_workspace_size(bd) == 0, bad
+        with pytest.raises(dfa.DfaError) as e:
+            _lib._check(_lib.lib().dfa_moe_route(ctypes.byref(bd), FAKE, FAKE, FAKE, 1 << 20, None))
+        assert _lib.STATUS[e.value.status] == "DFA_ERR_SHAPE", bad
+
+
+def test_moe_call_errors():
+    d = moe_desc()
+    rb, wb = dfa.dfa_moe_routing_size(d), dfa.dfa_moe_workspace_size(d)
+
+    def route(**kw):
+        p = dict(r1=FAKE, r2=FAKE, rt=FAKE, nb=rb)
+        p.update(kw)
+        with pytest.raises(dfa.DfaError) as e:
+            _lib._check(_lib.lib().dfa_moe_route(ctypes.byref(d), p["r1"], p["r2"], p["rt"], p["nb"], None))
+        return _lib.STATUS[e.value.status]
+
+    def ffn(**kw):
+        p = dict(wg=FAKE, wu=FAKE, wd=FAKE, b=None, c=None, h1=FAKE, h2=FAKE, res1=None, res2=None, rt=FAKE,
+                 o1=FAKE, o2=FAKE, ws=FAKE, nb=wb - 4)
+        p.update(kw)
+        with pytest.raises(dfa.DfaError) as e:
+            _lib._check(_lib.lib().dfa_moe_ffn(ctypes.byref(d), p["wg"], p["wu"], p["wd"], p["b"], p["c"], p["h1"],
+                                               p["h2"], p["res1"], p["res2"], p["rt"], p["o1"], p["o2"], p["ws"],
+                                               p["nb"], None))
+        return _lib.STATUS[e.value.status]
+
+    for name in ("r1", "r2", "rt"):
+        assert route(**{name: None}) == "DFA_ERR_NULL"
+        assert route(**{name: FAKE + 4}) == "DFA_ERR_ALIGNMENT"
+    assert route(nb=rb - 4) == "DFA_ERR_WORKSPACE"
+    for name in ("wg", "wu", "wd", "h1", "h2", "rt", "o1", "o2"):
+        assert ffn(**{name: None}) == "DFA_ERR_NULL", name
+    for name in ("wg", "b", "c", "h2", "res1", "res2", "o2"):
+        assert ffn(**{name: FAKE + 4}) == "DFA_ERR_ALIGNMENT", name
+    assert ffn() == "DFA_ERR_WORKSPACE"
+    assert ffn(ws=None, nb=wb) == "DFA_ERR_WORKSPACE"

@@ -10,6 +10,7 @@
 
 #include "../../include/dfa.h"
 #include "dfa_internal.h"
+#include "ops_internal.h"
 
 namespace {
 

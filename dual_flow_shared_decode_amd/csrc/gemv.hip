@@ -42,6 +42,7 @@
 #include <math.h>
 
 #include "dfa_internal.h"
+#include "ops_internal.h"
 
 namespace dfa {
 

@@ -29,6 +29,7 @@
 #include <stdint.h>
 
 #include "dfa_internal.h"
+#include "ops_internal.h"
 
 namespace dfa {
 

@@ -23,6 +23,7 @@
 #include <stdint.h>
 
 #include "dfa_internal.h"
+#include "ops_internal.h"
 
 namespace dfa {
 

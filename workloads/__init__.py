@@ -41,7 +41,7 @@ _TAG = {"q1": 1, "q2": 2, "a": 3, "k": 4, "v": 5, "peak": 6, "len": 7, "perm": 8
         "x1": 11, "x2": 12, "wq": 13, "wk": 14, "wv": 15, "wo": 16, "wg": 17,
         "wu": 18, "wd": 19, "b": 20, "c": 21, "l1": 22, "l2": 23, "u": 24, "lpeak": 25, "wlm": 26,
         "h1": 27, "h2": 28, "mh1": 29, "mh2": 30, "mg": 31, "mu": 32, "md": 33, "mr": 34, "mb": 35, "mc": 36,
-        "mres1": 37, "mres2": 38}
+        "mres1": 37, "mres2": 38, "pq": 39, "pk": 40, "pv": 41, "pq2": 42, "pa": 43}
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -126,7 +126,7 @@ C3 = AttnConfig("c3", batch=64, num_q_heads=64, num_kv_heads=8, head_dim=128, dt
 C4 = AttnConfig("c4", batch=4, num_q_heads=32, num_kv_heads=8, head_dim=128, dtype="bf16",
                 ctx_lens=(131072,) * 4, peaky_fraction=0.01, peaky_factor=8.0)
 ATTN_CONFIGS = {"c1": C1, "c2": C2, "c3": C3, "c4": C4}
-SEEDS = {"c1": 1001, "c2": 1002, "c3": 1003, "c4": 1004, "c5": 1005, "head": 1006, "mix": 1007, "moe": 1008}
+SEEDS = {"c1": 1001, "c2": 1002, "c3": 1003, "c4": 1004, "c5": 1005, "head": 1006, "mix": 1007, "moe": 1008, "prefill": 1009}
 
 
 def draw_ctx_lens(cfg: AttnConfig, seed: int) -> np.ndarray:
@@ -476,3 +476,70 @@ def make_moe_case(cfg: MoeConfig, seed: int) -> MoeCase:
                    _normal(seed, "mres2", (), (cfg.batch, cfg.hidden)), wg, wu, wd, wr,
                    _normal(seed, "mb", (), (cfg.mlp,), cfg.coupling_std),
                    _normal(seed, "mc", (), (cfg.hidden,), cfg.coupling_std))
+
+
+# --------------------------------------------------------------------------
+# Prefill workloads
+# --------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class PrefillConfig:
+    """Prompts processed by the primary flow (causal self-attention), written to a paged cache."""
+
+    name: str
+    batch: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    lens: Tuple[int, ...]     # prompt lengths
+    block_size: int = 16
+    shuffle_blocks: bool = True
+    extra_slots: int = 16     # cache room past each prompt (the decode steps that follow)
+    std: float = 1.0
+    a_std: float = 0.1
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+    def replace(self, **kw) -> "PrefillConfig":
+        return dataclasses.replace(self, **kw)
+
+
+# Prompts of 4096 tokens, batch 4, 32/8 heads of 128 (the decode workloads' attention shape).
+PREFILL = PrefillConfig("prefill", batch=4, num_q_heads=32, num_kv_heads=8, head_dim=128, lens=(4096,) * 4)
+
+
+@dataclass
+class PrefillCase:
+    cfg: PrefillConfig
+    q: np.ndarray        # bf16 bits [B, Lmax, Hq, D]: the primary's queries over the prompt
+    k: np.ndarray        # bf16 bits [B, Lmax, Hkv, D]
+    v: np.ndarray
+    lens: np.ndarray     # int32 [B]
+    q2: np.ndarray       # bf16 bits [B, Hq, D]: the auxiliary query at the last prompt position
+    a: np.ndarray        # float32 [Hq * D]
+    k_cache: np.ndarray  # empty paged cache (NaN) that the prefill fills
+    v_cache: np.ndarray
+    block_table: np.ndarray
+    block_size: int
+    max_blocks_per_seq: int
+
+
+def make_prefill_case(cfg: PrefillConfig, seed: int) -> PrefillCase:
+    lens = np.asarray(cfg.lens, dtype=np.int32)
+    if lens.shape != (cfg.batch,):
+        raise ValueError("one length per prompt")
+    lmax = int(lens.max())
+    layout = plan_cache(cfg.batch, lens, cfg.block_size, 0, cfg.shuffle_blocks, seed, extra_slots=cfg.extra_slots)
+    q = f32_to_bf16_bits(_normal(seed, "pq", (), (cfg.batch, lmax, cfg.num_q_heads, cfg.head_dim), cfg.std))
+    k = f32_to_bf16_bits(_normal(seed, "pk", (), (cfg.batch, lmax, cfg.num_kv_heads, cfg.head_dim), cfg.std))
+    v = f32_to_bf16_bits(_normal(seed, "pv", (), (cfg.batch, lmax, cfg.num_kv_heads, cfg.head_dim), cfg.std))
+    q2 = f32_to_bf16_bits(_normal(seed, "pq2", (), (cfg.batch, cfg.num_q_heads, cfg.head_dim), cfg.std))
+    a = _normal(seed, "pa", (), (cfg.num_q_heads * cfg.head_dim,), cfg.a_std)
+    for b in range(cfg.batch):  # positions past a prompt are NaN: any read of them shows up
+        for x in (q, k, v):
+            x[b, lens[b]:] = BF16_NAN_BITS
+    k_cache, v_cache = empty_cache(layout, cfg.num_kv_heads, cfg.head_dim, "bf16")
+    return PrefillCase(cfg, q, k, v, lens, q2, a, k_cache, v_cache, layout.block_table, layout.block_size,
+                       layout.max_blocks_per_seq)

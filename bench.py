@@ -20,7 +20,7 @@ of the split kernel against the 8 TB/s peak, the measured stream-read ceiling,
 the auxiliary flow's increment over a one-flow run of the same kernel, and the
 CPU oracle's rate on a bounded sample (context only).
 
-    python bench.py [--steps K] [--warmup W] [--config c2|c3|c4|c5|head|moe]
+    python bench.py [--steps K] [--warmup W] [--config c2|c3|c4|c5|head|moe|prefill]
 """
 import argparse
 import hashlib
@@ -358,14 +358,87 @@ def bench_moe(args):
                       "aux_fanout_increment": ms / ms_eq - 1.0}), flush=True)
 
 
+def bench_prefill(args):
+    """Primary-only prefill of 4 prompts of 4096 tokens (32/8 heads of 128): the prompts' keys and values
+    written to the paged cache and causal self-attention (dfa_prefill), then the auxiliary flow's first
+    step at the last prompt position (dfa_decode_attn over the 4096 cached positions, both flows)."""
+    import numpy as np
+    import torch
+
+    import dual_flow_shared_decode_amd as dfa
+    import workloads as W
+    from workloads.device import to_device
+
+    cfg = W.PREFILL
+    log("generating prefill inputs")
+    case = W.make_prefill_case(cfg, W.SEEDS["prefill"])
+    t = {name: to_device(getattr(case, name)) for name in ("q", "k", "v", "lens", "k_cache", "v_cache",
+                                                            "block_table")}
+    lmax = case.q.shape[1]
+    o = torch.empty(case.q.shape, dtype=torch.float32, device="cuda")
+    pd = dfa.PrefillDesc(batch=cfg.batch, num_q_heads=cfg.num_q_heads, num_kv_heads=cfg.num_kv_heads,
+                         head_dim=cfg.head_dim, max_prompt_len=lmax, block_size=case.block_size,
+                         max_blocks_per_seq=case.max_blocks_per_seq, num_blocks=case.k_cache.shape[0],
+                         scale=cfg.scale)
+    stream = torch.cuda.current_stream()
+    last = to_device(np.stack([case.q[b, int(case.lens[b]) - 1] for b in range(cfg.batch)]))
+    ad = dfa.AttnDesc(batch=cfg.batch, num_q_heads=cfg.num_q_heads, num_kv_heads=cfg.num_kv_heads,
+                      head_dim=cfg.head_dim, block_size=case.block_size, max_blocks_per_seq=case.max_blocks_per_seq,
+                      num_blocks=case.k_cache.shape[0], max_ctx_len=int(case.lens.max()), num_flows=2, split_len=0,
+                      scale=cfg.scale, q_dtype=dfa.DFA_BF16, kv_dtype=dfa.DFA_BF16)
+    aws = torch.empty(max(dfa.dfa_decode_attn_workspace_size(ad) // 4, 4), device="cuda")
+    o1 = torch.empty((cfg.batch, cfg.num_q_heads, cfg.head_dim), device="cuda")
+    o2 = torch.empty_like(o1)
+    q2, a = to_device(case.q2), to_device(case.a)
+
+    def prefill():
+        dfa.dfa_prefill(pd, t["q"], t["k"], t["v"], t["lens"], t["k_cache"], t["v_cache"], t["block_table"], o, stream)
+
+    def aux_step():
+        dfa.dfa_decode_attn(ad, last, q2, a, t["k_cache"], t["v_cache"], t["block_table"], t["lens"], aws, o1, o2,
+                            stream)
+
+    def timed(fn, steps, warmup):
+        for _ in range(warmup):
+            fn()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(steps):
+            fn()
+        end.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / steps
+
+    warmup = max(args.warmup, 5)
+    ms = timed(prefill, args.steps, warmup)
+    aux_ms = timed(aux_step, args.steps, warmup)
+    pairs = sum(int(n) * (int(n) + 1) // 2 for n in case.lens)  # (query, key) pairs per head
+    flops = 4.0 * cfg.head_dim * cfg.num_q_heads * pairs  # scores and weighted values, 2 flops per product
+    tflops = flops / (ms * 1e-3) / 1e12
+    tokens = int(case.lens.sum())
+    log(f"prefill {ms * 1e3:.1f} us for {tokens} prompt tokens: {tflops:.0f} TFLOP/s of causal attention "
+        f"({100 * tflops / 2500:.0f}% of the 2.5 PFLOP/s bf16 peak); the auxiliary flow's first step over the "
+        f"cache: {aux_ms * 1e3:.1f} us")
+    print(json.dumps({"metric": "primary-only prefill (causal attention + cache write): prompt tokens/s + TFLOP/s",
+                      "value": tokens / (ms * 1e-3), "unit": "prompt tokens/s", "n_gpus": 1, "steps": args.steps,
+                      "warmup": warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+                      "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+                      "config": {"workload": "prefill: 4 prompts of 4096 tokens, 32/8 heads of 128, causal, "
+                                             "16-position paged cache", "batch": cfg.batch, "prompt_len": lmax},
+                      "attention_tflops": tflops, "mfma_peak_tflops": 2500.0, "frac_of_peak": tflops / 2500.0,
+                      "flops_per_step": flops, "aux_first_step_us": aux_ms * 1e3}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="c2", choices=["c2", "c3", "c4", "c5", "head", "moe"],
+    ap.add_argument("--config", default="c2", choices=["c2", "c3", "c4", "c5", "head", "moe", "prefill"],
                     help="c2 (default): the attention workload the metric is quoted on; c5: a whole layer step; "
-                         "head: the dual output head and mixture sampling; moe: the MoE FFN with router replay")
+                         "head: the dual output head and mixture sampling; moe: the MoE FFN with router replay; "
+                         "prefill: the primary-only prefill and the first auxiliary step")
     ap.add_argument("--split", type=int, default=0, help="positions per split (0: library choice)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -395,6 +468,9 @@ def main():
         return
     if args.config == "moe":
         bench_moe(args)
+        return
+    if args.config == "prefill":
+        bench_prefill(args)
         return
     cfg = W.ATTN_CONFIGS[args.config]
     log(f"generating {cfg.name} inputs")

@@ -22,7 +22,7 @@ EXPORTS = ["dfa_decode_attn_split_len", "dfa_decode_attn_num_splits", "dfa_decod
            "dfa_dual_gemv_workspace_size", "dfa_dual_gemv", "dfa_pack_weight",
            "dfa_decode_layer_workspace_size", "dfa_decode_layer",
            "dfa_mixture_workspace_size", "dfa_mixture_sample",
-           "dfa_moe_routing_size", "dfa_moe_route", "dfa_moe_workspace_size", "dfa_moe_ffn",
+           "dfa_moe_routing_size", "dfa_moe_route", "dfa_moe_workspace_size", "dfa_moe_ffn", "dfa_prefill",
            "dfa_status_string", "dfa_last_error", "dfa_version", "dfa_stream_read", "dfa_stream_read_sink_bytes"]
 
 DFA_EPI_NONE, DFA_EPI_RESIDUAL, DFA_EPI_SWIGLU, DFA_EPI_RESIDUAL_COUPLED, DFA_EPI_KV_APPEND = range(5)
@@ -88,6 +88,14 @@ class MoeDesc(ctypes.Structure):
     _fields_ = [(f, ctypes.c_int32) for f in ("batch", "hidden", "mlp", "num_experts", "k1", "k2", "x_exact_bf16")]
 
 
+class PrefillDesc(ctypes.Structure):
+    """Mirror of dfa_prefill_desc."""
+
+    _fields_ = [(f, ctypes.c_int32) for f in ("batch", "num_q_heads", "num_kv_heads", "head_dim", "max_prompt_len",
+                                              "block_size", "max_blocks_per_seq", "num_blocks")] + \
+               [("scale", ctypes.c_float)]
+
+
 class KernelEvents(ctypes.Structure):
     """Mirror of dfa_kernel_events (hipEvent_t handles)."""
 
@@ -130,6 +138,7 @@ def lib() -> ctypes.CDLL:
             "dfa_moe_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(MoeDesc)]),
             "dfa_moe_ffn": (ctypes.c_int, [ctypes.POINTER(MoeDesc), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                            _P, ctypes.c_size_t, _P]),
+            "dfa_prefill": (ctypes.c_int, [ctypes.POINTER(PrefillDesc), _P, _P, _P, _P, _P, _P, _P, _P, _P]),
             "dfa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
             "dfa_last_error": (ctypes.c_char_p, []),
             "dfa_version": (ctypes.c_int32, []),
@@ -304,6 +313,11 @@ def dfa_moe_ffn(desc, w_gate, w_up, w_down, b, c, h1, h2, res1, res2, routing, o
     _check(lib().dfa_moe_ffn(ctypes.byref(desc), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(b), _ptr(c), _ptr(h1),
                              _ptr(h2), _ptr(res1), _ptr(res2), _ptr(routing), _ptr(out1), _ptr(out2), _ptr(workspace),
                              _nbytes(workspace), _stream(stream)))
+
+
+def dfa_prefill(desc, q, k, v, prompt_lens, k_cache, v_cache, block_table, o, stream=None):
+    _check(lib().dfa_prefill(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(prompt_lens), _ptr(k_cache),
+                             _ptr(v_cache), _ptr(block_table), _ptr(o), _stream(stream)))
 
 
 def dfa_stream_read(buf, sink, stream=None):

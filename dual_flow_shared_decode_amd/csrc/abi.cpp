@@ -735,6 +735,57 @@ dfa_status dfa_moe_ffn(const dfa_moe_desc* d, const uint16_t* w_gate, const uint
   }
 }
 
+dfa_status dfa_prefill(const dfa_prefill_desc* d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                       const int32_t* prompt_lens, void* k_cache, void* v_cache, const int32_t* block_table,
+                       float* o, void* stream) {
+  try {
+    if (!d) return fail(DFA_ERR_NULL, "desc is NULL");
+    if (d->batch < 1 || d->batch > 65535) return fail(DFA_ERR_SHAPE, "batch must be in [1, 65535]");
+    if (d->num_kv_heads < 1 || d->num_q_heads < 1 || d->num_q_heads % d->num_kv_heads != 0)
+      return fail(DFA_ERR_SHAPE, "num_q_heads must be a positive multiple of num_kv_heads");
+    const int group = d->num_q_heads / d->num_kv_heads;
+    if (!is_pow2(group) || group > 16)
+      return fail(DFA_ERR_UNSUPPORTED, "query heads per kv head must be 1, 2, 4, 8 or 16");
+    if (d->num_kv_heads > 65535) return fail(DFA_ERR_SHAPE, "num_kv_heads must be at most 65535");
+    if (d->head_dim != 64 && d->head_dim != 128) return fail(DFA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+    if (!is_pow2(d->block_size) || d->block_size < 16 || d->max_blocks_per_seq < 1 || d->num_blocks < 1)
+      return fail(DFA_ERR_SHAPE, "block_size a power of two >= 16; positive table sizes");
+    if (d->max_prompt_len < 1 || int64_t(d->max_prompt_len) > int64_t(d->max_blocks_per_seq) * d->block_size)
+      return fail(DFA_ERR_SHAPE, "max_prompt_len must be in [1, max_blocks_per_seq * block_size]");
+    if (!(d->scale > 0.f) || !std::isfinite(d->scale)) return fail(DFA_ERR_SHAPE, "scale must be positive and finite");
+    if (!q || !k || !v || !prompt_lens || !k_cache || !v_cache || !block_table || !o)
+      return fail(DFA_ERR_NULL, "every pointer is required");
+    const void* ptrs[] = {q, k, v, prompt_lens, k_cache, v_cache, block_table, o};
+    for (const void* x : ptrs)
+      if (!aligned16(x)) return fail(DFA_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
+    dfa::PrefillParams p{};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.lens = prompt_lens;
+    p.table = block_table;
+    p.k_cache = static_cast<uint16_t*>(k_cache);
+    p.v_cache = static_cast<uint16_t*>(v_cache);
+    p.o = o;
+    p.batch = d->batch;
+    p.hq = d->num_q_heads;
+    p.hkv = d->num_kv_heads;
+    p.lmax = d->max_prompt_len;
+    p.lmax_tiles = (d->max_prompt_len + 15) / 16;
+    p.g_log2 = log2i(group);
+    p.bs_log2 = log2i(d->block_size);
+    p.max_blocks = d->max_blocks_per_seq;
+    p.num_blocks = d->num_blocks;
+    p.blk_stride = int64_t(d->num_kv_heads) * d->block_size * d->head_dim;
+    p.qscale = d->scale * 1.4426950408889634f;
+    const hipError_t e = dfa::launch_prefill(p, d->head_dim, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(DFA_ERR_HIP, std::string("prefill launch: ") + hipGetErrorString(e));
+    return DFA_OK;
+  } catch (...) {
+    return fail(DFA_ERR_HIP, "unexpected host exception");
+  }
+}
+
 dfa_status dfa_pack_weight(const uint16_t* w, uint16_t* w_tiled, int32_t n, int32_t k, void* stream) {
   if (!w || !w_tiled) return fail(DFA_ERR_NULL, "w and w_tiled are required");
   if (n < 16 || n % 16 != 0 || k < 8 || k % 8 != 0) return fail(DFA_ERR_SHAPE, "n must be a multiple of 16, k of 8");

@@ -93,7 +93,26 @@ struct MoeCombineParams {
   int32_t batch, hidden, k1, k2;
 };
 
+// Primary-only prefill: the prompt's keys and values into the paged cache, then
+// causal self-attention. q [batch][lmax][hq][D], k, v [batch][lmax][hkv][D]
+// (bf16), o [batch][lmax][hq][D] (float32); cache layouts as the decode kernels'.
+struct PrefillParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* lens;   // [batch] prompt lengths (clamped to [0, lmax])
+  const int32_t* table;  // [batch][max_blocks] (entries clamped to [0, num_blocks))
+  uint16_t* k_cache;
+  uint16_t* v_cache;
+  float* o;
+  int32_t batch, hq, hkv, lmax, lmax_tiles, g_log2, bs_log2, max_blocks, num_blocks;
+  int64_t blk_stride;  // elements per physical block: hkv * block_size * D
+  float qscale;        // scale * log2(e)
+};
+
 // Launchers return the launch status (hipGetLastError after the launch).
+hipError_t launch_prefill(const PrefillParams& p, int head_dim, hipStream_t s);
+int prefill_rows_per_workgroup();
 hipError_t launch_gemv(const GemvParams& p, hipStream_t s);
 hipError_t launch_gemv_finalize(const GemvParams& p, hipStream_t s);
 hipError_t launch_pack_weight(const uint16_t* w, uint16_t* wt, int n, int k, hipStream_t s);

@@ -408,6 +408,44 @@ DFA_API dfa_status dfa_moe_ffn(const dfa_moe_desc* desc, const uint16_t* w_gate,
                                const float* h2, const float* res1, const float* res2, const void* routing,
                                float* out1, float* out2, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * --------------------------------------------------------- primary prefill
+ * Prefill of a batch of prompts by the primary flow alone ("Custos de
+ * Inferência vs. Treinamento": prefill costs what a standard Transformer's
+ * does, the auxiliary flow being skipped; "Arquitetura Central": only the
+ * primary flow writes the cache). Two launches on `stream`:
+ *  1. the prompts' keys and values go to positions [0, L_b) of each sequence
+ *     b in the paged cache (layouts above; other slots are left as they are);
+ *  2. causal self-attention, for every prompt b, position t < L_b, head h:
+ *       O[b,t,h] = sum_{u <= t} softmax_u(scale * <Q[b,t,h], K[b,u,g]>) V[b,u,g]
+ *     with g = h / (num_q_heads / num_kv_heads), keys and values read back
+ *     from the cache.
+ * The auxiliary flow joins at the last prompt position ("Dual-Flow
+ * Transformers: Decoupling the Primary Prefill Path from Additional Decode
+ * Computation"): that first auxiliary step is dfa_decode_attn with
+ * ctx_lens[b] = L_b, Q1 = the primary's queries at position L_b - 1 and Q2 the
+ * auxiliary flow's.
+ *  q:  bf16 [batch, max_prompt_len, num_q_heads, head_dim]
+ *  k, v: bf16 [batch, max_prompt_len, num_kv_heads, head_dim]
+ *  prompt_lens: int32 [batch], L_b in [0, max_prompt_len] (clamped there);
+ *      rows at positions >= L_b are never read
+ *  block_table: int32 [batch, max_blocks_per_seq] covering positions [0, L_b)
+ *      (entries clamped to [0, num_blocks))
+ *  o:  float32 [batch, max_prompt_len, num_q_heads, head_dim]; rows at
+ *      positions >= L_b are not written
+ * Supported: head_dim 64 or 128; 1, 2, 4, 8 or 16 query heads per kv head.
+ */
+typedef struct dfa_prefill_desc {
+  int32_t batch, num_q_heads, num_kv_heads, head_dim;
+  int32_t max_prompt_len;  /* row stride of q, k, v and o */
+  int32_t block_size, max_blocks_per_seq, num_blocks;
+  float scale;
+} dfa_prefill_desc;
+
+DFA_API dfa_status dfa_prefill(const dfa_prefill_desc* desc, const uint16_t* q, const uint16_t* k,
+                               const uint16_t* v, const int32_t* prompt_lens, void* k_cache, void* v_cache,
+                               const int32_t* block_table, float* o, void* stream);
+
 /* Short fixed description of a status code. Never NULL. */
 DFA_API const char* dfa_status_string(dfa_status status);
 

@@ -250,3 +250,36 @@ def test_moe_call_errors():
         assert ffn(**{name: FAKE + 4}) == "DFA_ERR_ALIGNMENT", name
     assert ffn() == "DFA_ERR_WORKSPACE"
     assert ffn(ws=None, nb=wb) == "DFA_ERR_WORKSPACE"
+
+
+def prefill_desc(**kw):
+    d = dict(batch=4, num_q_heads=32, num_kv_heads=8, head_dim=128, max_prompt_len=4096, block_size=16,
+             max_blocks_per_seq=257, num_blocks=1028, scale=1 / math.sqrt(128))
+    d.update(kw)
+    return dfa.PrefillDesc(**d)
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(batch=0), "DFA_ERR_SHAPE"), (dict(num_q_heads=30), "DFA_ERR_SHAPE"),
+    (dict(num_q_heads=24), "DFA_ERR_UNSUPPORTED"),  # 3 query heads per kv head
+    (dict(num_q_heads=256), "DFA_ERR_UNSUPPORTED"),  # 32 per kv head
+    (dict(head_dim=96), "DFA_ERR_UNSUPPORTED"), (dict(block_size=24), "DFA_ERR_SHAPE"),
+    (dict(max_prompt_len=0), "DFA_ERR_SHAPE"), (dict(max_prompt_len=257 * 16 + 1), "DFA_ERR_SHAPE"),
+    (dict(scale=0.0), "DFA_ERR_SHAPE"), (dict(scale=float("inf")), "DFA_ERR_SHAPE"),
+])
+def test_prefill_validation(change, status):
+    with pytest.raises(dfa.DfaError) as e:
+        _lib._check(_lib.lib().dfa_prefill(ctypes.byref(prefill_desc(**change)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                           FAKE, FAKE, None))
+    assert _lib.STATUS[e.value.status] == status
+
+
+def test_prefill_pointer_errors():
+    names = ["q", "k", "v", "lens", "kc", "vc", "table", "o"]
+    for i, name in enumerate(names):
+        for bad, status in ((None, "DFA_ERR_NULL"), (FAKE + 4, "DFA_ERR_ALIGNMENT")):
+            args = [FAKE] * 8
+            args[i] = bad
+            with pytest.raises(dfa.DfaError) as e:
+                _lib._check(_lib.lib().dfa_prefill(ctypes.byref(prefill_desc()), *args, None))
+            assert _lib.STATUS[e.value.status] == status, name

@@ -753,6 +753,8 @@ dfa_status dfa_prefill(const dfa_prefill_desc* d, const uint16_t* q, const uint1
     if (d->max_prompt_len < 1 || int64_t(d->max_prompt_len) > int64_t(d->max_blocks_per_seq) * d->block_size)
       return fail(DFA_ERR_SHAPE, "max_prompt_len must be in [1, max_blocks_per_seq * block_size]");
     if (!(d->scale > 0.f) || !std::isfinite(d->scale)) return fail(DFA_ERR_SHAPE, "scale must be positive and finite");
+    if ((d->max_prompt_len + d->block_size - 1) / d->block_size > dfa::kPrefillMaxBlocks)
+      return fail(DFA_ERR_UNSUPPORTED, "a prompt may span at most 2048 cache blocks");
     if (!q || !k || !v || !prompt_lens || !k_cache || !v_cache || !block_table || !o)
       return fail(DFA_ERR_NULL, "every pointer is required");
     const void* ptrs[] = {q, k, v, prompt_lens, k_cache, v_cache, block_table, o};

@@ -27,8 +27,9 @@
 //           query rows as given (exact bf16; the scale multiplies the fp32
 //           scores), one product per 32 dimensions;
 //   output  O^T[dim][row] += V^T . P^T, A = values from LDS (positions 4*grp..
-//           of both tiles), B = the weights, split hi/lo (about 16 significant
-//           bits per product), whose score layout is already the operand's.
+//           of both tiles), B = the weights, split hi/lo (hi: the top 16 bits,
+//           lo: the rest rounded to bf16; about 16 significant bits per
+//           product), whose score layout is already the operand's.
 // Online softmax in base 2 with each row's own lazy rescale; query blocks run
 // longest first (the last block of a prompt attends the most positions).
 #include <hip/hip_runtime.h>
@@ -51,12 +52,25 @@ constexpr int kPfThreads = 64 * kPfWaves;
 constexpr int kPfCb = 2;                            // 16-row column blocks per wave
 constexpr int kPfRows = kPfWaves * kPfCb * 16;      // query rows per workgroup
 constexpr float kPfLazy = 8.f;                      // a row's max lags its scores by at most 2^8
+constexpr int kPfTable = kPrefillMaxBlocks;         // block-table entries staged in LDS
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return min(max(x, lo), hi); }
+
+// Max over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four k-groups of an MFMA
+// column). A register swapped with itself by v_permlane16_swap (odd 16-lane
+// rows against even ones) or v_permlane32_swap (upper 32 lanes against lower)
+// leaves each lane its own value and its partner's in the two results; these
+// are VALU operations, no trip through LDS.
+__device__ __forceinline__ float max_over_groups(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
 
 // Physical block of position t of prompt b (clamped into the cache).
 __device__ __forceinline__ int block_of(const PrefillParams& p, int b, int t) {
@@ -120,10 +134,39 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillParams 
   constexpr int DB = D / 16;                 // 16-dimension blocks of the output
   constexpr int kTile = 16 * D;              // elements of one 16-position tile
   constexpr int kPieces = kTile * 2 / 16;    // 16-byte pieces of one tile
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][4][kTile];  // [buffer][K tile 0, K tile 1, V tile 0, V tile 1]
+  // LDS, double-buffered: keys as in the cache ([D/8][16][8] per tile); values
+  // regrouped per tile as [4 position groups][D (+4 padding)][4 positions], so
+  // the 16 lanes of an operand read phase (dimensions 16*db .. +15, one
+  // position group) take 128 contiguous bytes (the cache's [D][16] order puts
+  // dimensions 32 bytes apart: a 4-way bank conflict), and the padding keeps
+  // the staging writes of the two halves of a cache row on different banks.
+  // The two tiles of a chunk lie a multiple of 512 bytes apart, so one
+  // ds_read2st64_b64 fetches a lane's 8 bytes of both into adjacent registers
+  // (the MFMA operand) with no moves.
+  constexpr int kVRow = D + 4;                                 // dimension rows of one position group
+  constexpr int kVTile = ((4 * kVRow * 4 * 2 + 511) / 512) * 512 / 2;  // elements per regrouped tile (padded)
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][2][kTile];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][2][kVTile];
+  __shared__ int tbl[kPfTable];  // the block-table entries of positions [0, q_end)
 
-  const int b = blockIdx.z, g = blockIdx.y;
-  const int qb = gridDim.x - 1 - blockIdx.x;  // longest blocks first
+  // Workgroup -> (prompt, kv head, query block). Workgroups go to the 8 XCDs in
+  // turn (linear index mod 8); with a multiple of 8 (prompt, kv head) pairs,
+  // all query blocks of a pair run on one XCD, longest first, so the
+  // workgroups resident there stream the same keys and values at the same
+  // pace and the XCD's L2 serves them.
+  const int nqb = gridDim.x, pairs = gridDim.y * gridDim.z;
+  const int lin = blockIdx.x + nqb * (blockIdx.y + gridDim.y * blockIdx.z);
+  int pair, rank;
+  if ((pairs & 7) == 0) {
+    const int j = lin >> 3;
+    pair = (lin & 7) + 8 * (j / nqb);
+    rank = j % nqb;
+  } else {
+    pair = lin / nqb;
+    rank = lin % nqb;
+  }
+  const int b = pair / p.hkv, g = pair - b * p.hkv;
+  const int qb = nqb - 1 - rank;  // longest blocks first
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, grp = lane >> 4;
   const int gl2 = p.g_log2;
@@ -150,33 +193,52 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillParams 
       qf[cb][st] = live ? v : bf16x8{};
     }
   }
-  // the last position any row of this wave attends
-  const int wave_last = min(p0 + ((((wave + 1) * kPfCb * 16) - 1) >> gl2), q_end - 1);
+  // the positions of this wave's first row and the last position any of its
+  // rows attends (-1: every row of the wave lies past the prompt)
+  const int wave_first = p0 + ((wave * kPfCb * 16) >> gl2);
+  const int wave_last = wave_first < q_end ? min(p0 + ((((wave + 1) * kPfCb * 16) - 1) >> gl2), q_end - 1) : -1;
 
   // ---- chunk staging: 4 tiles of kPieces 16-byte pieces, one piece per thread and tile ----
   const int bs = 1 << p.bs_log2;
   const size_t head_off = (size_t)g * bs * D;
   const int last_tile = (q_end - 1) & ~15;  // tiles past it fall back onto it (their positions are masked)
+  const int nblk = (last_tile >> p.bs_log2) + 1;  // at most kPfTable (checked on the host)
+  for (int i = threadIdx.x; i < nblk; i += kPfThreads) tbl[i] = block_of(p, b, i << p.bs_log2);
   auto tile_of = [&](int tt) __attribute__((always_inline)) {
-    return (size_t)block_of(p, b, tt) * p.blk_stride + head_off + (size_t)((tt & (bs - 1)) >> 4) * kTile;
+    return (size_t)tbl[tt >> p.bs_log2] * p.blk_stride + head_off + (size_t)((tt & (bs - 1)) >> 4) * kTile;
   };
-  u32x4 sk0, sk1, sv0, sv1;  // this thread's 16-byte piece of each tile of the next chunk
-  auto fetch = [&](int c) __attribute__((always_inline)) {
+  // Every thread issues the same loads on every path (threads past a tile's
+  // pieces read its last piece again), so the compiler's count of loads in
+  // flight is exact and a store to LDS waits only for its own chunk.
+  const int piece = min((int)threadIdx.x, kPieces - 1);
+  // this thread's 16-byte piece of each tile of a chunk; two sets alternate so
+  // that the loads of chunk c + 2 are in flight while chunk c is multiplied
+  struct Stage {
+    u32x4 k0, k1, v0, v1;
+  };
+  Stage sa, sb;
+  auto fetch = [&](int c, Stage& st) __attribute__((always_inline)) {
+    c = min(c, nch - 1);  // past the end: the last chunk again (never used); keeps the load count fixed
     const size_t t0 = tile_of(min(32 * c, last_tile)), t1 = tile_of(min(32 * c + 16, last_tile));
-    if (threadIdx.x < kPieces) {
-      // plain loads: every query block of the prompt reads these tiles again, so they stay in L2
-      sk0 = *((const u32x4*)(p.k_cache + t0) + threadIdx.x);
-      sk1 = *((const u32x4*)(p.k_cache + t1) + threadIdx.x);
-      sv0 = *((const u32x4*)(p.v_cache + t0) + threadIdx.x);
-      sv1 = *((const u32x4*)(p.v_cache + t1) + threadIdx.x);
-    }
+    // plain loads: every query block of the prompt reads these tiles again, so they stay in L2
+    st.k0 = *((const u32x4*)(p.k_cache + t0) + piece);
+    st.k1 = *((const u32x4*)(p.k_cache + t1) + piece);
+    st.v0 = *((const u32x4*)(p.v_cache + t0) + piece);
+    st.v1 = *((const u32x4*)(p.v_cache + t1) + piece);
   };
-  auto put = [&](int buf) __attribute__((always_inline)) {
+  auto put = [&](int buf, const Stage& st) __attribute__((always_inline)) {
     if (threadIdx.x < kPieces) {
-      *((u32x4*)&lds[buf][0][0] + threadIdx.x) = sk0;
-      *((u32x4*)&lds[buf][1][0] + threadIdx.x) = sk1;
-      *((u32x4*)&lds[buf][2][0] + threadIdx.x) = sv0;
-      *((u32x4*)&lds[buf][3][0] + threadIdx.x) = sv1;
+      *((u32x4*)&k_lds[buf][0][0] + threadIdx.x) = st.k0;
+      *((u32x4*)&k_lds[buf][1][0] + threadIdx.x) = st.k1;
+      // value piece = cache row d = piece / 2, positions 8 * (piece % 2) .. +7:
+      // position groups 2 * (piece % 2) and 2 * (piece % 2) + 1
+      const int d = threadIdx.x >> 1, g0 = 2 * (threadIdx.x & 1);
+      uint16_t* v0 = &v_lds[buf][0][0];
+      uint16_t* v1 = &v_lds[buf][1][0];
+      *(u32x2*)(v0 + (g0 * kVRow + d) * 4) = u32x2{st.v0[0], st.v0[1]};
+      *(u32x2*)(v0 + ((g0 + 1) * kVRow + d) * 4) = u32x2{st.v0[2], st.v0[3]};
+      *(u32x2*)(v1 + (g0 * kVRow + d) * 4) = u32x2{st.v1[0], st.v1[1]};
+      *(u32x2*)(v1 + ((g0 + 1) * kVRow + d) * 4) = u32x2{st.v1[2], st.v1[3]};
     }
   };
 
@@ -190,16 +252,11 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillParams 
     for (int db = 0; db < DB; ++db) oacc[cb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  fetch(0);
-  put(0);
-  __syncthreads();
-  for (int c = 0; c < nch; ++c) {
-    const int buf = c & 1;
-    if (c + 1 < nch) fetch(c + 1);  // in flight while this chunk is multiplied
+  auto chunk = [&](int c, int buf) __attribute__((always_inline)) {
     const int t0 = 32 * c;
     if (t0 <= wave_last) {  // wave-uniform: some row of this wave sees a position of the chunk
-      const uint16_t* kt = &lds[buf][0][0];
-      const uint16_t* vt = &lds[buf][2][0];
+      const uint16_t* kt = &k_lds[buf][0][0];
+      const uint16_t* vt = &v_lds[buf][0][0];
       // scores of both tiles for both column blocks
       f32x4 sv[2][kPfCb];
 #pragma unroll
@@ -216,32 +273,30 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillParams 
           sv[u][cb] = acc;
         }
       }
-      // values of this lane: dimension 16*db + n, positions 4*grp .. +3 of both tiles;
-      // positions past the block's last one are zeroed (their cache slots may be unwritten)
-      uint32_t keep[2][2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int tv = t0 + 16 * u + 4 * grp + 2 * h;
-          keep[u][h] = (tv < q_end ? 0x0000FFFFu : 0u) | (tv + 1 < q_end ? 0xFFFF0000u : 0u);
-        }
-      bf16x8 pa[kPfCb], pb[kPfCb];
+      // wave-uniform: only chunks that reach past a row's position need the
+      // causal mask, and only the last chunk holds positions past the block
+      const bool diag = t0 + 31 > wave_first;
+      const bool tail = t0 + 32 > q_end;
+      u32x4 pa[kPfCb];
+      bf16x8 pb[kPfCb];
 #pragma unroll
       for (int cb = 0; cb < kPfCb; ++cb) {
-        float sc[8];
+        float sc[8];  // raw scores q.k; the scale enters with the exponent
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int t = t0 + 16 * u + 4 * grp + i;
-            sc[4 * u + i] = t <= pos_r[cb] ? sv[u][cb][i] * p.qscale : -INFINITY;  // causal
-          }
+          for (int i = 0; i < 4; ++i) sc[4 * u + i] = sv[u][cb][i];
+        if (diag) {
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (t0 + 16 * u + 4 * grp + i > pos_r[cb]) sc[4 * u + i] = -INFINITY;  // causal
+        }
         float cmax = sc[0];
 #pragma unroll
         for (int j = 1; j < 8; ++j) cmax = fmaxf(cmax, sc[j]);
-        cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-        cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+        cmax = max_over_groups(cmax) * p.qscale;  // base-2 units (qscale > 0)
         const bool moves = cmax > m_run[cb] + kPfLazy;  // this row's own decision
         if (__builtin_amdgcn_ballot_w64(moves) != 0) {
           const float m_new = moves ? cmax : m_run[cb];
@@ -251,35 +306,65 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillParams 
           for (int db = 0; db < DB; ++db) oacc[cb][db] *= alpha;
           m_run[cb] = m_new;
         }
+        // weights x = 2^(scale*log2(e)*s - m), split x = hi + lo: hi = x truncated to
+        // its top 16 bits (packed in pairs by one byte permute), lo = bf16(x - hi)
+        const float neg_m = -m_run[cb];
         float psum = 0.f;
+        uint32_t xb[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const float x = __builtin_amdgcn_exp2f(sc[j] - m_run[cb]);
+          const float x = __builtin_amdgcn_exp2f(fmaf(sc[j], p.qscale, neg_m));
           psum += x;
-          const __bf16 hi = (__bf16)x;
-          pa[cb][j] = hi;
-          pb[cb][j] = (__bf16)(x - (float)hi);
+          xb[j] = __float_as_uint(x);
+          pb[cb][j] = (__bf16)(x - __uint_as_float(xb[j] & 0xFFFF0000u));
         }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pa[cb][j] = __builtin_amdgcn_perm(xb[2 * j + 1], xb[2 * j], 0x07060302u);
         l_run[cb] += psum;
       }
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const u32x2 w0 = *(const u32x2*)(vt + ((16 * db + n) * 16 + 4 * grp));
-        const u32x2 w1 = *(const u32x2*)(vt + kTile + ((16 * db + n) * 16 + 4 * grp));
+        const u32x2 w0 = *(const u32x2*)(vt + (grp * kVRow + 16 * db + n) * 4);
+        const u32x2 w1 = *(const u32x2*)(vt + kVTile + (grp * kVRow + 16 * db + n) * 4);
         u32x4 vw;
-        vw[0] = w0[0] & keep[0][0];
-        vw[1] = w0[1] & keep[0][1];
-        vw[2] = w1[0] & keep[1][0];
-        vw[3] = w1[1] & keep[1][1];
+        vw[0] = w0[0];
+        vw[1] = w0[1];
+        vw[2] = w1[0];
+        vw[3] = w1[1];
+        if (tail) {  // positions past the block are zeroed (their cache slots may be unwritten)
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            const int tv = t0 + 16 * (h >> 1) + 4 * grp + 2 * (h & 1);
+            vw[h] &= (tv < q_end ? 0x0000FFFFu : 0u) | (tv + 1 < q_end ? 0xFFFF0000u : 0u);
+          }
+        }
         const bf16x8 va = __builtin_bit_cast(bf16x8, vw);
 #pragma unroll
         for (int cb = 0; cb < kPfCb; ++cb) {
-          oacc[cb][db] = mfma(va, pa[cb], oacc[cb][db]);
+          oacc[cb][db] = mfma(va, __builtin_bit_cast(bf16x8, pa[cb]), oacc[cb][db]);
           oacc[cb][db] = mfma(va, pb[cb], oacc[cb][db]);
         }
       }
     }
-    if (c + 1 < nch) put(buf ^ 1);
+  };
+
+  __syncthreads();  // the table slice
+  fetch(0, sa);
+  fetch(1, sb);
+  put(0, sa);
+  __syncthreads();
+  // iteration c multiplies chunk c from LDS buffer c & 1, fetches chunk c + 2
+  // into the register set chunk c came from, and moves chunk c + 1 (fetched a
+  // whole iteration earlier) into the other LDS buffer
+  for (int c = 0; c < nch; c += 2) {
+    fetch(c + 2, sa);
+    chunk(c, 0);
+    put(1, sb);
+    __syncthreads();
+    if (c + 1 >= nch) break;
+    fetch(c + 3, sb);
+    chunk(c + 1, 1);
+    put(0, sa);
     __syncthreads();
   }
 

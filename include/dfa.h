@@ -433,7 +433,8 @@ DFA_API dfa_status dfa_moe_ffn(const dfa_moe_desc* desc, const uint16_t* w_gate,
  *      (entries clamped to [0, num_blocks))
  *  o:  float32 [batch, max_prompt_len, num_q_heads, head_dim]; rows at
  *      positions >= L_b are not written
- * Supported: head_dim 64 or 128; 1, 2, 4, 8 or 16 query heads per kv head.
+ * Supported: head_dim 64 or 128; 1, 2, 4, 8 or 16 query heads per kv head;
+ * ceil(max_prompt_len / block_size) <= 2048 (the table slice is staged on chip).
  */
 typedef struct dfa_prefill_desc {
   int32_t batch, num_q_heads, num_kv_heads, head_dim;

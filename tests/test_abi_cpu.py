@@ -266,6 +266,7 @@ def prefill_desc(**kw):
     (dict(head_dim=96), "DFA_ERR_UNSUPPORTED"), (dict(block_size=24), "DFA_ERR_SHAPE"),
     (dict(max_prompt_len=0), "DFA_ERR_SHAPE"), (dict(max_prompt_len=257 * 16 + 1), "DFA_ERR_SHAPE"),
     (dict(scale=0.0), "DFA_ERR_SHAPE"), (dict(scale=float("inf")), "DFA_ERR_SHAPE"),
+    (dict(max_prompt_len=2048 * 16 + 16, max_blocks_per_seq=4096), "DFA_ERR_UNSUPPORTED"),  # over 2048 blocks
 ])
 def test_prefill_validation(change, status):
     with pytest.raises(dfa.DfaError) as e:

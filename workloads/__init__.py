@@ -41,7 +41,7 @@ _TAG = {"q1": 1, "q2": 2, "a": 3, "k": 4, "v": 5, "peak": 6, "len": 7, "perm": 8
         "x1": 11, "x2": 12, "wq": 13, "wk": 14, "wv": 15, "wo": 16, "wg": 17,
         "wu": 18, "wd": 19, "b": 20, "c": 21, "l1": 22, "l2": 23, "u": 24, "lpeak": 25, "wlm": 26,
         "h1": 27, "h2": 28, "mh1": 29, "mh2": 30, "mg": 31, "mu": 32, "md": 33, "mr": 34, "mb": 35, "mc": 36,
-        "mres1": 37, "mres2": 38, "pq": 39, "pk": 40, "pv": 41, "pq2": 42, "pa": 43}
+        "mres1": 37, "mres2": 38, "pq": 39, "pk": 40, "pv": 41, "pq2": 42, "pa": 43, "na": 44, "nm": 45}
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -126,7 +126,7 @@ C3 = AttnConfig("c3", batch=64, num_q_heads=64, num_kv_heads=8, head_dim=128, dt
 C4 = AttnConfig("c4", batch=4, num_q_heads=32, num_kv_heads=8, head_dim=128, dtype="bf16",
                 ctx_lens=(131072,) * 4, peaky_fraction=0.01, peaky_factor=8.0)
 ATTN_CONFIGS = {"c1": C1, "c2": C2, "c3": C3, "c4": C4}
-SEEDS = {"c1": 1001, "c2": 1002, "c3": 1003, "c4": 1004, "c5": 1005, "head": 1006, "mix": 1007, "moe": 1008, "prefill": 1009}
+SEEDS = {"c1": 1001, "c2": 1002, "c3": 1003, "c4": 1004, "c5": 1005, "head": 1006, "mix": 1007, "moe": 1008, "prefill": 1009, "stack": 1010}
 
 
 def draw_ctx_lens(cfg: AttnConfig, seed: int) -> np.ndarray:
@@ -543,3 +543,88 @@ def make_prefill_case(cfg: PrefillConfig, seed: int) -> PrefillCase:
     k_cache, v_cache = empty_cache(layout, cfg.num_kv_heads, cfg.head_dim, "bf16")
     return PrefillCase(cfg, q, k, v, lens, q2, a, k_cache, v_cache, layout.block_table, layout.block_size,
                        layout.max_blocks_per_seq)
+
+
+# --------------------------------------------------------------------------
+# Layer stacks (one decode step through several layers)
+# --------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class StackConfig:
+    """`layers` dual-flow layers of shape `layer`, optional pre-norm RMSNorm and rotary embeddings."""
+
+    name: str
+    layer: LayerConfig
+    layers: int
+    rope: str = "half"        # "none", "half" or "interleaved"
+    rms: bool = True
+    eps: float = 1e-5
+    norm_std: float = 0.1     # RMSNorm weights ~ 1 + N(0, norm_std)
+    rope_base: float = 10000.0
+
+    def replace(self, **kw) -> "StackConfig":
+        return dataclasses.replace(self, **kw)
+
+
+# Four C5-shaped layers (batch 32, hidden 4096, 32/8 heads of 128, SwiGLU 14336, 4096 cached positions
+# per layer) with RMSNorm and rotate-half rotary embeddings.
+STACK = StackConfig("stack", C5, layers=4)
+
+
+def rope_tables(max_pos: int, head_dim: int, base: float = 10000.0):
+    """The conventional rotary angle tables (model configuration, like the weights): angle
+    p * base^(-2i / head_dim) for position p and pair i; float32 cos, sin [max_pos, head_dim / 2]."""
+    inv = np.power(float(base), -np.arange(0, head_dim, 2, dtype=np.float64) / head_dim)
+    ang = np.arange(max_pos, dtype=np.float64)[:, None] * inv[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+@dataclass
+class StackCase:
+    cfg: StackConfig
+    x1: np.ndarray
+    x2: np.ndarray
+    layers: list           # per layer: dict of wq, wk, wv, wo, wg, wu, wd (bf16 bits), a, b, c, n_attn, n_mlp
+    k_caches: list
+    v_caches: list
+    block_table: np.ndarray
+    ctx_lens: np.ndarray
+    block_size: int
+    max_blocks_per_seq: int
+    cos: np.ndarray        # float32 [max_pos, D/2]
+    sin: np.ndarray
+
+
+def make_stack_case(cfg: StackConfig, seed: int, pad_nan: bool = True) -> StackCase:
+    """All layers share the cache layout, positions and inputs of make_layer_case(cfg.layer, seed); layer
+    l draws its weights, couplings, norms and cached keys/values from seed + 7919 * l (so layer 0 is
+    exactly that layer case)."""
+    lc = cfg.layer
+    lens = np.full(lc.batch, lc.ctx, dtype=np.int32)
+    layout = plan_cache(lc.batch, lens, lc.block_size, lc.capacity, lc.shuffle_blocks, seed, extra_slots=1)
+    x1 = bf16_bits_to_f32(f32_to_bf16_bits(_normal(seed, "x1", (), (lc.batch, lc.hidden), lc.x_std)))
+    x2 = bf16_bits_to_f32(f32_to_bf16_bits(_normal(seed, "x2", (), (lc.batch, lc.hidden), lc.x_std)))
+    layers, kcs, vcs = [], [], []
+    for li in range(cfg.layers):
+        sl = seed + 7919 * li
+        w = {name: f32_to_bf16_bits(_normal(sl, name, (), shape, lc.w_std)) for name, shape in weight_shapes(lc).items()}
+        w.update(a=_normal(sl, "a", (), (lc.num_q_heads * lc.head_dim,), lc.coupling_std),
+                 b=_normal(sl, "b", (), (lc.mlp,), lc.coupling_std),
+                 c=_normal(sl, "c", (), (lc.hidden,), lc.coupling_std),
+                 n_attn=1.0 + _normal(sl, "na", (), (lc.hidden,), cfg.norm_std),
+                 n_mlp=1.0 + _normal(sl, "nm", (), (lc.hidden,), cfg.norm_std))
+        k_cache, v_cache = empty_cache(layout, lc.num_kv_heads, lc.head_dim, "bf16")
+        if not pad_nan:
+            k_cache[...] = 0
+            v_cache[...] = 0
+        for bi in range(lc.batch):
+            for g in range(lc.num_kv_heads):
+                kr, vr = kv_rows(sl, bi, g, lc.ctx, lc.head_dim, "bf16", lc.kv_std)
+                store_rows(k_cache, v_cache, layout, bi, g, kr, vr)
+        layers.append(w)
+        kcs.append(k_cache)
+        vcs.append(v_cache)
+    max_pos = layout.max_blocks_per_seq * layout.block_size
+    cos, sin = rope_tables(max_pos, lc.head_dim, cfg.rope_base)
+    return StackCase(cfg, x1, x2, layers, kcs, vcs, layout.block_table, lens, layout.block_size,
+                     layout.max_blocks_per_seq, cos, sin)

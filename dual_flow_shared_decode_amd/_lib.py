@@ -20,12 +20,14 @@ STATUS = {0: "DFA_OK", 1: "DFA_ERR_NULL", 2: "DFA_ERR_SHAPE", 3: "DFA_ERR_DTYPE"
 EXPORTS = ["dfa_decode_attn_split_len", "dfa_decode_attn_num_splits", "dfa_decode_attn_workspace_size",
            "dfa_decode_attn", "dfa_decode_attn_timed", "dfa_decode_attn_partials", "dfa_combine",
            "dfa_dual_gemv_workspace_size", "dfa_dual_gemv", "dfa_pack_weight",
-           "dfa_decode_layer_workspace_size", "dfa_decode_layer",
+           "dfa_decode_layer_workspace_size", "dfa_decode_layer", "dfa_decode_stack_workspace_size",
+           "dfa_decode_stack",
            "dfa_mixture_workspace_size", "dfa_mixture_sample",
            "dfa_moe_routing_size", "dfa_moe_route", "dfa_moe_workspace_size", "dfa_moe_ffn", "dfa_prefill",
            "dfa_status_string", "dfa_last_error", "dfa_version", "dfa_stream_read", "dfa_stream_read_sink_bytes"]
 
 DFA_EPI_NONE, DFA_EPI_RESIDUAL, DFA_EPI_SWIGLU, DFA_EPI_RESIDUAL_COUPLED, DFA_EPI_KV_APPEND = range(5)
+DFA_ROPE_NONE, DFA_ROPE_HALF, DFA_ROPE_INTERLEAVED = range(3)
 
 
 class DfaError(RuntimeError):
@@ -74,6 +76,20 @@ class LayerWeights(ctypes.Structure):
     """Mirror of dfa_layer_weights."""
 
     _fields_ = [(f, ctypes.c_void_p) for f in ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down", "a", "b", "c")]
+
+
+class StackDesc(ctypes.Structure):
+    """Mirror of dfa_stack_desc."""
+
+    _fields_ = [("layer", LayerDesc), ("num_layers", ctypes.c_int32), ("rope", ctypes.c_int32),
+                ("rope_max_pos", ctypes.c_int32), ("rms_norm", ctypes.c_int32), ("rms_eps", ctypes.c_float)]
+
+
+class StackLayer(ctypes.Structure):
+    """Mirror of dfa_stack_layer."""
+
+    _fields_ = [("w", LayerWeights), ("norm_attn", ctypes.c_void_p), ("norm_mlp", ctypes.c_void_p),
+                ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p)]
 
 
 class MixtureDesc(ctypes.Structure):
@@ -139,6 +155,9 @@ def lib() -> ctypes.CDLL:
             "dfa_moe_ffn": (ctypes.c_int, [ctypes.POINTER(MoeDesc), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                            _P, ctypes.c_size_t, _P]),
             "dfa_prefill": (ctypes.c_int, [ctypes.POINTER(PrefillDesc), _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+            "dfa_decode_stack_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(StackDesc)]),
+            "dfa_decode_stack": (ctypes.c_int, [ctypes.POINTER(StackDesc), ctypes.POINTER(StackLayer), _P, _P, _P, _P,
+                                                _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
             "dfa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
             "dfa_last_error": (ctypes.c_char_p, []),
             "dfa_version": (ctypes.c_int32, []),
@@ -318,6 +337,30 @@ def dfa_moe_ffn(desc, w_gate, w_up, w_down, b, c, h1, h2, res1, res2, routing, o
 def dfa_prefill(desc, q, k, v, prompt_lens, k_cache, v_cache, block_table, o, stream=None):
     _check(lib().dfa_prefill(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(prompt_lens), _ptr(k_cache),
                              _ptr(v_cache), _ptr(block_table), _ptr(o), _stream(stream)))
+
+
+def dfa_decode_stack_workspace_size(desc: StackDesc) -> int:
+    return int(lib().dfa_decode_stack_workspace_size(ctypes.byref(desc)))
+
+
+def stack_layers(entries):
+    """A dfa_stack_layer array from (layer_weights(...), norm_attn, norm_mlp, k_cache, v_cache) tuples (tensors
+    or None); the array keeps the tensors alive."""
+    arr = (StackLayer * len(entries))()
+    keep = []
+    for i, (w, na, nm, kc, vc) in enumerate(entries):
+        arr[i] = StackLayer(w, _ptr(na), _ptr(nm), _ptr(kc), _ptr(vc))
+        keep.append((w, na, nm, kc, vc))
+    arr._tensors = keep
+    return arr
+
+
+def dfa_decode_stack(desc, layers, rope_cos, rope_sin, x1, x2, block_table, ctx_lens, out1, out2, workspace,
+                     stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().dfa_decode_stack(ctypes.byref(desc), layers, _ptr(rope_cos), _ptr(rope_sin), _ptr(x1), _ptr(x2),
+                                  _ptr(block_table), _ptr(ctx_lens), _ptr(out1), _ptr(out2), _ptr(workspace),
+                                  ws_bytes, _stream(stream)))
 
 
 def dfa_stream_read(buf, sink, stream=None):

@@ -361,9 +361,23 @@ GemvPlan plan_qkv(const dfa_gemv_desc& d) {
   return pl;
 }
 
+// Options of a layer step beyond the plain layer: pre-norm RMSNorm (norm
+// weights and a buffer for the normalised rows of both flows) and rotary
+// embeddings of the queries and keys.
+struct LayerExtras {
+  const float* norm_attn = nullptr;
+  const float* norm_mlp = nullptr;
+  float* norm_buf = nullptr;  // 2 * batch * hidden floats
+  float eps = 0.f;
+  int32_t rope = dfa::kRopeNone;
+  const float* rope_cos = nullptr;
+  const float* rope_sin = nullptr;
+  int32_t rope_max_pos = 0;
+};
+
 dfa_status qkv_impl(const dfa_layer_desc* d, const GemvPlan& pl, const dfa_layer_weights* w, const float* x1,
-                    const float* x2, float* q1, float* q2, const dfa_kv_target& kv, void* workspace,
-                    hipStream_t hs) {
+                    const float* x2, bool x_exact, const LayerExtras& ex, float* q1, float* q2,
+                    const dfa_kv_target& kv, void* workspace, hipStream_t hs) {
   const int32_t qd = d->num_q_heads * d->head_dim, kd = d->num_kv_heads * d->head_dim;
   dfa::GemvParams p{};
   p.w = w->wq;
@@ -387,8 +401,12 @@ dfa_status qkv_impl(const dfa_layer_desc* d, const GemvPlan& pl, const dfa_layer
   p.k_split = pl.k_split;
   p.k_range = pl.k_range;
   p.pair = 0;
-  p.x_exact = d->x_exact_bf16 != 0;
+  p.x_exact = x_exact;
   p.epilogue = dfa::kEpiQkv;
+  p.rope = ex.rope;
+  p.rope_cos = ex.rope_cos;
+  p.rope_sin = ex.rope_sin;
+  p.rope_max_pos = ex.rope_max_pos;
   p.rows_per_wg = pl.rows_per_wg;
   p.kv_k = static_cast<uint16_t*>(kv.k_cache);
   p.kv_v = static_cast<uint16_t*>(kv.v_cache);
@@ -469,22 +487,15 @@ size_t dfa_decode_layer_workspace_size(const dfa_layer_desc* desc) {
   return plan_layer(desc, &lp) == DFA_OK ? lp.total : 0;
 }
 
-dfa_status dfa_decode_layer(const dfa_layer_desc* d, const dfa_layer_weights* w, const float* x1, const float* x2,
-                            void* k_cache, void* v_cache, const int32_t* block_table, const int32_t* ctx_lens,
-                            float* out1, float* out2, void* workspace, size_t ws_bytes, void* stream) {
-  try {
-    LayerPlan lp;
-    dfa_status st = plan_layer(d, &lp);
-    if (st != DFA_OK) return st;
-    if (!w || !w->wq || !w->wk || !w->wv || !w->wo || !w->w_gate || !w->w_up || !w->w_down || !w->a)
-      return fail(DFA_ERR_NULL, "every weight matrix and the coupling vector a are required");
-    if (!x1 || !x2 || !out1 || !out2 || !k_cache || !v_cache || !block_table || !ctx_lens)
-      return fail(DFA_ERR_NULL, "x1, x2, out1, out2, the caches, block_table and ctx_lens are required");
-    if (!workspace) return fail(DFA_ERR_WORKSPACE, "workspace is required");
-    if (!aligned16(workspace)) return fail(DFA_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
-    if (ws_bytes < lp.total) return fail(DFA_ERR_WORKSPACE, "workspace smaller than dfa_decode_layer_workspace_size()");
-    hipStream_t hs = static_cast<hipStream_t>(stream);
-    char* ws = static_cast<char*>(workspace);
+namespace {
+// One layer step (the plan and arguments already validated), with the options of `ex`.
+// x_exact: x1 and x2 hold exact bf16 values (the caller's inputs of a first layer only).
+dfa_status layer_step(const dfa_layer_desc* d, const LayerPlan& lp, const dfa_layer_weights* w, const LayerExtras& ex,
+                      bool x_exact, const float* x1, const float* x2, void* k_cache, void* v_cache,
+                      const int32_t* block_table, const int32_t* ctx_lens, float* out1, float* out2, char* ws,
+                      hipStream_t hs) {
+  {
+    dfa_status st;
     const size_t B = size_t(d->batch);
     const size_t qd = size_t(d->num_q_heads) * d->head_dim;
     float* q1 = reinterpret_cast<float*>(ws + lp.off_q);
@@ -498,11 +509,24 @@ dfa_status dfa_decode_layer(const dfa_layer_desc* d, const dfa_layer_weights* w,
     void* aws = ws + lp.off_attn;
     void* gws = ws + lp.off_gemv;
     const size_t aws_bytes = lp.off_gemv - lp.off_attn, gws_bytes = lp.total - lp.off_gemv;
+    // pre-norm of both flows (shared weights) into ex.norm_buf
+    auto rmsnorm = [&](const float* a, const float* b, const float* wn, const float** n1, const float** n2) {
+      dfa::NormParams np{a, b, wn, ex.norm_buf, ex.norm_buf + B * d->hidden, d->batch, d->hidden, ex.eps};
+      const hipError_t e = dfa::launch_rmsnorm(np, hs);
+      if (e != hipSuccess) return fail(DFA_ERR_HIP, std::string("rmsnorm launch: ") + hipGetErrorString(e));
+      *n1 = np.y1;
+      *n2 = np.y2;
+      return DFA_OK;
+    };
+    const float* a1 = x1;
+    const float* a2 = x2;
+    if (ex.norm_attn && (st = rmsnorm(x1, x2, ex.norm_attn, &a1, &a2)) != DFA_OK) return st;
     // 1-2. both flows' queries (aux query from its own embedding input x2) and the primary's
-    // keys and values, appended at position ctx_lens[b]; the auxiliary flow writes no KV
+    // keys and values (rotated when ex.rope is set), appended at position ctx_lens[b]; the
+    // auxiliary flow writes no KV
     const dfa_kv_target kv{k_cache, v_cache, block_table, ctx_lens, d->num_kv_heads, d->head_dim, d->block_size,
                            d->max_blocks_per_seq, d->num_blocks};
-    st = qkv_impl(d, lp.qkv_plan, w, x1, x2, q1, q2, kv, gws, hs);
+    st = qkv_impl(d, lp.qkv_plan, w, a1, a2, x_exact && !ex.norm_attn, ex, q1, q2, kv, gws, hs);
     if (st != DFA_OK) return st;
     // 3. both flows attend the primary cache, now ctx_lens[b] + 1 positions; q2 coupled by a
     st = attn_impl(&lp.attn, q1, q2, w->a, k_cache, v_cache, block_table, ctx_lens, 1, aws, aws_bytes, o1, o2, hs,
@@ -511,12 +535,126 @@ dfa_status dfa_decode_layer(const dfa_layer_desc* d, const dfa_layer_weights* w,
     // 4. output projection + residual
     st = gemv_impl(&lp.o, w->wo, nullptr, o1, o2, nullptr, x1, x2, h1, h2, nullptr, gws, gws_bytes, hs);
     if (st != DFA_OK) return st;
-    // 5. SwiGLU, MLP-intermediate coupling b
-    st = gemv_impl(&lp.mlp_in, w->w_gate, w->w_up, h1, h2, w->b, nullptr, nullptr, z1, z2, nullptr, gws, gws_bytes,
+    // 5. SwiGLU (on the pre-normed rows when ex.norm_mlp is set), MLP-intermediate coupling b
+    const float* m1 = h1;
+    const float* m2 = h2;
+    if (ex.norm_mlp && (st = rmsnorm(h1, h2, ex.norm_mlp, &m1, &m2)) != DFA_OK) return st;
+    st = gemv_impl(&lp.mlp_in, w->w_gate, w->w_up, m1, m2, w->b, nullptr, nullptr, z1, z2, nullptr, gws, gws_bytes,
                    hs);
     if (st != DFA_OK) return st;
     // 6. down projection, MLP-output coupling c, residual
     return gemv_impl(&lp.mlp_out, w->w_down, nullptr, z1, z2, w->c, h1, h2, out1, out2, nullptr, gws, gws_bytes, hs);
+  }
+}
+
+dfa_status check_layer_weights(const dfa_layer_weights* w) {
+  if (!w || !w->wq || !w->wk || !w->wv || !w->wo || !w->w_gate || !w->w_up || !w->w_down || !w->a)
+    return fail(DFA_ERR_NULL, "every weight matrix and the coupling vector a are required");
+  const void* ptrs[] = {w->wq, w->wk, w->wv, w->wo, w->w_gate, w->w_up, w->w_down, w->a, w->b, w->c};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return fail(DFA_ERR_ALIGNMENT, "weights and couplings must be 16-byte aligned");
+  return DFA_OK;
+}
+}  // namespace
+
+dfa_status dfa_decode_layer(const dfa_layer_desc* d, const dfa_layer_weights* w, const float* x1, const float* x2,
+                            void* k_cache, void* v_cache, const int32_t* block_table, const int32_t* ctx_lens,
+                            float* out1, float* out2, void* workspace, size_t ws_bytes, void* stream) {
+  try {
+    LayerPlan lp;
+    dfa_status st = plan_layer(d, &lp);
+    if (st != DFA_OK) return st;
+    if ((st = check_layer_weights(w)) != DFA_OK) return st;
+    if (!x1 || !x2 || !out1 || !out2 || !k_cache || !v_cache || !block_table || !ctx_lens)
+      return fail(DFA_ERR_NULL, "x1, x2, out1, out2, the caches, block_table and ctx_lens are required");
+    if (!workspace) return fail(DFA_ERR_WORKSPACE, "workspace is required");
+    if (!aligned16(workspace)) return fail(DFA_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
+    if (ws_bytes < lp.total) return fail(DFA_ERR_WORKSPACE, "workspace smaller than dfa_decode_layer_workspace_size()");
+    return layer_step(d, lp, w, LayerExtras{}, d->x_exact_bf16 != 0, x1, x2, k_cache, v_cache, block_table,
+                      ctx_lens, out1, out2, static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
+  } catch (...) {
+    return fail(DFA_ERR_HIP, "unexpected host exception");
+  }
+}
+
+namespace {
+struct StackPlan {
+  LayerPlan lp;
+  size_t off_norm, off_act, act_bytes, total;
+};
+
+dfa_status plan_stack(const dfa_stack_desc* d, StackPlan* sp) {
+  if (!d) return fail(DFA_ERR_NULL, "desc is NULL");
+  dfa_status st = plan_layer(&d->layer, &sp->lp);
+  if (st != DFA_OK) return st;
+  if (d->num_layers < 1 || d->num_layers > 4096) return fail(DFA_ERR_SHAPE, "num_layers must be in [1, 4096]");
+  if (d->rope != DFA_ROPE_NONE && d->rope != DFA_ROPE_HALF && d->rope != DFA_ROPE_INTERLEAVED)
+    return fail(DFA_ERR_SHAPE, "rope must be DFA_ROPE_NONE, DFA_ROPE_HALF or DFA_ROPE_INTERLEAVED");
+  if (d->rope != DFA_ROPE_NONE && d->rope_max_pos < d->layer.max_ctx_len)
+    return fail(DFA_ERR_SHAPE, "rope_max_pos must cover every position (>= max_ctx_len)");
+  if (d->rms_norm != 0 && d->rms_norm != 1) return fail(DFA_ERR_SHAPE, "rms_norm must be 0 or 1");
+  if (d->rms_norm && (!(d->rms_eps >= 0.f) || !std::isfinite(d->rms_eps)))
+    return fail(DFA_ERR_SHAPE, "rms_eps must be finite and >= 0");
+  const size_t act = align256(2 * size_t(d->layer.batch) * d->layer.hidden * sizeof(float));
+  sp->off_norm = sp->lp.total;
+  sp->off_act = sp->off_norm + act;
+  sp->act_bytes = act;
+  sp->total = sp->off_act + 2 * act;
+  return DFA_OK;
+}
+}  // namespace
+
+size_t dfa_decode_stack_workspace_size(const dfa_stack_desc* desc) {
+  StackPlan sp;
+  return plan_stack(desc, &sp) == DFA_OK ? sp.total : 0;
+}
+
+dfa_status dfa_decode_stack(const dfa_stack_desc* d, const dfa_stack_layer* layers, const float* rope_cos,
+                            const float* rope_sin, const float* x1, const float* x2, const int32_t* block_table,
+                            const int32_t* ctx_lens, float* out1, float* out2, void* workspace, size_t ws_bytes,
+                            void* stream) {
+  try {
+    StackPlan sp;
+    dfa_status st = plan_stack(d, &sp);
+    if (st != DFA_OK) return st;
+    if (!layers) return fail(DFA_ERR_NULL, "layers is NULL");
+    if (!x1 || !x2 || !out1 || !out2 || !block_table || !ctx_lens)
+      return fail(DFA_ERR_NULL, "x1, x2, out1, out2, block_table and ctx_lens are required");
+    if (d->rope != DFA_ROPE_NONE && (!rope_cos || !rope_sin)) return fail(DFA_ERR_NULL, "rotary tables are required");
+    for (int32_t l = 0; l < d->num_layers; ++l) {
+      if ((st = check_layer_weights(&layers[l].w)) != DFA_OK) return st;
+      if (!layers[l].k_cache || !layers[l].v_cache) return fail(DFA_ERR_NULL, "every layer needs its caches");
+      if (d->rms_norm && (!layers[l].norm_attn || !layers[l].norm_mlp))
+        return fail(DFA_ERR_NULL, "every layer needs its norm weights");
+    }
+    if (!workspace || ws_bytes < sp.total) return fail(DFA_ERR_WORKSPACE, "workspace smaller than dfa_decode_stack_workspace_size()");
+    if (!aligned16(workspace)) return fail(DFA_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
+    char* ws = static_cast<char*>(workspace);
+    const size_t bh = size_t(d->layer.batch) * d->layer.hidden;
+    float* act[2] = {reinterpret_cast<float*>(ws + sp.off_act), reinterpret_cast<float*>(ws + sp.off_act + sp.act_bytes)};
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    for (int32_t l = 0; l < d->num_layers; ++l) {
+      LayerExtras ex;
+      if (d->rms_norm) {
+        ex.norm_attn = layers[l].norm_attn;
+        ex.norm_mlp = layers[l].norm_mlp;
+        ex.norm_buf = reinterpret_cast<float*>(ws + sp.off_norm);
+        ex.eps = d->rms_eps;
+      }
+      ex.rope = d->rope;
+      ex.rope_cos = rope_cos;
+      ex.rope_sin = rope_sin;
+      ex.rope_max_pos = d->rope_max_pos;
+      const float* in1 = l == 0 ? x1 : act[(l - 1) & 1];
+      const float* in2 = l == 0 ? x2 : act[(l - 1) & 1] + bh;
+      float* o1 = l == d->num_layers - 1 ? out1 : act[l & 1];
+      float* o2 = l == d->num_layers - 1 ? out2 : act[l & 1] + bh;
+      // only the caller's inputs can be exact bf16; later layers read float32 outputs
+      st = layer_step(&d->layer, sp.lp, &layers[l].w, ex, l == 0 && d->layer.x_exact_bf16 != 0, in1, in2,
+                      layers[l].k_cache, layers[l].v_cache, block_table, ctx_lens, o1, o2, ws, hs);
+      if (st != DFA_OK) return st;
+    }
+    return DFA_OK;
   } catch (...) {
     return fail(DFA_ERR_HIP, "unexpected host exception");
   }

@@ -518,16 +518,65 @@ __global__ __launch_bounds__(kFinalizeThreads) void gemv_finalize_kernel(GemvPar
 #pragma unroll
       for (int j = 0; j < 4; ++j) y[f][mat][j] = 0.f;
   if (p.epilogue == kEpiQkv) {
-    if (n0 < p.q_cols) {  // both flows' queries
+    // Both flows' queries (columns [0, q_cols)) and the primary's keys with
+    // their values (the next kv_cols, then kv_cols more), rotated at position
+    // ctx_lens[s] when rope is set. Rotate-half pairs dimension d < D/2 of a
+    // head with d + D/2: the thread of the first half takes both.
+    const int D = p.kv_head_dim, half = D >> 1;
+    const bool in_q = n0 < p.q_cols, in_k = !in_q && n0 < p.q_cols + p.kv_cols;
+    if (!in_q && !in_k) return;  // value columns: written with their keys
+    const int col = in_q ? n0 : n0 - p.q_cols;
+    const int d0 = col % D;
+    if (p.rope == kRopeHalf && d0 >= half) return;
+    const int pos = p.rope == kRopeNone ? 0 : min(max(p.kv_ctx[s], 0), p.rope_max_pos - 1);
+    const float* cs = p.rope_cos + (size_t)pos * half;
+    const float* sn = p.rope_sin + (size_t)pos * half;
+    auto rot_pairs = [&](float (&v)[4]) __attribute__((always_inline)) {  // interleaved: (d, d + 1)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float c = cs[(d0 >> 1) + j], sv = sn[(d0 >> 1) + j], a = v[2 * j], b = v[2 * j + 1];
+        v[2 * j] = a * c - b * sv;
+        v[2 * j + 1] = a * sv + b * c;
+      }
+    };
+    auto rot_halves = [&](float (&lo)[4], float (&hi)[4]) __attribute__((always_inline)) {  // (d, d + D/2)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float c = cs[d0 + j], sv = sn[d0 + j], a = lo[j], b = hi[j];
+        lo[j] = a * c - b * sv;
+        hi[j] = a * sv + b * c;
+      }
+    };
+    float u[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};  // the second halves (rotate-half)
+    if (in_q) {
       sum_splits<KS>(p, 1, 0, (size_t)s, n0, y[0][0]);
       sum_splits<KS>(p, 1, 0, (size_t)(p.cbf * 16 + s), n0, y[1][0]);
       const size_t o = (size_t)s * p.q_cols + n0;
+      if (p.rope == kRopeHalf) {
+        sum_splits<KS>(p, 1, 0, (size_t)s, n0 + half, u[0]);
+        sum_splits<KS>(p, 1, 0, (size_t)(p.cbf * 16 + s), n0 + half, u[1]);
+        rot_halves(y[0][0], u[0]);
+        rot_halves(y[1][0], u[1]);
+        store4(p.y1 + o + half, u[0]);
+        store4(p.y2 + o + half, u[1]);
+      } else if (p.rope == kRopeInterleaved) {
+        rot_pairs(y[0][0]);
+        rot_pairs(y[1][0]);
+      }
       store4(p.y1 + o, y[0][0]);
       store4(p.y2 + o, y[1][0]);
-    } else if (n0 < p.q_cols + p.kv_cols) {  // the primary's key and value of the same kv columns
+    } else {
       sum_splits<KS>(p, 1, 0, (size_t)s, n0, y[0][0]);
       sum_splits<KS>(p, 1, 0, (size_t)s, n0 + p.kv_cols, y[0][1]);
-      kv_append(p, s, n0 - p.q_cols, y[0][0], y[0][1]);
+      if (p.rope == kRopeHalf) {
+        sum_splits<KS>(p, 1, 0, (size_t)s, n0 + half, u[0]);
+        sum_splits<KS>(p, 1, 0, (size_t)s, n0 + p.kv_cols + half, u[1]);
+        rot_halves(y[0][0], u[0]);
+        kv_append(p, s, col + half, u[0], u[1]);
+      } else if (p.rope == kRopeInterleaved) {
+        rot_pairs(y[0][0]);
+      }
+      kv_append(p, s, col, y[0][0], y[0][1]);
     }
     return;
   }

@@ -42,6 +42,12 @@ struct GemvParams {
   const int32_t* moe_sel;
   int64_t moe_wstride;
   int32_t moe_k1, moe_k2, moe_experts, moe_rgs, moe_row_s, moe_row_slot, moe_row_f;
+  // kEpiQkv: rotary embedding of both flows' queries and the primary's keys at
+  // position ctx_lens[s] (kRopeNone, kRopeHalf: pairs (i, i + D/2) of a head,
+  // kRopeInterleaved: pairs (2i, 2i + 1)); tables [rope_max_pos][D/2], D = kv_head_dim.
+  const float* rope_cos;
+  const float* rope_sin;
+  int32_t rope, rope_max_pos;
   uint16_t* kv_k;      // KV append target
   uint16_t* kv_v;
   const int32_t* kv_table;
@@ -110,7 +116,21 @@ struct PrefillParams {
   float qscale;        // scale * log2(e)
 };
 
+enum : int32_t { kRopeNone = 0, kRopeHalf = 1, kRopeInterleaved = 2 };
+
+// RMSNorm of rows of both flows: y_f = x_f / sqrt(mean(x_f^2) + eps) * w.
+struct NormParams {
+  const float* x1;
+  const float* x2;
+  const float* w;  // [n]
+  float* y1;
+  float* y2;
+  int32_t rows, n;
+  float eps;
+};
+
 // Launchers return the launch status (hipGetLastError after the launch).
+hipError_t launch_rmsnorm(const NormParams& p, hipStream_t s);
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, hipStream_t s);
 int prefill_rows_per_workgroup();
 constexpr int kPrefillMaxBlocks = 2048;  // cache blocks one prompt may span (staged in LDS)

@@ -306,6 +306,57 @@ DFA_API dfa_status dfa_decode_layer(const dfa_layer_desc* desc, const dfa_layer_
                                     float* out2, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * ------------------------------------------------------------- layer stack
+ * One decode step through num_layers dual-flow layers of the shape `layer`
+ * (the layer of dfa_decode_layer, "Arquitetura Central", "Mecanismos Chave"),
+ * each flow's output feeding the next layer, with the LLaMA-like options the
+ * pages do not name (this library's choices):
+ *  - rms_norm = 1: pre-norm RMSNorm before the attention block and before the
+ *    MLP block, y = x / sqrt(mean(x^2) + rms_eps) * w, one weight vector per
+ *    block and layer, shared by both flows; the residuals add the un-normed x
+ *    and h;
+ *  - rope: rotary embeddings of both flows' queries and of the primary's key
+ *    at position ctx_lens[b] (before the query coupling and the cache
+ *    append): dimension pairs of each head, (i, i + head_dim/2) for
+ *    DFA_ROPE_HALF or (2i, 2i + 1) for DFA_ROPE_INTERLEAVED, rotated
+ *    (x, y) -> (x cos - y sin, x sin + y cos) by the caller's tables
+ *    rope_cos, rope_sin: float32 [rope_max_pos, head_dim / 2] (row p: the
+ *    angles of position p; positions are clamped to rope_max_pos - 1).
+ * Every layer appends the primary's key and value at ctx_lens[b] of its own
+ * cache (all layers share block_table and ctx_lens); the caller advances
+ * ctx_lens afterwards. layer.x_exact_bf16 describes x1 and x2 (the first
+ * layer's input) only. With rope = DFA_ROPE_NONE and rms_norm = 0 each layer
+ * is exactly dfa_decode_layer. The step allocates nothing and issues only
+ * kernel launches, so it can be captured in a HIP graph.
+ */
+typedef enum dfa_rope { DFA_ROPE_NONE = 0, DFA_ROPE_HALF = 1, DFA_ROPE_INTERLEAVED = 2 } dfa_rope;
+
+typedef struct dfa_stack_desc {
+  dfa_layer_desc layer;  /* shape of every layer (as dfa_decode_layer) */
+  int32_t num_layers;    /* 1..4096 */
+  int32_t rope;          /* dfa_rope */
+  int32_t rope_max_pos;  /* rows of the rotary tables (>= layer.max_ctx_len when rope is set) */
+  int32_t rms_norm;      /* 0 or 1 */
+  float rms_eps;         /* >= 0 */
+} dfa_stack_desc;
+
+typedef struct dfa_stack_layer {
+  dfa_layer_weights w;     /* as dfa_decode_layer */
+  const float* norm_attn;  /* [hidden] (rms_norm) */
+  const float* norm_mlp;   /* [hidden] (rms_norm) */
+  void* k_cache;           /* this layer's cache (layout of dfa_decode_attn) */
+  void* v_cache;
+} dfa_stack_layer;
+
+DFA_API size_t dfa_decode_stack_workspace_size(const dfa_stack_desc* desc);
+
+/* layers: host array [num_layers]; x1, x2, out1, out2: float32 [batch, hidden]. */
+DFA_API dfa_status dfa_decode_stack(const dfa_stack_desc* desc, const dfa_stack_layer* layers, const float* rope_cos,
+                                    const float* rope_sin, const float* x1, const float* x2,
+                                    const int32_t* block_table, const int32_t* ctx_lens, float* out1, float* out2,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * ------------------------------------------------------ mixture decoding
  * Next token from the mixture of the two flows' distributions ("Mecanismos
  * Chave", mixture objective): with p_f = softmax(logits_f) over the vocabulary,

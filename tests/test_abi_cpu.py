@@ -284,3 +284,19 @@ def test_prefill_pointer_errors():
             with pytest.raises(dfa.DfaError) as e:
                 _lib._check(_lib.lib().dfa_prefill(ctypes.byref(prefill_desc()), *args, None))
             assert _lib.STATUS[e.value.status] == status, name
+
+
+def test_stack_validation():
+    layer = dfa.LayerDesc(batch=4, hidden=256, num_q_heads=4, num_kv_heads=2, head_dim=64, mlp=256, block_size=16,
+                          max_blocks_per_seq=4, num_blocks=16, max_ctx_len=64, scale=0.125, x_exact_bf16=1)
+    ok = dict(layer=layer, num_layers=2, rope=dfa.DFA_ROPE_HALF, rope_max_pos=64, rms_norm=1, rms_eps=1e-5)
+    assert dfa.dfa_decode_stack_workspace_size(dfa.StackDesc(**ok)) == \
+        dfa.dfa_decode_layer_workspace_size(layer) + 3 * 2 * 4 * 256 * 4
+    for bad in (dict(num_layers=0), dict(rope=3), dict(rope_max_pos=63), dict(rms_norm=2), dict(rms_eps=-1.0)):
+        assert dfa.dfa_decode_stack_workspace_size(dfa.StackDesc(**dict(ok, **bad))) == 0, bad
+    # no rotary tables with rope set
+    arr = (dfa.StackLayer * 2)()
+    with pytest.raises(dfa.DfaError) as e:
+        _lib._check(_lib.lib().dfa_decode_stack(ctypes.byref(dfa.StackDesc(**ok)), arr, None, None, FAKE, FAKE, FAKE,
+                                                FAKE, FAKE, FAKE, FAKE, 1 << 30, None))
+    assert _lib.STATUS[e.value.status] == "DFA_ERR_NULL"

@@ -20,7 +20,7 @@ of the split kernel against the 8 TB/s peak, the measured stream-read ceiling,
 the auxiliary flow's increment over a one-flow run of the same kernel, and the
 CPU oracle's rate on a bounded sample (context only).
 
-    python bench.py [--steps K] [--warmup W] [--config c2|c3|c4|c5|head|moe|prefill]
+    python bench.py [--steps K] [--warmup W] [--config c2|c3|c4|c5|head|moe|prefill|stack]
 """
 import argparse
 import hashlib
@@ -430,15 +430,107 @@ def bench_prefill(args):
                       "flops_per_step": flops, "aux_first_step_us": aux_ms * 1e3}), flush=True)
 
 
+def bench_stack(args):
+    """One token through 4 dual-flow layers of the c5 shape (batch 32, hidden 4096, 32/8 heads of 128, SwiGLU
+    14336, 4096 cached positions) with RMSNorm and rotate-half rotary embeddings (dfa_decode_stack), launched
+    eagerly and replayed from a HIP graph that holds the whole step. The layers hold equal values in
+    separate buffers (one layer's draw copied): every layer reads its own 436 MB of weights and its own
+    cache, as a deeper model would."""
+    import torch
+
+    import dual_flow_shared_decode_amd as dfa
+    import workloads as W
+    from workloads.device import to_device
+
+    cfg = W.STACK
+    lc = cfg.layer
+    log(f"generating stack inputs ({cfg.layers} layers)")
+    sc = W.make_stack_case(cfg.replace(layers=1), W.SEEDS["stack"], pad_nan=False)
+    w0 = sc.layers[0]
+    packed = {}
+    for name in ("wq", "wk", "wv", "wo", "wg", "wu", "wd"):
+        dev = to_device(w0[name])
+        packed[name] = torch.empty_like(dev)
+        dfa.dfa_pack_weight(dev, packed[name], w0[name].shape[0], w0[name].shape[1])
+        del dev
+    vecs = {name: to_device(w0[name].astype("float32")) for name in ("a", "b", "c", "n_attn", "n_mlp")}
+    k0, v0 = to_device(sc.k_caches[0]), to_device(sc.v_caches[0])
+    entries = []
+    for li in range(cfg.layers):
+        p = packed if li == 0 else {k: t.clone() for k, t in packed.items()}
+        vv = vecs if li == 0 else {k: t.clone() for k, t in vecs.items()}
+        lw = dfa.layer_weights(p["wq"], p["wk"], p["wv"], p["wo"], p["wg"], p["wu"], p["wd"], vv["a"], vv["b"], vv["c"])
+        entries.append((lw, vv["n_attn"], vv["n_mlp"], k0.clone(), v0.clone()))
+    del k0, v0
+    layers = dfa.stack_layers(entries)
+    desc = dfa.StackDesc(layer=dfa.LayerDesc(batch=lc.batch, hidden=lc.hidden, num_q_heads=lc.num_q_heads,
+                                             num_kv_heads=lc.num_kv_heads, head_dim=lc.head_dim, mlp=lc.mlp,
+                                             block_size=sc.block_size, max_blocks_per_seq=sc.max_blocks_per_seq,
+                                             num_blocks=sc.k_caches[0].shape[0], max_ctx_len=lc.ctx + 1,
+                                             scale=lc.scale, x_exact_bf16=1),
+                         num_layers=cfg.layers, rope=dfa.DFA_ROPE_HALF, rope_max_pos=sc.cos.shape[0], rms_norm=1,
+                         rms_eps=cfg.eps)
+    cos, sin = to_device(sc.cos), to_device(sc.sin)
+    x1, x2 = to_device(sc.x1), to_device(sc.x2)
+    table, ctx = to_device(sc.block_table), to_device(sc.ctx_lens)
+    ws = torch.empty(dfa.dfa_decode_stack_workspace_size(desc) // 4 + 64, device="cuda")
+    out1 = torch.empty_like(x1)
+    out2 = torch.empty_like(x2)
+
+    def step():  # every step appends at the same position (the same values each time)
+        dfa.dfa_decode_stack(desc, layers, cos, sin, x1, x2, table, ctx, out1, out2, ws)
+
+    def timed(fn, steps):
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(steps):
+            fn()
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / steps
+
+    warmup = max(args.warmup, 50)
+    for _ in range(warmup):
+        step()
+    ms = timed(step, args.steps)
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(10):
+        graph.replay()
+    ms_graph = timed(graph.replay, args.steps)
+    nbytes = cfg.layers * layer_bytes(lc)
+    gbps = nbytes / (ms_graph * 1e-3) / 1e9
+    log(f"stack of {cfg.layers} layers: {ms * 1e3:.1f} us per token eager, {ms_graph * 1e3:.1f} us replayed from a "
+        f"graph ({ms_graph * 1e3 / cfg.layers:.1f} us per layer, {gbps:.0f} GB/s over {nbytes / 1e6:.0f} MB)")
+    print(json.dumps({"metric": "dual-flow decode step through a layer stack: tokens/s (both flows) + HBM GB/s",
+                      "value": 2 * lc.batch / (ms_graph * 1e-3), "unit": "tokens/s (both flows)", "n_gpus": 1,
+                      "steps": args.steps, "warmup": warmup, "ms_per_step": ms_graph, "higher_is_better": True,
+                      "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+                      "config": {"workload": f"stack: {cfg.layers} dual-flow layers of the c5 shape with RMSNorm and "
+                                             "rotate-half rotary embeddings, batch 32, one token, HIP graph",
+                                 "batch": lc.batch, "layers": cfg.layers},
+                      "ms_per_step_eager": ms, "achieved_gbps": gbps, "hbm_peak_gbps": HBM_PEAK_GBPS,
+                      "frac_of_peak": gbps / HBM_PEAK_GBPS, "algorithmic_bytes_per_step": nbytes}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="c2", choices=["c2", "c3", "c4", "c5", "head", "moe", "prefill"],
+    ap.add_argument("--config", default="c2", choices=["c2", "c3", "c4", "c5", "head", "moe", "prefill", "stack"],
                     help="c2 (default): the attention workload the metric is quoted on; c5: a whole layer step; "
                          "head: the dual output head and mixture sampling; moe: the MoE FFN with router replay; "
-                         "prefill: the primary-only prefill and the first auxiliary step")
+                         "prefill: the primary-only prefill and the first auxiliary step; stack: 4 layers with RMSNorm "
+                         "and rotary embeddings in a HIP graph")
     ap.add_argument("--split", type=int, default=0, help="positions per split (0: library choice)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -471,6 +563,9 @@ def main():
         return
     if args.config == "prefill":
         bench_prefill(args)
+        return
+    if args.config == "stack":
+        bench_stack(args)
         return
     cfg = W.ATTN_CONFIGS[args.config]
     log(f"generating {cfg.name} inputs")

@@ -132,7 +132,6 @@ struct NormParams {
 // Launchers return the launch status (hipGetLastError after the launch).
 hipError_t launch_rmsnorm(const NormParams& p, hipStream_t s);
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, hipStream_t s);
-int prefill_rows_per_workgroup();
 constexpr int kPrefillMaxBlocks = 2048;  // cache blocks one prompt may span (staged in LDS)
 hipError_t launch_gemv(const GemvParams& p, hipStream_t s);
 hipError_t launch_gemv_finalize(const GemvParams& p, hipStream_t s);

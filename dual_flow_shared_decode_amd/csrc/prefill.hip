@@ -402,6 +402,5 @@ hipError_t launch_prefill(const PrefillParams& p, int head_dim, hipStream_t stre
   return hipGetLastError();
 }
 
-int prefill_rows_per_workgroup() { return kPfRows; }
 
 }  // namespace dfa

@@ -109,6 +109,7 @@ SMALL = {
     "equal_fanout": W.MoeConfig("eq", batch=12, hidden=256, mlp=128, experts=8, k1=3, k2=3, w_std=0.05),
     "all_experts": W.MoeConfig("all", batch=32, hidden=128, mlp=128, experts=4, k1=2, k2=4, w_std=0.05),
     "one_expert": W.MoeConfig("one", batch=9, hidden=256, mlp=256, experts=1, k1=1, k2=1, w_std=0.05),
+    "max_fanout": W.MoeConfig("wide", batch=3, hidden=128, mlp=128, experts=40, k1=1, k2=32, w_std=0.05),
 }
 
 

@@ -73,6 +73,8 @@ CASES = {
                                block_size=64), 54),
     "g2_d128": (W.PrefillConfig("g2", batch=1, num_q_heads=4, num_kv_heads=2, head_dim=128, lens=(300,),
                                 shuffle_blocks=False), 55),
+    "g4_d64": (W.PrefillConfig("g4d64", batch=2, num_q_heads=16, num_kv_heads=4, head_dim=64, lens=(161, 2),
+                               block_size=32), 57),
 }
 
 

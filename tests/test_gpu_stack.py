@@ -90,7 +90,7 @@ def oracle(sc):
 
 
 CASES = [("half", True, SMALL, 3), ("interleaved", True, SMALL, 3), ("half", False, SMALL, 2),
-         ("none", True, SMALL, 2), ("half", True, WIDE, 2)]
+         ("none", True, SMALL, 2), ("half", True, WIDE, 2), ("interleaved", False, WIDE, 2)]
 
 
 @pytest.mark.parametrize("rope,rms,layer,layers", CASES,

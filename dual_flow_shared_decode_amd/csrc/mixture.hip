@@ -4,8 +4,10 @@
 // from the primary's collision probability, the primary keeping at least half
 // of the weight). This library's reading of alpha: (1 + sum_v p1(v)^2) / 2.
 //
-// Three launches per call, on the flows' float32 logits [batch, vocab], the
-// vocabulary cut into chunks of kMixChunk tokens:
+// Vocabularies of at most kMixFusedMaxVocab tokens take one launch,
+// mix_fused_kernel, one workgroup per sequence holding the sequence's logits
+// in registers. Larger ones take three launches on the flows' float32 logits
+// [batch, vocab], the vocabulary cut into chunks of kMixChunk tokens:
 //   mix_stats_kernel  workgroup = (chunk, sequence): each flow's largest logit
 //                     and sum of exponentials over the chunk, and the
 //                     primary's sum of squared exponentials;
@@ -20,7 +22,7 @@
 //                     chunks' maxima.
 // Masses are summed as integers: each token's p_mix (at most 1) is scaled by
 // 2^35 and truncated, so every sum is exact, in any order, and the search
-// meets the same sums at the chunk and at the token level. A token below
+// meets the same sums at every level (chunk or wave, row, token). A token below
 // 2^-35 of mass is never drawn. Exponentials are 2^((x - m) log2 e) on the
 // hardware unit, the difference taken before scaling so that it is exact near
 // the maximum however large the logits. Results do not depend on timing.
@@ -96,7 +98,8 @@ __device__ __forceinline__ uint64_t shfl_up_u64(uint64_t x, int d) {
 }
 
 // Exclusive prefix of x over the workgroup in thread order, and the total
-// (integers: exact). sh: kMixWaves words of LDS.
+// (integers: exact). sh: NW words of LDS.
+template <int NW>
 __device__ __forceinline__ uint64_t block_excl_scan(uint64_t x, uint64_t* sh, uint64_t& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint64_t incl = x;
@@ -111,7 +114,7 @@ __device__ __forceinline__ uint64_t block_excl_scan(uint64_t x, uint64_t* sh, ui
   uint64_t before = incl - x;
   total = 0;
 #pragma unroll
-  for (int w = 0; w < kMixWaves; ++w) {
+  for (int w = 0; w < NW; ++w) {
     if (w < wave) before += sh[w];
     total += sh[w];
   }
@@ -119,6 +122,7 @@ __device__ __forceinline__ uint64_t block_excl_scan(uint64_t x, uint64_t* sh, ui
 }
 
 // First maximum (largest value, smallest token on ties) over the workgroup.
+template <int NW>
 __device__ __forceinline__ void block_first_max(float& v, int& i, float* shv, int* shi) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
@@ -139,7 +143,7 @@ __device__ __forceinline__ void block_first_max(float& v, int& i, float* shv, in
   v = shv[0];
   i = shi[0];
 #pragma unroll
-  for (int w = 1; w < kMixWaves; ++w)
+  for (int w = 1; w < NW; ++w)
     if (shv[w] > v || (shv[w] == v && shi[w] < i)) {
       v = shv[w];
       i = shi[w];
@@ -240,8 +244,8 @@ __global__ __launch_bounds__(kMixThreads) void mix_chunk_kernel(MixParams p) {
     }
   }
   uint64_t total;
-  block_excl_scan(mass, shm, total);
-  block_first_max(bv, bi, shv, shi);
+  block_excl_scan<kMixWaves>(mass, shm, total);
+  block_first_max<kMixWaves>(bv, bi, shv, shi);
   if (threadIdx.x == 0) {
     uint32_t* r = p.crec + ((size_t)b * p.chunks + chunk) * 4;
     *(uint4*)r = make_uint4((uint32_t)total, (uint32_t)(total >> 32), __float_as_uint(bv), (uint32_t)bi);
@@ -269,7 +273,7 @@ __global__ __launch_bounds__(kMixThreads) void mix_pick_kernel(MixParams p) {
     bi = (int)r.w;
   }
   uint64_t total;
-  const uint64_t before = block_excl_scan(mass, shm, total);
+  const uint64_t before = block_excl_scan<kMixWaves>(mass, shm, total);
   const float u = fminf(fmaxf(p.u[b], 0.f), 0x1.fffffep-1f);  // clamped to [0, 1)
   uint64_t target = (uint64_t)((double)u * (double)total);
   if (target >= total) target = total - 1;  // total > 0: the largest p_mix is at least 1 / vocab
@@ -277,7 +281,7 @@ __global__ __launch_bounds__(kMixThreads) void mix_pick_kernel(MixParams p) {
     sel_chunk = t;
     sel_base = before;
   }
-  block_first_max(bv, bi, shv, shi);  // its barriers also publish sel_chunk and sel_base
+  block_first_max<kMixWaves>(bv, bi, shv, shi);  // its barriers also publish sel_chunk and sel_base
   // ---- token level inside the chosen chunk: the masses mix_chunk_kernel summed ----
   const float* l1 = p.logits1 + (size_t)b * p.vocab;
   const float* l2 = p.logits2 + (size_t)b * p.vocab;
@@ -298,7 +302,7 @@ __global__ __launch_bounds__(kMixThreads) void mix_pick_kernel(MixParams p) {
   const uint64_t local = target - sel_base;  // below the chunk's mass
   if (t == 0) sel_tok = min(sel_chunk * kMixChunk + kMixChunk, p.vocab) - 1;  // not reached: one thread claims
   uint64_t chunk_total;
-  uint64_t cum = block_excl_scan(run, shm, chunk_total);
+  uint64_t cum = block_excl_scan<kMixWaves>(run, shm, chunk_total);
   if (cum <= local && local < cum + run) {  // exactly one thread
     int tok = v0 + kRun - 1;
 #pragma unroll
@@ -318,9 +322,227 @@ __global__ __launch_bounds__(kMixThreads) void mix_pick_kernel(MixParams p) {
   }
 }
 
+namespace {
+constexpr int kFuseThreads = 1024;
+constexpr int kFuseWaves = kFuseThreads / 64;
+constexpr int kFuseRows = 8;  // float4 groups per lane and flow
+static_assert(kFuseWaves * 64 * kFuseRows * 4 == kMixFusedMaxVocab, "one token per register slot");
+
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)x, m), hi = __shfl_xor((uint32_t)(x >> 32), m);
+    x += ((uint64_t)hi << 32) | lo;
+  }
+  return x;
+}
+
+__device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint64_t o = shfl_up_u64(x, d);
+    if (lane >= d) x += o;
+  }
+  return x;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  return v;
+}
+}  // namespace
+
+// The whole mixture of one sequence in one workgroup, for vocabularies of at
+// most kMixFusedMaxVocab tokens: wave w holds tokens [2048 w, 2048 w + 2048)
+// of both flows in registers (lane l, row i: the four tokens of group
+// 64 i + l, so every load instruction reads 1 KB of consecutive logits). One
+// read of the logits gives the softmax statistics, alpha, p_mix, the greedy
+// token and the inverse-CDF token. The draw follows the token order from the
+// outside in: the wave whose tokens hold the target (wave totals, in wave
+// order), then the row of that wave (row totals, in row order), then the lane
+// (a scan over the row), then the token among the lane's four. The masses and
+// the rule are those of the chunked kernels: p_mix scaled by 2^35 and
+// truncated, target = floor(u total).
+__global__ __launch_bounds__(kFuseThreads) void mix_fused_kernel(MixParams p) {
+  __shared__ float shs[kFuseWaves][3];
+  __shared__ uint64_t shm[kFuseWaves];
+  __shared__ float shv[kFuseWaves];
+  __shared__ int shi[kFuseWaves];
+  __shared__ int sel_tok;
+  const int b = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const float* l1 = p.logits1 + (size_t)b * p.vocab;
+  const float* l2 = p.logits2 + (size_t)b * p.vocab;
+  const int g0 = wave * (64 * kFuseRows) + lane;  // group of row 0; row i adds 64 i
+  float4 x1[kFuseRows], x2[kFuseRows];
+#pragma unroll
+  for (int i = 0; i < kFuseRows; ++i) {
+    const int v = (g0 + 64 * i) * 4;
+    const bool in = v < p.vocab;  // the vocabulary is a multiple of 4: a group is all in or all out
+    x1[i] = in ? *(const float4*)(l1 + v) : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+    x2[i] = in ? *(const float4*)(l2 + v) : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+  }
+  // ---- softmax statistics: maxima, then sums in a fixed order ----
+  float m1 = -INFINITY, m2 = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kFuseRows; ++i) {
+    m1 = fmaxf(m1, fmaxf(fmaxf(x1[i].x, x1[i].y), fmaxf(x1[i].z, x1[i].w)));
+    m2 = fmaxf(m2, fmaxf(fmaxf(x2[i].x, x2[i].y), fmaxf(x2[i].z, x2[i].w)));
+  }
+  m1 = wave_max(m1);
+  m2 = wave_max(m2);
+  if (lane == 0) {
+    shs[wave][0] = m1;
+    shs[wave][1] = m2;
+  }
+  __syncthreads();
+  m1 = shs[0][0];
+  m2 = shs[0][1];
+#pragma unroll
+  for (int w = 1; w < kFuseWaves; ++w) {
+    m1 = fmaxf(m1, shs[w][0]);
+    m2 = fmaxf(m2, shs[w][1]);
+  }
+  float s1 = 0.f, q1 = 0.f, s2 = 0.f;
+#pragma unroll
+  for (int i = 0; i < kFuseRows; ++i) {
+    const float a[4] = {x1[i].x, x1[i].y, x1[i].z, x1[i].w};
+    const float c[4] = {x2[i].x, x2[i].y, x2[i].z, x2[i].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float e1 = ex2((a[j] - m1) * kLog2e);  // 0 for padding (-inf)
+      s1 += e1;
+      q1 += e1 * e1;
+      s2 += ex2((c[j] - m2) * kLog2e);
+    }
+  }
+  s1 = wave_sum(s1);
+  q1 = wave_sum(q1);
+  s2 = wave_sum(s2);
+  __syncthreads();  // every wave has read the maxima
+  if (lane == 0) {
+    shs[wave][0] = s1;
+    shs[wave][1] = q1;
+    shs[wave][2] = s2;
+  }
+  __syncthreads();
+  s1 = shs[0][0];
+  q1 = shs[0][1];
+  s2 = shs[0][2];
+#pragma unroll
+  for (int w = 1; w < kFuseWaves; ++w) {
+    s1 += shs[w][0];
+    q1 += shs[w][1];
+    s2 += shs[w][2];
+  }
+  Norm n;
+  n.m1 = m1;
+  n.m2 = m2;
+  n.alpha = __builtin_fmaf(0.5f, q1 / (s1 * s1), 0.5f);
+  n.w1 = n.alpha / s1;
+  n.w2 = (1.f - n.alpha) / s2;
+  // ---- p_mix, the masses and the first maximum ----
+  float* pm = p.p_mix ? p.p_mix + (size_t)b * p.vocab : nullptr;
+  float4 q[kFuseRows];
+  uint64_t mrow[kFuseRows];
+  uint64_t mine = 0;
+  float bv = -1.f;
+  int bi = p.vocab;
+#pragma unroll
+  for (int i = 0; i < kFuseRows; ++i) {
+    const int v = (g0 + 64 * i) * 4;
+    q[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    mrow[i] = 0;
+    if (v < p.vocab) {
+      const float a[4] = {x1[i].x, x1[i].y, x1[i].z, x1[i].w};
+      const float c[4] = {x2[i].x, x2[i].y, x2[i].z, x2[i].w};
+      float r[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        r[j] = __builtin_fmaf(n.w1, ex2((a[j] - n.m1) * kLog2e), n.w2 * ex2((c[j] - n.m2) * kLog2e));
+        mrow[i] += fixed(r[j]);
+        if (r[j] > bv) {  // tokens of a lane rise with i and j: the first maximum stays
+          bv = r[j];
+          bi = v + j;
+        }
+      }
+      q[i] = make_float4(r[0], r[1], r[2], r[3]);
+      if (pm) *(float4*)(pm + v) = q[i];
+    }
+    mine += mrow[i];
+  }
+  // ---- the draw: wave, row, lane, token ----
+  const uint64_t wtot = wave_sum_u64(mine);
+  if (lane == 0) shm[wave] = wtot;
+  if (threadIdx.x == 0) sel_tok = p.vocab - 1;  // not reached: one lane claims
+  block_first_max<kFuseWaves>(bv, bi, shv, shi);  // its barriers also publish shm and sel_tok
+  uint64_t total = 0, wbefore = 0;
+#pragma unroll
+  for (int w = 0; w < kFuseWaves; ++w) {
+    if (w < wave) wbefore += shm[w];
+    total += shm[w];
+  }
+  const float u = fminf(fmaxf(p.u[b], 0.f), 0x1.fffffep-1f);  // clamped to [0, 1)
+  uint64_t target = (uint64_t)((double)u * (double)total);
+  if (target >= total) target = total - 1;  // total > 0: the largest p_mix is at least 1 / vocab
+  if (wbefore <= target && target < wbefore + wtot) {  // exactly one wave: the intervals tile [0, total)
+    const uint64_t local = target - wbefore;
+    uint64_t rbase = 0, mr = 0, lane_mass = 0;
+    int row = -1;
+    float4 qr = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int i = 0; i < kFuseRows; ++i) {
+      const uint64_t t_i = wave_sum_u64(mrow[i]);
+      if (row < 0) {
+        if (local < rbase + t_i) {
+          row = i;
+          lane_mass = mrow[i];
+          qr = q[i];
+        } else {
+          rbase += t_i;
+        }
+      }
+    }
+    mr = local - rbase;  // below the row's total
+    const uint64_t incl = wave_incl_scan_u64(lane_mass);
+    uint64_t cum = incl - lane_mass;
+    if (cum <= mr && mr < incl) {  // exactly one lane
+      const float r[4] = {qr.x, qr.y, qr.z, qr.w};
+      const int v = (g0 + 64 * row) * 4;
+      int tok = v + 3;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        cum += fixed(r[j]);
+        if (cum > mr) {
+          tok = v + j;
+          break;
+        }
+      }
+      sel_tok = tok;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    p.token[b] = sel_tok;
+    p.greedy[b] = bi;
+    p.alpha[b] = n.alpha;
+  }
+}
+
 size_t mixture_chunks(int vocab) { return (size_t)((vocab + kMixChunk - 1) / kMixChunk); }
 
 hipError_t launch_mixture(const MixParams& p, hipStream_t stream) {
+  if (p.vocab <= kMixFusedMaxVocab) {
+    hipLaunchKernelGGL(mix_fused_kernel, dim3(p.batch), dim3(kFuseThreads), 0, stream, p);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(mix_stats_kernel, dim3(p.chunks, p.batch), dim3(kMixThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

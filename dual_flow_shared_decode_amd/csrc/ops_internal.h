@@ -60,6 +60,8 @@ struct GemvParams {
 constexpr int kMixChunk = 4096;
 constexpr int kMixMaxChunks = 256;
 constexpr int kMixRec = 8;  // floats per chunk-statistics record (5 used, 32-byte aligned)
+// Vocabularies up to this size take one workgroup per sequence (the logits held in registers).
+constexpr int kMixFusedMaxVocab = 32768;
 
 struct MixParams {
   const float* logits1;  // [batch, vocab]

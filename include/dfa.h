@@ -376,10 +376,12 @@ DFA_API dfa_status dfa_decode_stack(const dfa_stack_desc* desc, const dfa_stack_
  * caller; results independent of timing.
  * Masses are summed as integers (p_mix scaled by 2^35, truncated), so the
  * search is exact and independent of summation order; a token with less than
- * 2^-35 of mass is never drawn. Three launches on `stream`.
+ * 2^-35 of mass is never drawn. One launch on `stream` for vocab <= 32768,
+ * three above.
  * Limits: batch 1..65535; vocab a multiple of 4 in [4, 2^20]. The workspace
- * (dfa_mixture_workspace_size bytes, 16-byte aligned) holds per-chunk records;
- * its contents on entry do not matter.
+ * (dfa_mixture_workspace_size bytes, 16-byte aligned) holds per-chunk records
+ * for vocab > 32768 (required at every size); its contents on entry do not
+ * matter.
  */
 typedef struct dfa_mixture_desc {
   int32_t batch;

@@ -259,6 +259,10 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillParams 
       const uint16_t* vt = &v_lds[buf][0][0];
       // scores of both tiles for both column blocks
       f32x4 sv[2][kPfCb];
+      // the MFMA phases run at raised wave priority, so that while one wave
+      // feeds the matrix unit the other wave on the SIMD fills the gaps with
+      // its vector work (measured: 1005 -> 984 us at 4 x 4096 tokens)
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         bf16x8 kf[KS];
@@ -273,6 +277,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillParams 
           sv[u][cb] = acc;
         }
       }
+      __builtin_amdgcn_s_setprio(0);
       // wave-uniform: only chunks that reach past a row's position need the
       // causal mask, and only the last chunk holds positions past the block
       const bool diag = t0 + 31 > wave_first;
@@ -322,6 +327,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillParams 
         for (int j = 0; j < 4; ++j) pa[cb][j] = __builtin_amdgcn_perm(xb[2 * j + 1], xb[2 * j], 0x07060302u);
         l_run[cb] += psum;
       }
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const u32x2 w0 = *(const u32x2*)(vt + (grp * kVRow + 16 * db + n) * 4);
@@ -345,6 +351,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillParams 
           oacc[cb][db] = mfma(va, pb[cb], oacc[cb][db]);
         }
       }
+      __builtin_amdgcn_s_setprio(0);
     }
   };
 

@@ -110,6 +110,7 @@ SMALL = {
     "all_experts": W.MoeConfig("all", batch=32, hidden=128, mlp=128, experts=4, k1=2, k2=4, w_std=0.05),
     "one_expert": W.MoeConfig("one", batch=9, hidden=256, mlp=256, experts=1, k1=1, k2=1, w_std=0.05),
     "max_fanout": W.MoeConfig("wide", batch=3, hidden=128, mlp=128, experts=40, k1=1, k2=32, w_std=0.05),
+    "max_experts": W.MoeConfig("e1024", batch=6, hidden=128, mlp=128, experts=1024, k1=2, k2=8, w_std=0.05),
 }
 
 

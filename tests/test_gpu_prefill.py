@@ -7,8 +7,8 @@ prompt are not written. The first auxiliary step (dfa_decode_attn over the writt
 ctx_lens = prompt lengths) gives the primary's last prefill row for flow 1 and the oracle's
 auxiliary output for flow 2. Cases: 1, 2, 4, 8 and 16 query heads per kv head, head_dim 64 and 128,
 ragged prompts (lengths 0, 1, partial tiles, several query blocks and chunks), shuffled paged caches
-with 16-, 32- and 64-position blocks, and the full workload (4 prompts of 4096 tokens, 32/8 heads of
-128) on sampled rows.
+with 16-, 32- and 64-position blocks, the full workload (4 prompts of 4096 tokens, 32/8 heads of
+128) on sampled rows, and the longest prompt the kernel takes (2048 cache blocks).
 """
 import numpy as np
 import pytest
@@ -140,3 +140,25 @@ def test_full_workload_sampled():
     last, o1, o2 = first_aux_step(case, t)
     rows = np.stack([o[b, int(case.lens[b]) - 1] for b in range(cfg.batch)])
     assert_close(o1, rows, TOL, "full first step o1 vs the prefill's last row")
+
+
+def test_longest_prompt_fills_the_block_table():
+    """A 32768-token prompt in 16-position blocks: 2048 block-table entries, the most the kernel stages
+    (the host rejects one block more). Cache bit for bit, sampled rows against the decode oracle."""
+    cfg = W.PrefillConfig("max", batch=1, num_q_heads=8, num_kv_heads=1, head_dim=128, lens=(32768,))
+    say("case prefill: 32768 positions, 2048 cache blocks")
+    case = W.make_prefill_case(cfg, 58)
+    assert -(-int(case.lens.max()) // case.block_size) == 2048  # blocks the prompt spans (the table has a spare)
+    t, o = run_prefill(case)
+    assert np.all(np.isfinite(o))
+    ref_cache = PF.cache_after_prefill(case.k_cache, case.v_cache, case.block_table, case.k, case.v, case.lens,
+                                       case.block_size)
+    assert np.array_equal(cache_bits(t["k_cache"]), ref_cache["k_cache"])
+    assert np.array_equal(cache_bits(t["v_cache"]), ref_cache["v_cache"])
+    for pos in (0, 15, 16, 4095, 16383, 16384, 32751, 32752, 32767):
+        lens = np.array([pos + 1], dtype=np.int32)
+        ref = A.decode_attention(case.q[0, pos][None], None, None, ref_cache["k_cache"], ref_cache["v_cache"],
+                                 case.block_table, lens, num_kv_heads=cfg.num_kv_heads, scale=cfg.scale,
+                                 block_size=case.block_size, num_flows=1, q_dtype="bf16", kv_dtype="bf16")
+        assert_close(o[0, pos], ref["o1"][0], TOL, f"prefill t={pos}")
+

@@ -832,21 +832,25 @@ dfa_status dfa_moe_ffn(const dfa_moe_desc* d, const uint16_t* w_gate, const uint
     hipError_t e = dfa::launch_gemv(up, hs);
     if (e != hipSuccess) return fail(DFA_ERR_HIP, std::string("moe gate/up launch: ") + hipGetErrorString(e));
     // down projection of every selected expert, from the intermediates [batch][k2][2][mlp]
+    // (the two halves of each expert's matrix as the two matrices of one
+    // workgroup where they tile evenly: twice the weight bytes per stage)
     dfa::GemvParams dn = g;
+    const bool halves = (d->hidden / 2) % kMoeRowsDown == 0;
     dn.w = w_down;
     dn.x1 = dn.x2 = z;
     dn.y1 = dn.y2 = y;
-    dn.n = d->hidden;
+    dn.n = halves ? d->hidden / 2 : d->hidden;
     dn.k = d->mlp;
     dn.k_range = d->mlp;
-    dn.pair = 0;
+    dn.pair = halves ? 1 : 0;
+    dn.w2 = halves ? w_down + size_t(dn.n) * d->mlp : nullptr;  // packed by 16-row tiles: rows [n, 2n)
     dn.x_exact = 0;
-    dn.epilogue = dfa::kEpiNone;
+    dn.epilogue = halves ? dfa::kEpiSplitPair : dfa::kEpiNone;
     dn.w_seg1 = dn.w_seg2 = w_down;
-    dn.seg1_row = dn.seg2_row = d->hidden;
+    dn.seg1_row = dn.seg2_row = dn.n;
     dn.moe_wstride = int64_t(d->hidden) * d->mlp;
-    dn.rows_per_wg = d->hidden % kMoeRowsDown == 0 ? kMoeRowsDown : 64;
-    dn.moe_rgs = d->hidden / dn.rows_per_wg;
+    dn.rows_per_wg = dn.n % kMoeRowsDown == 0 ? kMoeRowsDown : 64;
+    dn.moe_rgs = dn.n / dn.rows_per_wg;
     dn.moe_row_s = 2 * d->k2;
     dn.moe_row_slot = 2;
     dn.moe_row_f = 1;

@@ -174,6 +174,14 @@ __device__ __forceinline__ void apply_epilogue(const GemvParams& p, int s, size_
       if (p.y2) store4(p.y2 + o1, y[0][1]);
       kv_append(p, s, n0, y[0][0], y[0][1]);
       break;
+    case kEpiSplitPair:
+      store4(p.y1 + o1, y[0][0]);
+      store4(p.y1 + o1 + p.n, y[0][1]);
+      if (two) {
+        store4(p.y2 + o2, y[1][0]);
+        store4(p.y2 + o2 + p.n, y[1][1]);
+      }
+      break;
   }
 }
 
@@ -465,10 +473,11 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvParams p) {
         y[f][mat][0] = v.x; y[f][mat][1] = v.y; y[f][mat][2] = v.z; y[f][mat][3] = v.w;
       }
     const int n0 = rg * kRowsPerWg + c4;
-    if (GROUPED) {  // rows (sequence, slot, flow) of the output: [batch][k2][2][n]
+    if (GROUPED) {  // rows (sequence, slot, flow) of the output: [batch][k2][2][n], or [2n] per row for split pairs
       const int s = ent[j] & 0xFFFF, slot = ent[j] >> 16;
-      const size_t o1 = ((size_t)(s * p.moe_k2 + slot) * 2) * p.n + n0;
-      apply_epilogue(p, s, o1, o1 + p.n, n0, y);
+      const size_t row = p.epilogue == kEpiSplitPair ? 2 * (size_t)p.n : (size_t)p.n;
+      const size_t o1 = ((size_t)(s * p.moe_k2 + slot) * 2) * row + n0;
+      apply_epilogue(p, s, o1, o1 + row, n0, y);
     } else {
       const size_t o = (size_t)j * p.n + n0;
       apply_epilogue(p, j, o, o, n0, y);

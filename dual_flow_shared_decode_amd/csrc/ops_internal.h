@@ -14,7 +14,10 @@ enum : int32_t { kEpiNone = 0, kEpiResidual = 1, kEpiSwiglu = 2, kEpiResidualCou
                  // layer-internal: rows [Wq; Wk; Wv]; columns [0, q_cols) are both flows' queries
                  // (y1/y2 [batch, q_cols]), the next kv_cols the primary's keys, then its values
                  // (appended to the cache). Split-K only (the finalize sees keys and values together).
-                 kEpiQkv = 5 };
+                 kEpiQkv = 5,
+                 // grouped (MoE) only: the two matrices are the two halves of one [2n, k] matrix;
+                 // outputs are rows of 2n floats, matrix 0 in columns [0, n), matrix 1 in [n, 2n)
+                 kEpiSplitPair = 6 };
 
 struct GemvParams {
   const uint16_t* w;   // tiled [n/16][k/8][16][8]

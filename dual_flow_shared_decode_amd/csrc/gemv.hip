@@ -488,7 +488,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvParams p) {
 // One thread per (sequence s, 4 columns): both flows' sums over the k-splits
 // (fixed order), then the epilogue. KS > 0: exactly KS splits, every load
 // issued before the first add; KS == 0: any number, four loads at a time.
-constexpr int kFinalizeThreads = 256;
+constexpr int kFinalizeThreads = 128;  // 128 rather than 256: the reduction spreads over twice as many CUs
 
 // Sum over the k-splits (fixed order) of partial row m, matrix mat, columns n0..n0+3.
 template <int KS>

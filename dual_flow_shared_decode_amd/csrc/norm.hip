@@ -14,7 +14,7 @@
 namespace dfa {
 
 namespace {
-constexpr int kNormThreads = 256;
+constexpr int kNormThreads = 1024;  // one float4 per thread at 4096 columns: one load round trip per pass
 }
 
 __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(NormParams p) {

@@ -29,7 +29,7 @@ namespace dfa {
 
 namespace {
 constexpr int kRouteThreads = 256;
-constexpr int kCombineThreads = 256;
+constexpr int kCombineThreads = 128;
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -79,31 +79,53 @@ __global__ __launch_bounds__(kCombineThreads) void moe_combine_kernel(MoeCombine
   const int item = blockIdx.x * kCombineThreads + threadIdx.x;
   if (item >= p.batch * groups) return;
   const int s = item / groups, n0 = (item - s * groups) * 4;
-  float4 m1 = make_float4(0.f, 0.f, 0.f, 0.f), m2 = m1;
-  for (int q = 0; q < p.k2; ++q) {
-    const float* row = p.y + ((size_t)(s * p.k2 + q) * 2) * p.hidden + n0;
-    if (q < p.k1) {
-      const float g = p.g1[(size_t)s * p.k1 + q];
-      const float4 v = *(const float4*)row;
-      m1.x = fmaf(g, v.x, m1.x); m1.y = fmaf(g, v.y, m1.y); m1.z = fmaf(g, v.z, m1.z); m1.w = fmaf(g, v.w, m1.w);
-    }
-    const float g = p.g2[(size_t)s * p.k2 + q];
-    const float4 v = *(const float4*)(row + p.hidden);
-    m2.x = fmaf(g, v.x, m2.x); m2.y = fmaf(g, v.y, m2.y); m2.z = fmaf(g, v.z, m2.z); m2.w = fmaf(g, v.w, m2.w);
-  }
   const size_t o = (size_t)s * p.hidden + n0;
+  const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+  const float4 c = p.c ? *(const float4*)(p.c + n0) : z;
+  const float4 r1 = p.res1 ? *(const float4*)(p.res1 + o) : z;
+  const float4 r2 = p.res2 ? *(const float4*)(p.res2 + o) : z;
+  float4 m1 = z, m2 = z;
+  // entries in batches: every load of a batch before its first product, the
+  // products in ranking order
+  constexpr int kBatch = 8;
+  for (int q0 = 0; q0 < p.k2; q0 += kBatch) {
+    float4 v1[kBatch], v2[kBatch];
+    float g1[kBatch], g2[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int q = q0 + j;
+      if (q < p.k2) {
+        const float* row = p.y + ((size_t)(s * p.k2 + q) * 2) * p.hidden + n0;
+        v2[j] = *(const float4*)(row + p.hidden);
+        g2[j] = p.g2[(size_t)s * p.k2 + q];
+        if (q < p.k1) {
+          v1[j] = *(const float4*)row;
+          g1[j] = p.g1[(size_t)s * p.k1 + q];
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int q = q0 + j;
+      if (q < p.k1) {
+        m1.x = fmaf(g1[j], v1[j].x, m1.x); m1.y = fmaf(g1[j], v1[j].y, m1.y);
+        m1.z = fmaf(g1[j], v1[j].z, m1.z); m1.w = fmaf(g1[j], v1[j].w, m1.w);
+      }
+      if (q < p.k2) {
+        m2.x = fmaf(g2[j], v2[j].x, m2.x); m2.y = fmaf(g2[j], v2[j].y, m2.y);
+        m2.z = fmaf(g2[j], v2[j].z, m2.z); m2.w = fmaf(g2[j], v2[j].w, m2.w);
+      }
+    }
+  }
   float4 o1 = m1, o2 = m2;
   if (p.c) {
-    const float4 c = *(const float4*)(p.c + n0);
     o2.x = fmaf(c.x, m1.x, o2.x); o2.y = fmaf(c.y, m1.y, o2.y); o2.z = fmaf(c.z, m1.z, o2.z); o2.w = fmaf(c.w, m1.w, o2.w);
   }
   if (p.res1) {
-    const float4 r = *(const float4*)(p.res1 + o);
-    o1.x = r.x + o1.x; o1.y = r.y + o1.y; o1.z = r.z + o1.z; o1.w = r.w + o1.w;
+    o1.x = r1.x + o1.x; o1.y = r1.y + o1.y; o1.z = r1.z + o1.z; o1.w = r1.w + o1.w;
   }
   if (p.res2) {
-    const float4 r = *(const float4*)(p.res2 + o);
-    o2.x = r.x + o2.x; o2.y = r.y + o2.y; o2.z = r.z + o2.z; o2.w = r.w + o2.w;
+    o2.x = r2.x + o2.x; o2.y = r2.y + o2.y; o2.z = r2.z + o2.z; o2.w = r2.w + o2.w;
   }
   *(float4*)(p.out1 + o) = o1;
   *(float4*)(p.out2 + o) = o2;

@@ -52,8 +52,20 @@ struct Norm {
   float alpha;
 };
 
-// The sequence's softmax normalisers and alpha from its chunk records, in
-// chunk order (every thread computes the same values).
+// The sequence's chunk records copied to LDS (thread t: record t; one load
+// round trip for all of them), for merge_records.
+__device__ __forceinline__ void stage_records(const float* rec, int chunks, float (*srec)[kMixRec]) {
+  const int t = threadIdx.x;
+  if (t < chunks) {
+    const float4 a = *(const float4*)(rec + (size_t)t * kMixRec);
+    const float4 c = *(const float4*)(rec + (size_t)t * kMixRec + 4);
+    srec[t][0] = a.x; srec[t][1] = a.y; srec[t][2] = a.z; srec[t][3] = a.w; srec[t][4] = c.x;
+  }
+  __syncthreads();
+}
+
+// The sequence's softmax normalisers and alpha from its chunk records (in
+// LDS), in chunk order (every thread computes the same values).
 __device__ __forceinline__ Norm merge_records(const float* rec, int chunks) {
   Norm n;
   n.m1 = -INFINITY;
@@ -217,8 +229,10 @@ __global__ __launch_bounds__(kMixThreads) void mix_chunk_kernel(MixParams p) {
   __shared__ uint64_t shm[kMixWaves];
   __shared__ float shv[kMixWaves];
   __shared__ int shi[kMixWaves];
+  __shared__ float srec[kMixMaxChunks][kMixRec];
   const int chunk = blockIdx.x, b = blockIdx.y;
-  const Norm n = merge_records(p.rec + (size_t)b * p.chunks * kMixRec, p.chunks);
+  stage_records(p.rec + (size_t)b * p.chunks * kMixRec, p.chunks, srec);
+  const Norm n = merge_records(&srec[0][0], p.chunks);
   const float* l1 = p.logits1 + (size_t)b * p.vocab;
   const float* l2 = p.logits2 + (size_t)b * p.vocab;
   float* pm = p.p_mix ? p.p_mix + (size_t)b * p.vocab : nullptr;
@@ -259,15 +273,17 @@ __global__ __launch_bounds__(kMixThreads) void mix_pick_kernel(MixParams p) {
   __shared__ int shi[kMixWaves];
   __shared__ int sel_chunk, sel_tok;
   __shared__ uint64_t sel_base;
+  __shared__ float srec[kMixMaxChunks][kMixRec];
   const int b = blockIdx.x, t = threadIdx.x;
-  // normalisers first: their loads overlap the chunk records'
-  const Norm n = merge_records(p.rec + (size_t)b * p.chunks * kMixRec, p.chunks);
-  // ---- chunk level: one chunk record per thread ----
+  // ---- chunk level: one chunk record per thread (loaded with the statistics) ----
   uint64_t mass = 0;
   float bv = -1.f;
   int bi = p.vocab;
+  uint4 r = make_uint4(0u, 0u, 0u, 0u);
+  if (t < p.chunks) r = *(const uint4*)(p.crec + ((size_t)b * p.chunks + t) * 4);
+  stage_records(p.rec + (size_t)b * p.chunks * kMixRec, p.chunks, srec);
+  const Norm n = merge_records(&srec[0][0], p.chunks);
   if (t < p.chunks) {
-    const uint4 r = *(const uint4*)(p.crec + ((size_t)b * p.chunks + t) * 4);
     mass = ((uint64_t)r.y << 32) | r.x;
     bv = __uint_as_float(r.z);
     bi = (int)r.w;

@@ -308,9 +308,18 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvParams p) {
     if (threadIdx.x < 64) {  // wave 0: lane s finds the slot of this expert in sequence s's selection
       const int s = threadIdx.x;
       int slot = -1;
-      if (s < p.batch)
-        for (int q = 0; q < p.moe_k2; ++q)
-          if (p.moe_sel[s * p.moe_k2 + q] == expert) slot = q;
+      if (s < p.batch) {
+        // eight selections in flight at a time (a sequence selects an expert at most once)
+        const int* sel = p.moe_sel + s * p.moe_k2;
+        for (int q0 = 0; q0 < p.moe_k2; q0 += 8) {
+          int v[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[j] = q0 + j < p.moe_k2 ? sel[q0 + j] : -1;
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (v[j] == expert) slot = q0 + j;
+        }
+      }
       const unsigned long long mask = __ballot(slot >= 0);
       if (slot >= 0) ent[__popcll(mask & ((1ull << s) - 1))] = s | (slot << 16);
       if (s == 0) ent_count = __popcll(mask);

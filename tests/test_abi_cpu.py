@@ -159,6 +159,9 @@ def test_gemv_plans():
     # KV append, one flow (32 padded rows), 1024 columns: 16 row groups -> 16 k-splits of two matrices
     assert dfa.dfa_dual_gemv_workspace_size(gemv_desc(n=1024, num_flows=1, epilogue=dfa.DFA_EPI_KV_APPEND)) == \
         16 * 2 * 32 * 1024 * 4
+    # 64 x 4096 (MoE router): one row group; the library's choice stops at 16 k-splits
+    assert dfa.dfa_dual_gemv_workspace_size(gemv_desc(n=64)) == 16 * rows * 64 * 4
+    assert dfa.dfa_dual_gemv_workspace_size(gemv_desc(n=64, k_split=32)) == 32 * rows * 64 * 4
     # 32000 x 4096 (output head over the vocabulary): 250 row groups of 128 rows, unsplit
     assert dfa.dfa_dual_gemv_workspace_size(gemv_desc(n=32000)) == 0
     assert dfa.dfa_dual_gemv_workspace_size(gemv_desc(n=32000, rows_per_wg=64, k_split=2)) == 2 * rows * 32000 * 4

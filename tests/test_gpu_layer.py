@@ -98,6 +98,27 @@ def test_gemv_epilogues(batch, k_split, rows):
     assert_close(y2, r2 + LY.couple(LY.linear(x2d, w), cpl.astype(np.float64), m1), what="coupled y2")
 
 
+@pytest.mark.parametrize("k_split", [0, 32])
+def test_gemv_many_k_ranges(k_split):
+    """64 x 4096, the shape of a MoE router: the library's choice (16 k-ranges, all of a reduction
+    thread's loads at once) and 32 k-ranges (the reduction's general path)."""
+    rng = np.random.default_rng(31 + k_split)
+    n, k = 64, 4096
+    x1, x2 = rng.standard_normal((2, 32, k)).astype(np.float32)
+    r1, r2 = rng.standard_normal((2, 32, n)).astype(np.float32)
+    cpl = rng.standard_normal(n).astype(np.float32) * np.float32(0.1)
+    w = rand_w(rng, n, k)
+    x1d, x2d = x1.astype(np.float64), x2.astype(np.float64)
+    say(f"case gemv 64 x 4096 k_split={k_split}")
+    y1, y2 = gemv(dfa.DFA_EPI_NONE, w, x1, x2, k_split=k_split)
+    assert_close(y1, LY.linear(x1d, w), what="router y1")
+    assert_close(y2, LY.linear(x2d, w), what="router y2")
+    y1, y2 = gemv(dfa.DFA_EPI_RESIDUAL_COUPLED, w, x1, x2, couple=cpl, res1=r1, res2=r2, k_split=k_split)
+    m1 = LY.linear(x1d, w)
+    assert_close(y1, r1 + m1, what="router coupled y1")
+    assert_close(y2, r2 + LY.couple(LY.linear(x2d, w), cpl.astype(np.float64), m1), what="router coupled y2")
+
+
 @pytest.mark.parametrize("k_split", [1, 3])
 def test_gemv_rows_multiple_of_64(k_split):
     rng = np.random.default_rng(11 + k_split)

@@ -11,7 +11,8 @@ import numpy as np
 def bf16_bits_to_f64(bits) -> np.ndarray:
     """Exact value of bf16 bit patterns as float64."""
     u32 = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
-    return u32.view(np.float32).astype(np.float64)
+    with np.errstate(invalid="ignore"):  # NaN patterns (padding of some inputs) decode to NaN
+        return u32.view(np.float32).astype(np.float64)
 
 
 def to_f64(x, dtype: str) -> np.ndarray:

@@ -55,22 +55,30 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(MoeRouteParams
     if (rank < p.k2) sel_sh[rank] = e;
   }
   __syncthreads();
-  if (t == 0) {
-    // softmax of each flow's logits over its set, summed in ranking order
-    const float m1 = r1s[sel_sh[0]];
-    float m2 = -INFINITY;
-    for (int q = 0; q < p.k2; ++q) m2 = fmaxf(m2, r2s[sel_sh[q]]);
+  if (t < 64) {
+    // softmax of each flow's logits over its set: lane q takes selection q
+    // (k2 <= 32), lane 0 sums the exponentials in ranking order
+    const int q = t;
+    const bool in2 = q < p.k2, in1 = q < p.k1;
+    const int e = in2 ? sel_sh[q] : 0;
+    const float a1 = r1s[e], a2 = r2s[e];
+    const float m1 = r1s[sel_sh[0]];  // the top-ranked logit is the primary's largest
+    float m2 = in2 ? a2 : -INFINITY;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m2 = fmaxf(m2, __shfl_xor(m2, o));
+    const float e1 = in1 ? ex2((a1 - m1) * kLog2e) : 0.f;
+    const float e2 = in2 ? ex2((a2 - m2) * kLog2e) : 0.f;
     float s1 = 0.f, s2 = 0.f;
-    for (int q = 0; q < p.k2; ++q) {
-      if (q < p.k1) s1 += ex2((r1s[sel_sh[q]] - m1) * kLog2e);
-      s2 += ex2((r2s[sel_sh[q]] - m2) * kLog2e);
+    for (int j = 0; j < p.k2; ++j) {  // every lane runs the same ordered sums
+      const float x1 = __shfl(e1, j), x2 = __shfl(e2, j);
+      if (j < p.k1) s1 += x1;
+      s2 += x2;
     }
-    for (int q = 0; q < p.k2; ++q) {
-      const int e = sel_sh[q];
+    if (in2) {
       p.sel[(size_t)s * p.k2 + q] = e;
-      if (q < p.k1) p.g1[(size_t)s * p.k1 + q] = ex2((r1s[e] - m1) * kLog2e) / s1;
-      p.g2[(size_t)s * p.k2 + q] = ex2((r2s[e] - m2) * kLog2e) / s2;
+      p.g2[(size_t)s * p.k2 + q] = e2 / s2;
     }
+    if (in1) p.g1[(size_t)s * p.k1 + q] = e1 / s1;
   }
 }
 

@@ -4,23 +4,30 @@
 One step = one dfa_decode_attn call over the whole batch: the attention
 kernel (auxiliary query coupled in its prologue; both flows' scores, online
 softmax and weighted values from one read of every cached key and value),
-followed by the log-sum-exp combine when the library splits sequences (for
-the default workload it uses two splits per sequence). The K timed steps run
-back to back between two HIP events on the launch stream; `value` and
-`ms_per_step` come from them. A second pass of K steps measures the attention
-kernel alone: each launch carries start/stop events recorded from its own
-dispatch (dfa_decode_attn_timed), and their mean is the kernel's average
-launch duration used for `roofline.achieved`. Inputs are resident in HBM
-before timing; four copies of the cache are rotated between steps so that no
-step finds the cache in the 256 MB last-level cache.
+followed by the log-sum-exp combine when the library splits sequences. The
+default workload is the largest attention workload that fits one GPU: batch
+4, 32 query / 8 kv heads of 128, 131072 cached positions per sequence (2 GiB
+of bf16 cache), 1% of the keys scaled by 8. The K timed steps run back to back
+between two HIP events on the launch stream; `value` and `ms_per_step` come
+from them. A second pass of K steps measures the attention kernel alone: each
+launch carries start/stop events recorded from its own dispatch
+(dfa_decode_attn_timed), and their mean is the kernel's average launch
+duration used for `roofline.achieved`. Inputs are resident in HBM before
+timing; when a cache is smaller than 1 GiB, copies of it are rotated between
+steps so that no step finds it in the 256 MB last-level cache.
 
 Prints one JSON line. `value` is tokens per second counting both flows (two
 per sequence per step). Also reported: achieved HBM bandwidth of the step and
-of the split kernel against the 8 TB/s peak, the measured stream-read ceiling,
-the auxiliary flow's increment over a one-flow run of the same kernel, and the
-CPU oracle's rate on a bounded sample (context only).
+of the split kernel against the 8 TB/s peak, the HBM traffic per launch from
+the committed counter summary of the workload (both flows and one flow), the
+measured stream-read ceiling, the auxiliary flow's increment over a one-flow
+run of the same kernel, the same figures for the two other attention
+workloads (`other_workloads`: batch 16 x 4096 positions; batch 64 with ragged
+lengths in a shuffled paged cache), and the CPU oracle's rate on a bounded
+sample (context only).
 
-    python bench.py [--steps K] [--warmup W] [--config c2|c3|c4|c5|head|moe|prefill|stack]
+    python bench.py [--steps K] [--warmup W] [--flows 1|2]
+                    [--config c2|c3|c4|c5|head|moe|prefill|stack]
 """
 import argparse
 import hashlib
@@ -37,7 +44,6 @@ METRIC = "dual-flow decode attn: tokens/s (both flows) + achieved HBM GB/s vs pe
 HBM_PEAK_GBPS = 8000.0
 KERNEL_SOURCES = ["dual_flow_shared_decode_amd/csrc/" + f
                   for f in ("attn_bf16.hip", "attn_common.h", "dfa_internal.h", "launch.h")]
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "attn_bf16_c2_counters.txt")
 
 
 def log(msg):
@@ -52,13 +58,18 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(config_name: str):
-    """HBM bytes per split-kernel launch from the committed counter summary, or None
-    when there is none for this workload or the kernel source changed since."""
-    if config_name != "c2" or not os.path.exists(COUNTERS_FILE):
+def counters_file(config_name: str) -> str:
+    return os.path.join(ROOT, "profiles", f"attn_bf16_{config_name}_counters.txt")
+
+
+def measured_traffic(config_name: str, flows: int = 2):
+    """HBM bytes per attention-kernel launch with `flows` flows from the committed counter summary
+    of the workload, or None when there is none or the kernel sources changed since it was made."""
+    path = counters_file(config_name)
+    if not os.path.exists(path):
         return None
     vals = {}
-    with open(COUNTERS_FILE) as f:
+    with open(path) as f:
         for line in f:
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
@@ -66,7 +77,7 @@ def measured_traffic(config_name: str):
     if vals.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
     try:
-        return float(vals["hbm_bytes_per_launch"])
+        return float(vals[f"hbm_bytes_per_launch_{flows}flow"])
     except (KeyError, ValueError):
         return None
 
@@ -85,8 +96,9 @@ def algorithmic_bytes(case, num_flows):
 
 
 def cpu_baseline(case, budget_s: float):
-    """The float64 oracle, as it stands, on (sequence, kv head) pairs of the same
-    workload until the time budget is spent; rate scaled to tokens/s of both flows."""
+    """The float64 oracle, as it stands, on (sequence, kv head) pairs of the same workload, taken in
+    order (cycling) until the time budget is spent; the rate is scaled to tokens/s of both flows (a
+    sequence is all of its kv heads)."""
     from threadpoolctl import threadpool_info
 
     from oracle import attention as A
@@ -94,23 +106,26 @@ def cpu_baseline(case, budget_s: float):
     pairs = [(b, g) for b in range(cfg.batch) for g in range(cfg.num_kv_heads)]
     t0 = time.perf_counter()
     done = 0
-    while time.perf_counter() - t0 < budget_s:  # whole passes over the batch until the budget is spent
-        for pair in pairs:
-            A.decode_attention(case.q1, case.q2, case.a, case.k_cache, case.v_cache, case.block_table,
-                               case.ctx_lens, num_kv_heads=cfg.num_kv_heads, scale=cfg.scale,
-                               block_size=case.block_size, num_flows=2, q_dtype=cfg.qtype, kv_dtype=cfg.dtype,
-                               pairs=[pair])
-            done += 1
-            if time.perf_counter() - t0 > 3 * budget_s:
-                break
+    positions = 0
+    while time.perf_counter() - t0 < budget_s:
+        b, g = pairs[done % len(pairs)]
+        A.decode_attention(case.q1, case.q2, case.a, case.k_cache, case.v_cache, case.block_table,
+                           case.ctx_lens, num_kv_heads=cfg.num_kv_heads, scale=cfg.scale,
+                           block_size=case.block_size, num_flows=2, q_dtype=cfg.qtype, kv_dtype=cfg.dtype,
+                           pairs=[(b, g)])
+        done += 1
+        positions += int(case.ctx_lens[b])
     dt = time.perf_counter() - t0
     blas = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
-    seqs = done / cfg.num_kv_heads
+    # a sequence-step is num_kv_heads pair evaluations of the sequence's length
+    mean_len = float(case.ctx_lens.mean())
+    seqs = positions / (mean_len * cfg.num_kv_heads)
     return {"value": 2.0 * seqs / dt, "unit": "tokens/s (both flows)", "cores": int(max(blas) if blas else 1),
             "kind": "oracle",
-            "sample": f"{done} (sequence, kv head) evaluations = {done / len(pairs):.2f} passes over the "
-                      f"{len(pairs)} pairs of {cfg.name} ({int(case.ctx_lens.max())} positions each), both flows, "
-                      f"float64 numpy oracle, {dt:.1f} s",
+            "sample": f"{done} (sequence, kv head) evaluations ({positions} cached positions, both flows, all "
+                      f"{cfg.num_q_heads // cfg.num_kv_heads} query heads of each kv head) of {cfg.name}, pairs "
+                      f"taken in order from the first; float64 numpy oracle, {dt:.1f} s; rate = positions / "
+                      f"(mean length x kv heads) sequence-steps per second, x2 flows",
             "host_cpus": len(os.sched_getaffinity(0))}
 
 
@@ -521,78 +536,42 @@ def bench_stack(args):
                       "frac_of_peak": gbps / HBM_PEAK_GBPS, "algorithmic_bytes_per_step": nbytes}), flush=True)
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="c2", choices=["c2", "c3", "c4", "c5", "head", "moe", "prefill", "stack"],
-                    help="c2 (default): the attention workload the metric is quoted on; c5: a whole layer step; "
-                         "head: the dual output head and mixture sampling; moe: the MoE FFN with router replay; "
-                         "prefill: the primary-only prefill and the first auxiliary step; stack: 4 layers with RMSNorm "
-                         "and rotary embeddings in a HIP graph")
-    ap.add_argument("--split", type=int, default=0, help="positions per split (0: library choice)")
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extras", action="store_true", help="time the steps only (for profiler runs)")
-    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
-                    help="after timing, copy a MIB-MiB buffer once (a known-size reference for HBM counters)")
-    args = ap.parse_args()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU (asked for --gpus {args.gpus}, WORLD_SIZE {world}); this "
-              "library runs on a single GPU and sharding across GPUs is not part of it", file=sys.stderr)
-        sys.exit(2)
-
-    import numpy as np
+def attn_measure(name, args, flows=2, one_flow=True, log_prefix=""):
+    """Times dfa_decode_attn on attention workload `name`: K steps back to back between two HIP
+    events, then K launches with per-dispatch events for the attention kernel alone, optionally the
+    same with one flow. Returns the case and the figures."""
     import torch
 
     import dual_flow_shared_decode_amd as dfa
     import workloads as W
     from workloads.device import upload_attn_case
 
-    torch.cuda.set_device(0)
-    if args.config == "c5":
-        bench_layer(args)
-        return
-    if args.config == "head":
-        bench_head(args)
-        return
-    if args.config == "moe":
-        bench_moe(args)
-        return
-    if args.config == "prefill":
-        bench_prefill(args)
-        return
-    if args.config == "stack":
-        bench_stack(args)
-        return
-    cfg = W.ATTN_CONFIGS[args.config]
-    log(f"generating {cfg.name} inputs")
+    cfg = W.ATTN_CONFIGS[name]
+    log(f"{log_prefix}generating {cfg.name} inputs")
     case = W.make_attn_case(cfg, W.SEEDS[cfg.name], pad_nan=False)
     t = upload_attn_case(case)
     kv_set_bytes = (case.k_cache.nbytes + case.v_cache.nbytes)
     nsets = max(1, min(4, math.ceil((1 << 30) / kv_set_bytes)))
     sets = [(t["k_cache"], t["v_cache"])] + [(t["k_cache"].clone(), t["v_cache"].clone()) for _ in range(nsets - 1)]
-    log(f"{nsets} cache copies of {kv_set_bytes / 2**20:.0f} MiB rotated between steps")
+    log(f"{log_prefix}{nsets} cache copies of {kv_set_bytes / 2**20:.0f} MiB rotated between steps")
 
-    def make_desc(flows):
+    def make_desc(nf):
         return dfa.AttnDesc(batch=cfg.batch, num_q_heads=cfg.num_q_heads, num_kv_heads=cfg.num_kv_heads,
                             head_dim=cfg.head_dim, block_size=case.block_size,
                             max_blocks_per_seq=case.max_blocks_per_seq, num_blocks=case.k_cache.shape[0],
-                            max_ctx_len=case.max_ctx_len, num_flows=flows, split_len=args.split,
+                            max_ctx_len=case.max_ctx_len, num_flows=nf, split_len=args.split,
                             scale=cfg.scale, q_dtype=dfa.DFA_BF16, kv_dtype=dfa.DFA_BF16)
 
     stream = torch.cuda.current_stream()
     o1 = torch.empty((cfg.batch, cfg.num_q_heads, cfg.head_dim), dtype=torch.float32, device="cuda")
     o2 = torch.empty_like(o1)
 
-    def runner(flows):
-        d = make_desc(flows)
+    def runner(nf):
+        d = make_desc(nf)
         ws = torch.zeros(max(dfa.dfa_decode_attn_workspace_size(d) // 4, 4), dtype=torch.float32, device="cuda")
-        q2 = t["q2"] if flows == 2 else None
-        a = t["a"] if flows == 2 else None
-        out2 = o2 if flows == 2 else None
+        q2 = t["q2"] if nf == 2 else None
+        a = t["a"] if nf == 2 else None
+        out2 = o2 if nf == 2 else None
 
         def step(i, ev=None):
             k, v = sets[i % nsets]
@@ -626,44 +605,126 @@ def main():
         torch.cuda.synchronize()
         return [e0.elapsed_time(e1) for e0, e1 in evs]
 
-    d2, step2 = runner(2)
-    log(f"split length {dfa.dfa_decode_attn_split_len(d2)}, {dfa.dfa_decode_attn_num_splits(d2)} splits; timing")
-    ms, wall = timed(step2, args.steps, args.warmup)
-    kern_all = sorted(kernel_ms(step2, args.steps))
-    kern_ms = sum(kern_all) / len(kern_all)
+    d_main, step_main = runner(flows)
+    log(f"{log_prefix}{flows} flow(s), split length {dfa.dfa_decode_attn_split_len(d_main)}, "
+        f"{dfa.dfa_decode_attn_num_splits(d_main)} splits; timing")
+    ms, wall = timed(step_main, args.steps, args.warmup)
+    kern_all = sorted(kernel_ms(step_main, args.steps))
+    m = {"case": case, "cfg": cfg, "flows": flows, "ms": ms, "wall": wall, "kern_all": kern_all,
+         "kern_ms": sum(kern_all) / len(kern_all), "split_len": dfa.dfa_decode_attn_split_len(d_main),
+         "num_splits": dfa.dfa_decode_attn_num_splits(d_main), "nsets": nsets,
+         "bytes": algorithmic_bytes(case, flows)}
+    log(f"{log_prefix}{cfg.name}: {ms * 1e3:.1f} us/step ({wall:.3f} s wall for {args.steps} steps); attention "
+        f"kernel {m['kern_ms'] * 1e3:.1f} us per launch; {m['bytes'] / (m['kern_ms'] * 1e-3) / 1e9:.0f} GB/s kernel")
+    if one_flow and flows == 2:
+        d1, step1 = runner(1)
+        ms1, _ = timed(step1, args.steps, args.warmup)
+        kern1 = sum(kernel_ms(step1, args.steps)) / args.steps
+        m["ms_one_flow"] = ms1
+        m["kern_ms_one_flow"] = kern1
+        log(f"{log_prefix}one flow: {ms1 * 1e3:.1f} us/step, kernel {kern1 * 1e3:.1f} us -> aux increment "
+            f"{100 * (ms / ms1 - 1):.1f}% (step), {100 * (m['kern_ms'] / kern1 - 1):.1f}% (kernel)")
+    del sets, t
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return m
+
+
+def kernel_name_of(cfg, flows):
+    rows = cfg.num_q_heads // cfg.num_kv_heads * flows
+    return (f"attn_bf16_kernel<{cfg.head_dim}, {8 if rows <= 8 else 16}, false>" if cfg.dtype == "bf16"
+            else f"attn_f32_kernel<{cfg.head_dim}>")
+
+
+def summary_of(m):
+    """The figures of one attention workload, as extra keys of the bench line."""
+    kb = m["bytes"] / (m["kern_ms"] * 1e-3) / 1e9
+    sb = m["bytes"] / (m["ms"] * 1e-3) / 1e9
+    out = {"workload": m["cfg"].name, "ms_per_step": m["ms"], "kernel_avg_us": m["kern_ms"] * 1e3,
+           "kernel": kernel_name_of(m["cfg"], m["flows"]), "algorithmic_bytes_per_launch": m["bytes"],
+           "kernel_gbps": kb, "frac": kb / HBM_PEAK_GBPS, "step_gbps": sb, "step_frac": sb / HBM_PEAK_GBPS,
+           "split_len": m["split_len"], "num_splits": m["num_splits"],
+           "tokens_per_s_both_flows": 2 * m["cfg"].batch / (m["ms"] * 1e-3),
+           "traffic": measured_traffic(m["cfg"].name, m["flows"])}
+    if "ms_one_flow" in m:
+        out["ms_per_step_one_flow"] = m["ms_one_flow"]
+        out["aux_increment"] = m["ms"] / m["ms_one_flow"] - 1.0
+        out["aux_increment_kernel"] = m["kern_ms"] / m["kern_ms_one_flow"] - 1.0
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="c4", choices=["c2", "c3", "c4", "c5", "head", "moe", "prefill", "stack"],
+                    help="c4 (default): the largest attention workload, the headline; c2, c3: the other attention "
+                         "workloads alone; c5: a whole layer step; head: the dual output head and mixture sampling; "
+                         "moe: the MoE FFN with router replay; prefill: the primary-only prefill and the first "
+                         "auxiliary step; stack: 4 layers with RMSNorm and rotary embeddings in a HIP graph")
+    ap.add_argument("--flows", type=int, default=2, choices=[1, 2],
+                    help="flows of the timed attention steps (1: the single-flow run of the same kernel, for "
+                         "counter comparisons)")
+    ap.add_argument("--split", type=int, default=0, help="positions per split (0: library choice)")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="time the steps only (for profiler runs)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="after timing, copy a MIB-MiB buffer once (a known-size reference for HBM counters)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU (asked for --gpus {args.gpus}, WORLD_SIZE {world}); this "
+              "library runs on a single GPU and sharding across GPUs is not part of it", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import dual_flow_shared_decode_amd as dfa
+
+    torch.cuda.set_device(0)
+    other = {"c5": bench_layer, "head": bench_head, "moe": bench_moe, "prefill": bench_prefill, "stack": bench_stack}
+    if args.config in other:
+        other[args.config](args)
+        return
+    stream = torch.cuda.current_stream()
+    m = attn_measure(args.config, args, flows=args.flows, one_flow=not args.no_extras)
+    case, cfg = m["case"], m["cfg"]
+    ms, kern_all, kern_ms = m["ms"], m["kern_all"], m["kern_ms"]
 
     def pct(v, q):  # nearest-rank percentile of a sorted list
         return v[min(len(v) - 1, max(0, int(math.ceil(q / 100 * len(v))) - 1))]
-    step_bytes = kern_bytes = algorithmic_bytes(case, 2)
-    rows = cfg.num_q_heads // cfg.num_kv_heads * 2
-    kernel_name = (f"attn_bf16_kernel<{cfg.head_dim}, {8 if rows <= 8 else 16}, false>" if cfg.dtype == "bf16"
-                   else f"attn_f32_kernel<{cfg.head_dim}>")
+    step_bytes = kern_bytes = m["bytes"]
     step_gbps = step_bytes / (ms * 1e-3) / 1e9
     kern_gbps = kern_bytes / (kern_ms * 1e-3) / 1e9
-    flow_tokens = 2 * cfg.batch / (ms * 1e-3)
-    log(f"{ms * 1e3:.1f} us/step ({wall:.3f} s wall for {args.steps} steps); attention kernel {kern_ms * 1e3:.1f} us "
-        f"per launch; {step_gbps:.0f} GB/s step, {kern_gbps:.0f} GB/s kernel")
-
-    rec = {"metric": METRIC, "value": flow_tokens, "unit": "tokens/s (both flows)", "n_gpus": 1,
+    flow_tokens = args.flows * cfg.batch / (ms * 1e-3)
+    rec = {"metric": METRIC, "value": flow_tokens,
+           "unit": "tokens/s (both flows)" if args.flows == 2 else "tokens/s (one flow)", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
            "config": {"workload": f"{cfg.name}: dual-flow decode attention, batch {cfg.batch}, "
                                   f"{cfg.num_q_heads} query / {cfg.num_kv_heads} kv heads, head_dim {cfg.head_dim}, "
                                   f"context {int(case.ctx_lens.min())}-{int(case.ctx_lens.max())}, bf16 cache, "
-                                  f"{'paged ' + str(case.block_size) if cfg.block_size else 'contiguous'}",
+                                  f"{'paged ' + str(case.block_size) if cfg.block_size else 'contiguous'}"
+                                  f"{', 1% of keys x8' if cfg.name == 'c4' else ''}",
                       "batch": cfg.batch, "num_q_heads": cfg.num_q_heads, "num_kv_heads": cfg.num_kv_heads,
-                      "head_dim": cfg.head_dim, "ctx_total": int(case.ctx_lens.sum()), "num_flows": 2,
-                      "split_len": dfa.dfa_decode_attn_split_len(d2),
-                      "num_splits": dfa.dfa_decode_attn_num_splits(d2), "cache_copies": nsets},
+                      "head_dim": cfg.head_dim, "ctx_total": int(case.ctx_lens.sum()), "num_flows": args.flows,
+                      "split_len": m["split_len"], "num_splits": m["num_splits"], "cache_copies": m["nsets"]},
            "accumulate": "f32",
            "seq_tokens_per_s": cfg.batch / (ms * 1e-3),
            "achieved_gbps": step_gbps, "hbm_peak_gbps": HBM_PEAK_GBPS, "frac_of_peak": step_gbps / HBM_PEAK_GBPS,
            "algorithmic_bytes_per_step": step_bytes,
-           "roofline": {"bound": "hbm", "kernel": kernel_name, "achieved": kern_gbps,
+           "roofline": {"bound": "hbm", "kernel": kernel_name_of(cfg, args.flows), "achieved": kern_gbps,
                         "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": kern_gbps / HBM_PEAK_GBPS,
-                        "traffic": measured_traffic(cfg.name), "algorithmic_bytes_per_launch": kern_bytes,
+                        "traffic": measured_traffic(cfg.name, args.flows), "algorithmic_bytes_per_launch": kern_bytes,
                         "avg_launch_us": kern_ms * 1e3, "median_launch_us": pct(kern_all, 50) * 1e3,
                         "p10_launch_us": pct(kern_all, 10) * 1e3, "p90_launch_us": pct(kern_all, 90) * 1e3}}
+    if rec["roofline"]["traffic"]:
+        rec["roofline"]["traffic_over_algorithmic"] = rec["roofline"]["traffic"] / kern_bytes
+    t2, t1 = measured_traffic(cfg.name, 2), measured_traffic(cfg.name, 1)
+    if t2 and t1:
+        rec["traffic_two_flows_over_one_flow"] = t2 / t1
 
     if args.copy_calibration:
         n = args.copy_calibration << 20
@@ -675,14 +736,10 @@ def main():
         rec["copy_calibration_bytes"] = n
         del src, dst
     if not args.no_extras:
-        d1, step1 = runner(1)
-        ms1, _ = timed(step1, args.steps, args.warmup)
-        kern1 = sum(kernel_ms(step1, args.steps)) / args.steps
-        rec["ms_per_step_one_flow"] = ms1
-        rec["aux_increment"] = ms / ms1 - 1.0
-        rec["aux_increment_kernel"] = kern_ms / kern1 - 1.0
-        log(f"one flow: {ms1 * 1e3:.1f} us/step, kernel {kern1 * 1e3:.1f} us -> aux increment "
-            f"{100 * rec['aux_increment']:.1f}%")
+        if "ms_one_flow" in m:
+            rec["ms_per_step_one_flow"] = m["ms_one_flow"]
+            rec["aux_increment"] = ms / m["ms_one_flow"] - 1.0
+            rec["aux_increment_kernel"] = kern_ms / m["kern_ms_one_flow"] - 1.0
         buf = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
         sink = torch.empty(dfa.dfa_stream_read_sink_bytes() // 4, dtype=torch.int32, device="cuda")
         for _ in range(3):
@@ -698,6 +755,13 @@ def main():
         rec["frac_of_stream_read"] = kern_gbps / ceil_gbps
         del buf
         log(f"stream-read ceiling {ceil_gbps:.0f} GB/s")
+        # the other attention workloads of the metric, timed the same way (the headline is the largest)
+        rec["other_workloads"] = {}
+        for name in ("c2", "c3", "c4"):
+            if name == cfg.name:
+                continue
+            rec["other_workloads"][name] = summary_of(attn_measure(name, args, flows=2, one_flow=True,
+                                                                   log_prefix="  "))
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
         rec["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)

@@ -102,7 +102,9 @@ __device__ __forceinline__ float4 mix4(const float* l1, const float* l2, int v, 
   return q;
 }
 
-__device__ __forceinline__ uint64_t fixed(float q) { return (uint64_t)(q * kFix); }
+// Integer mass of a probability: q * 2^35 truncated; 0 for NaN (a row with a
+// non-finite logit), so no conversion of a non-finite value happens.
+__device__ __forceinline__ uint64_t fixed(float q) { return q > 0.f ? (uint64_t)(fminf(q, 1.f) * kFix) : 0; }
 
 __device__ __forceinline__ uint64_t shfl_up_u64(uint64_t x, int d) {
   const uint32_t lo = __shfl_up((uint32_t)x, d), hi = __shfl_up((uint32_t)(x >> 32), d);
@@ -288,20 +290,35 @@ __global__ __launch_bounds__(kMixThreads) void mix_pick_kernel(MixParams p) {
     bv = __uint_as_float(r.z);
     bi = (int)r.w;
   }
+  // Defaults for a row no chunk claims (a row whose mixture has no finite
+  // mass, from a non-finite logit): chunk 0 at base 0. The scan's barriers
+  // publish them before any thread may overwrite them.
+  if (t == 0) {
+    sel_chunk = 0;
+    sel_base = 0;
+  }
   uint64_t total;
   const uint64_t before = block_excl_scan<kMixWaves>(mass, shm, total);
   const float u = fminf(fmaxf(p.u[b], 0.f), 0x1.fffffep-1f);  // clamped to [0, 1)
   uint64_t target = (uint64_t)((double)u * (double)total);
-  if (target >= total) target = total - 1;  // total > 0: the largest p_mix is at least 1 / vocab
-  if (before <= target && target < before + mass) {  // exactly one chunk: the intervals tile [0, total)
+  if (total > 0 && target >= total) target = total - 1;  // the largest p_mix is at least 1 / vocab
+  if (total > 0 && before <= target && target < before + mass) {  // one chunk: the intervals tile [0, total)
     sel_chunk = t;
     sel_base = before;
   }
   block_first_max<kMixWaves>(bv, bi, shv, shi);  // its barriers also publish sel_chunk and sel_base
+  if (total == 0) {  // workgroup-uniform: nothing to draw from; the defined token is the last one
+    if (t == 0) {
+      p.token[b] = p.vocab - 1;
+      p.greedy[b] = bi < p.vocab ? bi : p.vocab - 1;
+    }
+    return;
+  }
   // ---- token level inside the chosen chunk: the masses mix_chunk_kernel summed ----
   const float* l1 = p.logits1 + (size_t)b * p.vocab;
   const float* l2 = p.logits2 + (size_t)b * p.vocab;
-  const int v0 = sel_chunk * kMixChunk + t * kRun;
+  const int chunk_sel = min(max(sel_chunk, 0), p.chunks - 1);
+  const int v0 = chunk_sel * kMixChunk + t * kRun;
   uint64_t m[kRun];
   uint64_t run = 0;
 #pragma unroll
@@ -316,7 +333,7 @@ __global__ __launch_bounds__(kMixThreads) void mix_pick_kernel(MixParams p) {
     run += m[4 * i] + m[4 * i + 1] + m[4 * i + 2] + m[4 * i + 3];
   }
   const uint64_t local = target - sel_base;  // below the chunk's mass
-  if (t == 0) sel_tok = min(sel_chunk * kMixChunk + kMixChunk, p.vocab) - 1;  // not reached: one thread claims
+  if (t == 0) sel_tok = min(chunk_sel * kMixChunk + kMixChunk, p.vocab) - 1;  // not reached: one thread claims
   uint64_t chunk_total;
   uint64_t cum = block_excl_scan<kMixWaves>(run, shm, chunk_total);
   if (cum <= local && local < cum + run) {  // exactly one thread
@@ -334,7 +351,7 @@ __global__ __launch_bounds__(kMixThreads) void mix_pick_kernel(MixParams p) {
   __syncthreads();
   if (t == 0) {
     p.token[b] = sel_tok;
-    p.greedy[b] = bi;
+    p.greedy[b] = bi < p.vocab ? bi : p.vocab - 1;
   }
 }
 
@@ -507,8 +524,9 @@ __global__ __launch_bounds__(kFuseThreads) void mix_fused_kernel(MixParams p) {
   }
   const float u = fminf(fmaxf(p.u[b], 0.f), 0x1.fffffep-1f);  // clamped to [0, 1)
   uint64_t target = (uint64_t)((double)u * (double)total);
-  if (target >= total) target = total - 1;  // total > 0: the largest p_mix is at least 1 / vocab
-  if (wbefore <= target && target < wbefore + wtot) {  // exactly one wave: the intervals tile [0, total)
+  if (total > 0 && target >= total) target = total - 1;  // the largest p_mix is at least 1 / vocab
+  // total == 0 (no finite mass): no wave claims and the token stays vocab - 1
+  if (total > 0 && wbefore <= target && target < wbefore + wtot) {  // one wave: the intervals tile [0, total)
     const uint64_t local = target - wbefore;
     uint64_t rbase = 0, mr = 0, lane_mass = 0;
     int row = -1;
@@ -547,7 +565,7 @@ __global__ __launch_bounds__(kFuseThreads) void mix_fused_kernel(MixParams p) {
   __syncthreads();
   if (threadIdx.x == 0) {
     p.token[b] = sel_tok;
-    p.greedy[b] = bi;
+    p.greedy[b] = bi < p.vocab ? bi : p.vocab - 1;  // bi == vocab only for a row with no finite mass
     p.alpha[b] = n.alpha;
   }
 }

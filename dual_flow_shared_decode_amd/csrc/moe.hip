@@ -43,13 +43,18 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(MoeRouteParams
     r1s[e] = p.r1[(size_t)s * ne + e];
     r2s[e] = p.r2[(size_t)s * ne + e];
   }
-  if (t < kMoeMaxK) sel_sh[t] = 0;  // stays 0 only for logits that do not order (NaN)
+  if (t < kMoeMaxK) sel_sh[t] = 0;
   __syncthreads();
+  // Ranks on a key with NaN read as -inf, ties to the smaller index: a strict
+  // total order, so the ranks are a permutation and a selection never repeats
+  // an expert, whatever the logits hold.
   for (int e = t; e < ne; e += kRouteThreads) {
-    const float v = r1s[e];
+    const float v0 = r1s[e];
+    const float v = v0 == v0 ? v0 : -INFINITY;
     int rank = 0;
     for (int q = 0; q < ne; ++q) {
-      const float w = r1s[q];
+      const float w0 = r1s[q];
+      const float w = w0 == w0 ? w0 : -INFINITY;
       rank += (w > v) || (w == v && q < e);
     }
     if (rank < p.k2) sel_sh[rank] = e;

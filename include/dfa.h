@@ -370,7 +370,9 @@ DFA_API dfa_status dfa_decode_stack(const dfa_stack_desc* desc, const dfa_stack_
  *     greedy[b] = the smallest v with the largest p_mix(v);
  *     alpha[b]  = alpha.
  * logits1 (primary), logits2 (auxiliary): float32 [batch, vocab], row-major,
- * 16-byte aligned, finite. p_mix (optional, NULL to skip): float32
+ * 16-byte aligned, finite (a row with a non-finite logit returns token and
+ * greedy vocab - 1, or the first maximum where p_mix has one; never a token
+ * outside [0, vocab)). p_mix (optional, NULL to skip): float32
  * [batch, vocab], receives the mixture. u: float32 [batch]. token, greedy:
  * int32 [batch]; alpha: float32 [batch]. All device memory owned by the
  * caller; results independent of timing.

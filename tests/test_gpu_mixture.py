@@ -200,3 +200,26 @@ def test_dual_output_head(cfg):
     assert_close(g1, r1, TOL, "logits 1")
     assert_close(g2, r2, TOL, "logits 2")
     check_against_oracle(got, r1, r2, u, "head")
+
+
+@pytest.mark.parametrize("vocab", [32000, 40000])
+def test_non_finite_rows_return_the_defined_token(vocab):
+    """A row with a non-finite logit has no finite mixture mass: both paths (one launch up to
+    32768 tokens, chunked above) return token and greedy vocab - 1 for it, never an index
+    outside the vocabulary, and the other rows are untouched (regression: the chunked pick
+    once read an unset chunk index for such a row)."""
+    cfg = W.MIX.replace(batch=5, vocab=vocab)
+    l1, l2, u = W.make_mixture_case(cfg, 71 + vocab)
+    l1 = l1.copy()
+    l2 = l2.copy()
+    l1[1, 17] = np.nan          # primary NaN
+    l2[3, vocab - 5] = np.nan   # auxiliary NaN
+    l1[4, 123] = np.inf         # primary +inf
+    bad = np.array([1, 3, 4])
+    good = np.array([0, 2])
+    say(f"case mixture non-finite rows, vocab {vocab}")
+    got = run_mixture(l1, l2, u)
+    assert np.all(got["token"][bad] == vocab - 1), got["token"]
+    assert np.all(got["greedy"][bad] == vocab - 1), got["greedy"]
+    sub = {k: v[good] for k, v in got.items()}
+    check_against_oracle(sub, l1[good], l2[good], u[good], f"finite rows v{vocab}")

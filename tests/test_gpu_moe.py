@@ -215,3 +215,29 @@ def test_full_workload_sampled():
     assert_close(o1[rows], ref["out1"], TOL, "moe out1 (sampled)")
     assert_close(o2[rows], ref["out2"], TOL, "moe out2 (sampled)")
     assert_close(o1[rows] - case.res1[rows], ref["m1"], TOL, "moe m1 (sampled)")
+
+
+def test_route_with_nan_logits_selects_distinct_experts():
+    """NaN router logits (outside the header's contract) still give a valid routing: the ranking
+    reads NaN as -inf with ties to the smaller index, so every selection is k2 distinct experts in
+    range, the finite experts come first in descending order, and rows without NaN match the
+    oracle (regression: NaN once gave several experts one rank and repeated an expert)."""
+    rng = np.random.default_rng(404)
+    batch, experts, k1, k2 = 6, 12, 3, 8
+    r1 = rng.standard_normal((batch, experts), dtype=np.float32)
+    r2 = rng.standard_normal((batch, experts), dtype=np.float32)
+    r1[1, [0, 5]] = np.nan
+    r1[2, :] = np.nan
+    r1[4, 3:] = np.nan  # only 3 finite experts, fewer than k2
+    d = dfa.MoeDesc(batch=batch, hidden=128, mlp=128, num_experts=experts, k1=k1, k2=k2, x_exact_bf16=1)
+    say("case route with NaN router logits")
+    _, sel, _, _ = gpu_route(d, r1, r2)
+    for b in range(batch):
+        row = sel[b]
+        assert len(set(row.tolist())) == k2 and row.min() >= 0 and row.max() < experts, (b, row)
+        key = np.where(np.isnan(r1[b]), -np.inf, r1[b]).astype(np.float64)
+        order = sorted(range(experts), key=lambda e: (-key[e], e))
+        assert row.tolist() == order[:k2], (b, row, order[:k2])
+    clean = np.array([0, 3, 5])
+    ref = MO.route(r1[clean], r2[clean], k1, k2)
+    assert np.array_equal(sel[clean], ref["sel"])

@@ -18,7 +18,8 @@ STATUS = {0: "DFA_OK", 1: "DFA_ERR_NULL", 2: "DFA_ERR_SHAPE", 3: "DFA_ERR_DTYPE"
 
 # Every symbol include/dfa.h declares.
 EXPORTS = ["dfa_decode_attn_split_len", "dfa_decode_attn_num_splits", "dfa_decode_attn_workspace_size",
-           "dfa_decode_attn", "dfa_decode_attn_timed", "dfa_decode_attn_partials", "dfa_combine",
+           "dfa_decode_attn", "dfa_decode_attn_noalloc", "dfa_decode_attn_timed", "dfa_decode_attn_partials",
+           "dfa_combine",
            "dfa_dual_gemv_workspace_size", "dfa_dual_gemv", "dfa_pack_weight",
            "dfa_decode_layer_workspace_size", "dfa_decode_layer", "dfa_decode_stack_workspace_size",
            "dfa_decode_stack",
@@ -135,6 +136,7 @@ def lib() -> ctypes.CDLL:
             "dfa_decode_attn_num_splits": (ctypes.c_int32, [D]),
             "dfa_decode_attn_workspace_size": (ctypes.c_size_t, [D]),
             "dfa_decode_attn": (ctypes.c_int, [D, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P, _P, _P]),
+            "dfa_decode_attn_noalloc": (ctypes.c_int, [D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
             "dfa_decode_attn_timed": (ctypes.c_int, [D, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P, _P, _P,
                                                      ctypes.POINTER(KernelEvents)]),
             "dfa_decode_attn_partials": (ctypes.c_int, [D, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
@@ -219,6 +221,13 @@ def dfa_decode_attn(desc, q1, q2, a, k_cache, v_cache, block_table, ctx_lens, wo
     _check(lib().dfa_decode_attn(ctypes.byref(desc), _ptr(q1), _ptr(q2), _ptr(a), _ptr(k_cache),
                                  _ptr(v_cache), _ptr(block_table), _ptr(ctx_lens), _ptr(workspace),
                                  ws_bytes, _ptr(o1), _ptr(o2), _stream(stream)))
+
+
+def dfa_decode_attn_noalloc(desc, q1, q2, a, k_cache, v_cache, block_table, ctx_lens, o1, o2, stream=None):
+    """dfa_decode_attn without a workspace (the library's fixed device scratch holds the split records)."""
+    _check(lib().dfa_decode_attn_noalloc(ctypes.byref(desc), _ptr(q1), _ptr(q2), _ptr(a), _ptr(k_cache),
+                                         _ptr(v_cache), _ptr(block_table), _ptr(ctx_lens), _ptr(o1), _ptr(o2),
+                                         _stream(stream)))
 
 
 def _event_handle(ev):

@@ -174,18 +174,27 @@ dfa_status check_workspace(const dfa_attn_desc* d, int32_t split, const void* ws
   return DFA_OK;
 }
 
-dfa_status attn_impl(const dfa_attn_desc* desc, const void* q1, const void* q2, const float* a, const void* k_cache,
-                     const void* v_cache, const int32_t* block_table, const int32_t* ctx_lens, int32_t ctx_add,
-                     void* workspace, size_t ws_bytes, float* o1, float* o2, hipStream_t hs,
-                     const dfa_kernel_events* events) {
-  int32_t split = 0;
-  dfa_status st = validate_attn(desc, &split);
+// Every host-side check of an attention call except the workspace's.
+dfa_status check_attn_call(const dfa_attn_desc* desc, const void* q1, const void* q2, const float* a,
+                           const void* k_cache, const void* v_cache, const int32_t* block_table,
+                           const int32_t* ctx_lens, const float* o1, const float* o2, int32_t* split) {
+  dfa_status st = validate_attn(desc, split);
   if (st != DFA_OK) return st;
   st = check_tensors(desc, q1, q2, a, k_cache, v_cache, block_table, ctx_lens);
   if (st != DFA_OK) return st;
   if (!o1 || (desc->num_flows == 2 && !o2)) return fail(DFA_ERR_NULL, "o1 (and o2 with two flows) are required");
   if (!aligned16(o1) || (desc->num_flows == 2 && !aligned16(o2)))
     return fail(DFA_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
+  return DFA_OK;
+}
+
+dfa_status attn_impl(const dfa_attn_desc* desc, const void* q1, const void* q2, const float* a, const void* k_cache,
+                     const void* v_cache, const int32_t* block_table, const int32_t* ctx_lens, int32_t ctx_add,
+                     void* workspace, size_t ws_bytes, float* o1, float* o2, hipStream_t hs,
+                     const dfa_kernel_events* events) {
+  int32_t split = 0;
+  dfa_status st = check_attn_call(desc, q1, q2, a, k_cache, v_cache, block_table, ctx_lens, o1, o2, &split);
+  if (st != DFA_OK) return st;
   const int32_t ns = num_splits(desc, split);
   if (ns > 1) {
     st = check_workspace(desc, split, workspace, ws_bytes);
@@ -465,6 +474,19 @@ dfa_status plan_layer(const dfa_layer_desc* d, LayerPlan* lp) {
 }
 
 }  // namespace
+
+namespace dfa {
+dfa_status report_error(dfa_status st, const std::string& msg) { return fail(st, msg); }
+
+dfa_status attn_host_checks(const dfa_attn_desc* desc, const void* q1, const void* q2, const float* a,
+                            const void* k_cache, const void* v_cache, const int32_t* block_table,
+                            const int32_t* ctx_lens, const float* o1, const float* o2, int32_t* n_splits) {
+  int32_t split = 0;
+  const dfa_status st = check_attn_call(desc, q1, q2, a, k_cache, v_cache, block_table, ctx_lens, o1, o2, &split);
+  if (st == DFA_OK && n_splits) *n_splits = num_splits(desc, split);
+  return st;
+}
+}  // namespace dfa
 
 extern "C" {
 

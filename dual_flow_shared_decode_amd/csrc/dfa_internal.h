@@ -6,6 +6,10 @@
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
 
+#include <string>
+
+#include "../../include/dfa.h"
+
 namespace dfa {
 
 constexpr int kWaves = 4;          // waves per attention workgroup
@@ -49,6 +53,15 @@ struct KernelEvents {
   hipEvent_t start = nullptr;
   hipEvent_t stop = nullptr;
 };
+
+// Sets the calling thread's error message (dfa_last_error) and returns st.
+dfa_status report_error(dfa_status st, const std::string& msg);
+
+// The host-side checks of dfa_decode_attn short of the workspace (descriptor,
+// pointers, alignment); on success *n_splits is the split count of its plan.
+dfa_status attn_host_checks(const dfa_attn_desc* desc, const void* q1, const void* q2, const float* a,
+                            const void* k_cache, const void* v_cache, const int32_t* block_table,
+                            const int32_t* ctx_lens, const float* o1, const float* o2, int32_t* n_splits);
 
 // Launchers return the launch status (hipGetLastError after the launch).
 hipError_t launch_attn_bf16(const AttnParams& p, int head_dim, int rows_padded, hipStream_t s, const KernelEvents& ev);

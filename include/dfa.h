@@ -22,7 +22,8 @@
  *  - All tensor pointers are DEVICE pointers (hipMalloc'd or equivalent) and
  *    must be 16-byte aligned. The caller owns every buffer; the library
  *    allocates nothing, keeps no pointer after returning, and holds no global
- *    state besides a per-thread error message, so calls are thread-safe.
+ *    state besides a per-thread error message (and the fixed device scratch
+ *    of dfa_decode_attn_noalloc), so calls are thread-safe.
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *    Work is enqueued asynchronously; results are valid once the stream has
  *    been synchronised. Calls on one stream execute in order.
@@ -139,6 +140,25 @@ DFA_API dfa_status dfa_decode_attn(const dfa_attn_desc* desc, const void* q1, co
                            const int32_t* block_table, const int32_t* ctx_lens,
                            void* workspace, size_t workspace_bytes, float* o1, float* o2,
                            void* stream);
+
+/*
+ * dfa_decode_attn for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, split plan, kernels and results as dfa_decode_attn, without
+ * the workspace: the split records live in a device array of the library,
+ * DFA_NOALLOC_SCRATCH_BYTES (8 MiB) per GPU, held until the process ends. Its
+ * device address is looked up on the first call on each GPU (with that GPU
+ * current); no call allocates or frees memory.
+ * Limit: dfa_decode_attn_workspace_size(desc) <= DFA_NOALLOC_SCRATCH_BYTES
+ * whenever more than one split runs (checked on the host: DFA_ERR_WORKSPACE,
+ * nothing enqueued). Calls on one GPU share the array: calls that overlap in
+ * time (on different streams) race and must not be issued.
+ */
+#define DFA_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+DFA_API dfa_status dfa_decode_attn_noalloc(const dfa_attn_desc* desc, const void* q1, const void* q2,
+                                           const float* a, const void* k_cache, const void* v_cache,
+                                           const int32_t* block_table, const int32_t* ctx_lens, float* o1,
+                                           float* o2, void* stream);
 
 /*
  * Optional events for measuring the attention kernel itself: hipEvent_t

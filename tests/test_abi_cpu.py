@@ -303,3 +303,28 @@ def test_stack_validation():
         _lib._check(_lib.lib().dfa_decode_stack(ctypes.byref(dfa.StackDesc(**ok)), arr, None, None, FAKE, FAKE, FAKE,
                                                 FAKE, FAKE, FAKE, FAKE, 1 << 30, None))
     assert _lib.STATUS[e.value.status] == "DFA_ERR_NULL"
+
+
+def _call_noalloc(d, **ptrs):
+    p = dict(q1=FAKE, q2=FAKE, a=FAKE, k=FAKE, v=FAKE, table=FAKE, ctx=FAKE, o1=FAKE, o2=FAKE)
+    p.update(ptrs)
+    st = _lib.lib().dfa_decode_attn_noalloc(ctypes.byref(d), p["q1"], p["q2"], p["a"], p["k"], p["v"], p["table"],
+                                            p["ctx"], p["o1"], p["o2"], None)
+    _lib._check(st)
+
+
+def test_noalloc_validates_like_decode_attn_and_checks_its_scratch_limit():
+    # an invalid descriptor: the same status as dfa_decode_attn, nothing reaches the GPU
+    with pytest.raises(dfa.DfaError) as e:
+        _call_noalloc(c2_desc(num_flows=3))
+    assert _lib.STATUS[e.value.status] == "DFA_ERR_SHAPE"
+    with pytest.raises(dfa.DfaError) as e:
+        _call_noalloc(c2_desc(split_len=512), q1=None)
+    assert _lib.STATUS[e.value.status] == "DFA_ERR_NULL"
+    # records beyond the fixed 8 MiB scratch: refused on the host before any device call
+    d = c2_desc(batch=64, num_q_heads=64, block_size=4096, max_blocks_per_seq=1, num_blocks=64, split_len=256)
+    assert dfa.dfa_decode_attn_workspace_size(d) > 8 << 20
+    with pytest.raises(dfa.DfaError) as e:
+        _call_noalloc(d)
+    assert _lib.STATUS[e.value.status] == "DFA_ERR_WORKSPACE"
+    assert "scratch" in _lib.lib().dfa_last_error().decode()

@@ -8,7 +8,8 @@ ctx_lens = prompt lengths) gives the primary's last prefill row for flow 1 and t
 auxiliary output for flow 2. Cases: 1, 2, 4, 8 and 16 query heads per kv head, head_dim 64 and 128,
 ragged prompts (lengths 0, 1, partial tiles, several query blocks and chunks), shuffled paged caches
 with 16-, 32- and 64-position blocks, the full workload (4 prompts of 4096 tokens, 32/8 heads of
-128) on sampled rows, and the longest prompt the kernel takes (2048 cache blocks).
+128: every row of the first prompt, sampled rows of the others), and the longest prompt the kernel
+takes (2048 cache blocks).
 """
 import numpy as np
 import pytest
@@ -119,7 +120,7 @@ def test_first_auxiliary_step_after_prefill():
     assert_close(o1, rows, TOL, "first step o1 vs the prefill's last row")
 
 
-def test_full_workload_sampled():
+def test_full_workload():
     cfg = W.PREFILL
     say("case prefill full size: generating inputs")
     case = W.make_prefill_case(cfg, W.SEEDS["prefill"])
@@ -130,8 +131,15 @@ def test_full_workload_sampled():
                                        case.block_size)
     assert np.array_equal(cache_bits(t["k_cache"]), ref_cache["k_cache"])
     assert np.array_equal(cache_bits(t["v_cache"]), ref_cache["v_cache"])
-    # sampled rows: the attention of position t over [0, t] is the decode oracle with t + 1 cached positions
-    for b, pos in ((0, 0), (1, 1), (2, 1000), (3, 4095), (0, 2047), (3, 31)):
+    # every row of the first prompt (4096 positions, 32 heads) against the causal oracle (~10 s)
+    say("case prefill full size: causal oracle over every row of prompt 0")
+    ref0 = PF.causal_attention(case.q[:1], case.k[:1], case.v[:1], case.lens[:1], num_kv_heads=cfg.num_kv_heads,
+                               scale=cfg.scale)
+    n0 = int(case.lens[0])
+    assert_close(o[0, :n0], ref0[0, :n0], TOL, "prefill full prompt 0 (every row)")
+    # rows of the other prompts: the attention of position t over [0, t] is the decode oracle with t + 1
+    # cached positions
+    for b, pos in ((1, 1), (2, 1000), (3, 4095), (3, 31)):
         lens = np.array([pos + 1], dtype=np.int32)
         ref = A.decode_attention(case.q[b, pos][None], None, None, ref_cache["k_cache"], ref_cache["v_cache"],
                                  case.block_table[b:b + 1], lens, num_kv_heads=cfg.num_kv_heads, scale=cfg.scale,

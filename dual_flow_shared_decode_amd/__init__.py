@@ -5,7 +5,7 @@ csrc/, built by ``build``). This package is its ctypes binding (``_lib``: the
 same names as the C entry points, argument marshalling only). PyTorch serves
 only for device memory, streams and events.
 """
-from ._lib import (DFA_BF16, DFA_EPI_KV_APPEND, DFA_ROPE_HALF, DFA_ROPE_INTERLEAVED, DFA_ROPE_NONE, DFA_EPI_NONE, DFA_EPI_RESIDUAL,  # noqa: F401
+from ._lib import (DFA_TABLE_BAD_BLOCK, DFA_TABLE_BAD_LEN, dfa_check_kv_table, DFA_BF16, DFA_EPI_KV_APPEND, DFA_ROPE_HALF, DFA_ROPE_INTERLEAVED, DFA_ROPE_NONE, DFA_EPI_NONE, DFA_EPI_RESIDUAL,  # noqa: F401
                    DFA_EPI_RESIDUAL_COUPLED, DFA_EPI_SWIGLU, DFA_F32, AttnDesc, DfaError, GemvDesc,
                    KernelEvents, KvTarget, LayerDesc, LayerWeights, MixtureDesc, MoeDesc, PrefillDesc, StackDesc, StackLayer, dfa_combine, dfa_decode_attn,
                    dfa_decode_attn_noalloc, dfa_decode_attn_num_splits, dfa_decode_layer, dfa_decode_layer_workspace_size,

@@ -19,7 +19,7 @@ STATUS = {0: "DFA_OK", 1: "DFA_ERR_NULL", 2: "DFA_ERR_SHAPE", 3: "DFA_ERR_DTYPE"
 # Every symbol include/dfa.h declares.
 EXPORTS = ["dfa_decode_attn_split_len", "dfa_decode_attn_num_splits", "dfa_decode_attn_workspace_size",
            "dfa_decode_attn", "dfa_decode_attn_noalloc", "dfa_decode_attn_timed", "dfa_decode_attn_partials",
-           "dfa_combine",
+           "dfa_combine", "dfa_check_kv_table",
            "dfa_dual_gemv_workspace_size", "dfa_dual_gemv", "dfa_pack_weight",
            "dfa_decode_layer_workspace_size", "dfa_decode_layer", "dfa_decode_stack_workspace_size",
            "dfa_decode_stack",
@@ -137,6 +137,7 @@ def lib() -> ctypes.CDLL:
             "dfa_decode_attn_workspace_size": (ctypes.c_size_t, [D]),
             "dfa_decode_attn": (ctypes.c_int, [D, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P, _P, _P]),
             "dfa_decode_attn_noalloc": (ctypes.c_int, [D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+            "dfa_check_kv_table": (ctypes.c_int, [D, _P, _P, ctypes.c_int32, _P, _P]),
             "dfa_decode_attn_timed": (ctypes.c_int, [D, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P, _P, _P,
                                                      ctypes.POINTER(KernelEvents)]),
             "dfa_decode_attn_partials": (ctypes.c_int, [D, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
@@ -228,6 +229,16 @@ def dfa_decode_attn_noalloc(desc, q1, q2, a, k_cache, v_cache, block_table, ctx_
     _check(lib().dfa_decode_attn_noalloc(ctypes.byref(desc), _ptr(q1), _ptr(q2), _ptr(a), _ptr(k_cache),
                                          _ptr(v_cache), _ptr(block_table), _ptr(ctx_lens), _ptr(o1), _ptr(o2),
                                          _stream(stream)))
+
+
+DFA_TABLE_BAD_LEN, DFA_TABLE_BAD_BLOCK = 1, 2
+
+
+def dfa_check_kv_table(desc, block_table, ctx_lens, flags, ctx_add=0, stream=None):
+    """Device-side check of the lengths and block-table entries a decode call reads; writes flags
+    (int32 tensor [2], viewed as uint32): the DFA_TABLE_BAD_* bits and the first offending sequence."""
+    _check(lib().dfa_check_kv_table(ctypes.byref(desc), _ptr(block_table), _ptr(ctx_lens), ctx_add, _ptr(flags),
+                                    _stream(stream)))
 
 
 def _event_handle(ev):

@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdfa.so")
-SOURCES = ["abi.cpp", "attn_bf16.hip", "attn_f32.hip", "combine.hip", "gemv.hip", "measure.hip", "mixture.hip", "moe.hip", "noalloc.hip", "norm.hip", "prefill.hip"]
+SOURCES = ["abi.cpp", "attn_bf16.hip", "attn_f32.hip", "combine.hip", "debug.hip", "gemv.hip", "measure.hip", "mixture.hip", "moe.hip", "noalloc.hip", "norm.hip", "prefill.hip"]
 ARCH = os.environ.get("DFA_OFFLOAD_ARCH", "gfx950")
 # Packed fp32 VALU ops are disabled: the compiler would otherwise form them from
 # plain float code. MFMA accumulators are kept in ordinary VGPRs: the kernels

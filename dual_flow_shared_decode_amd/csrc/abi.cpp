@@ -1058,6 +1058,26 @@ const char* dfa_status_string(dfa_status s) {
   return "unknown status";
 }
 
+dfa_status dfa_check_kv_table(const dfa_attn_desc* desc, const int32_t* block_table, const int32_t* ctx_lens,
+                              int32_t ctx_add, uint32_t* flags, void* stream) {
+  try {
+    int32_t split = 0;
+    const dfa_status st = validate_attn(desc, &split);
+    if (st != DFA_OK) return st;
+    if (!block_table || !ctx_lens || !flags) return fail(DFA_ERR_NULL, "block_table, ctx_lens and flags are required");
+    if (!aligned16(block_table) || !aligned16(ctx_lens) || !aligned16(flags))
+      return fail(DFA_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
+    if (ctx_add < 0 || ctx_add > 1) return fail(DFA_ERR_SHAPE, "ctx_add must be 0 or 1");
+    dfa::TableCheckParams p{block_table, ctx_lens, flags, desc->batch, desc->max_blocks_per_seq, desc->num_blocks,
+                            desc->max_ctx_len, desc->block_size, ctx_add};
+    const hipError_t e = dfa::launch_check_table(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(DFA_ERR_HIP, std::string("table check launch: ") + hipGetErrorString(e));
+    return DFA_OK;
+  } catch (...) {
+    return fail(DFA_ERR_HIP, "unexpected host exception");
+  }
+}
+
 const char* dfa_last_error(void) { return g_last_error.c_str(); }
 
 int32_t dfa_version(void) { return 100; }

@@ -142,6 +142,30 @@ DFA_API dfa_status dfa_decode_attn(const dfa_attn_desc* desc, const void* q1, co
                            void* stream);
 
 /*
+ * Debug aid: checks on the device what a dfa_decode_attn call with `desc`
+ * would read of ctx_lens and block_table. The attention kernels clamp a
+ * length to [0, max_ctx_len] and a block id to [0, num_blocks), so that no
+ * access leaves the buffers; a corrupt table is then read silently as the
+ * nearest valid block. This call reports such entries instead: one small
+ * kernel on `stream` writes
+ *     flags[0] = DFA_TABLE_BAD_LEN   if some ctx_lens[b] + ctx_add lies outside
+ *                                    [0, max_ctx_len],
+ *              | DFA_TABLE_BAD_BLOCK if some entry among the first
+ *                                    ceil(len_b / block_size) of row b (len_b
+ *                                    the clamped length) lies outside
+ *                                    [0, num_blocks);
+ *     flags[1] = the smallest offending sequence index, or 0xFFFFFFFF.
+ * flags: device uint32 [2] (16-byte aligned), written by the call (no
+ * clearing needed). ctx_add: 0 as for dfa_decode_attn, 1 for the layer step
+ * (which attends the just-appended position). Scans every row in one
+ * workgroup: meant for debugging, not for the hot path.
+ */
+#define DFA_TABLE_BAD_LEN 1u
+#define DFA_TABLE_BAD_BLOCK 2u
+DFA_API dfa_status dfa_check_kv_table(const dfa_attn_desc* desc, const int32_t* block_table,
+                                      const int32_t* ctx_lens, int32_t ctx_add, uint32_t* flags, void* stream);
+
+/*
  * dfa_decode_attn for callers that cannot allocate device memory: code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
  * Same arguments, split plan, kernels and results as dfa_decode_attn, without

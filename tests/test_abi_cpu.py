@@ -328,3 +328,19 @@ def test_noalloc_validates_like_decode_attn_and_checks_its_scratch_limit():
         _call_noalloc(d)
     assert _lib.STATUS[e.value.status] == "DFA_ERR_WORKSPACE"
     assert "scratch" in _lib.lib().dfa_last_error().decode()
+
+
+def test_table_check_validation():
+    """dfa_check_kv_table: the descriptor's checks, then its own (pointers, alignment, ctx_add), all on the
+    host before any device call."""
+    call = lambda d, table=FAKE, ctx=FAKE, add=0, flags=FAKE: _lib._check(
+        _lib.lib().dfa_check_kv_table(ctypes.byref(d), table, ctx, add, flags, None))
+    for kw, args, status in ((dict(num_flows=3), {}, "DFA_ERR_SHAPE"),
+                             ({}, dict(flags=None), "DFA_ERR_NULL"),
+                             ({}, dict(table=None), "DFA_ERR_NULL"),
+                             ({}, dict(ctx=FAKE + 4), "DFA_ERR_ALIGNMENT"),
+                             ({}, dict(add=2), "DFA_ERR_SHAPE"),
+                             ({}, dict(add=-1), "DFA_ERR_SHAPE")):
+        with pytest.raises(dfa.DfaError) as e:
+            call(c2_desc(**kw), **args)
+        assert _lib.STATUS[e.value.status] == status, (kw, args)

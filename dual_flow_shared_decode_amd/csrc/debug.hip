@@ -5,7 +5,7 @@
 // nearest valid block. This kernel reports such entries instead.
 #include <hip/hip_runtime.h>
 
-#include "dfa_internal.h"
+#include "ops_internal.h"
 
 namespace dfa {
 

@@ -47,15 +47,6 @@ struct CombineParams {
   int32_t batch, hq, flows, n_splits;
 };
 
-// Device-side check of a decode call's lengths and block-table entries.
-enum : uint32_t { kTableBadLen = 1u, kTableBadBlock = 2u };
-struct TableCheckParams {
-  const int32_t* table;
-  const int32_t* ctx;
-  uint32_t* flags;  // [0]: bits, [1]: first offending sequence (0xFFFFFFFF: none)
-  int32_t batch, max_blocks, num_blocks, max_ctx, block_size, ctx_add;
-};
-
 // Optional events recorded by the runtime at the start and end of a kernel's
 // own dispatch (no extra commands on the stream).
 struct KernelEvents {
@@ -77,7 +68,6 @@ hipError_t launch_attn_bf16(const AttnParams& p, int head_dim, int rows_padded, 
 hipError_t launch_attn_f32(const AttnParams& p, int head_dim, hipStream_t s, const KernelEvents& ev);
 hipError_t launch_combine(const CombineParams& p, int head_dim, hipStream_t s);
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s);
-hipError_t launch_check_table(const TableCheckParams& p, hipStream_t s);
 size_t stream_read_threads();
 
 }  // namespace dfa

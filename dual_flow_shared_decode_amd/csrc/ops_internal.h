@@ -1,7 +1,8 @@
 // Internal interface between the host-side ABI (abi.cpp) and the launchers of
 // the weight-streaming and output-head kernels (gemv.hip, mixture.hip,
-// moe.hip). Plain structs passed by value to the kernels. The attention
-// kernels do not include this file.
+// moe.hip, prefill.hip, norm.hip) and of the debug check (debug.hip). Plain
+// structs passed by value to the kernels. The attention kernels do not
+// include this file.
 #pragma once
 
 #include <hip/hip_runtime_api.h>
@@ -134,6 +135,15 @@ struct NormParams {
   float eps;
 };
 
+// Debug aid: device-side check of a decode call's lengths and block-table entries.
+enum : uint32_t { kTableBadLen = 1u, kTableBadBlock = 2u };
+struct TableCheckParams {
+  const int32_t* table;
+  const int32_t* ctx;
+  uint32_t* flags;  // [0]: bits, [1]: first offending sequence (0xFFFFFFFF: none)
+  int32_t batch, max_blocks, num_blocks, max_ctx, block_size, ctx_add;
+};
+
 // Launchers return the launch status (hipGetLastError after the launch).
 hipError_t launch_rmsnorm(const NormParams& p, hipStream_t s);
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, hipStream_t s);
@@ -146,5 +156,6 @@ hipError_t launch_mixture(const MixParams& p, hipStream_t s);
 hipError_t launch_moe_route(const MoeRouteParams& p, hipStream_t s);
 hipError_t launch_moe_combine(const MoeCombineParams& p, hipStream_t s);
 size_t mixture_chunks(int vocab);
+hipError_t launch_check_table(const TableCheckParams& p, hipStream_t s);
 
 }  // namespace dfa

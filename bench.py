@@ -27,7 +27,7 @@ lengths in a shuffled paged cache), and the CPU oracle's rate on a bounded
 sample (context only).
 
     python bench.py [--steps K] [--warmup W] [--flows 1|2]
-                    [--config c2|c3|c4|c5|head|moe|prefill|stack]
+                    [--config c2|c3|c4|c5|gemv|head|moe|prefill|stack]
 """
 import argparse
 import hashlib
@@ -202,6 +202,102 @@ def bench_layer(args):
                                  "batch": cfg.batch},
                       "achieved_gbps": gbps, "hbm_peak_gbps": HBM_PEAK_GBPS, "frac_of_peak": gbps / HBM_PEAK_GBPS,
                       "algorithmic_bytes_per_step": nbytes}), flush=True)
+
+
+GEMV_SHAPES = (  # the dense layer's weight streams at hidden 4096, 32/8 heads of 128, SwiGLU 14336
+    ("qkv", 6144, 4096, "none", 1),            # [Wq; Wk; Wv], exact bf16 inputs (the layer's first GEMV)
+    ("wo", 4096, 4096, "residual", 0),
+    ("gate_up", 14336, 4096, "swiglu", 0),     # the SwiGLU pair: two 14336 x 4096 matrices
+    ("down", 4096, 14336, "residual_coupled", 0),
+)
+
+
+def bench_gemv(args):
+    """dfa_dual_gemv alone on the four weight streams of the layer workload (batch 32), one or two
+    flows: each shape's launches (GEMV and, when split, its reduction) timed back to back, with
+    enough copies of the weights rotated that the last-level cache never serves them. For HBM
+    counter runs: the weights must be read once whatever the number of flows."""
+    import torch
+
+    import dual_flow_shared_decode_amd as dfa
+
+    batch, flows = 32, args.flows
+    epi = {"none": dfa.DFA_EPI_NONE, "residual": dfa.DFA_EPI_RESIDUAL, "swiglu": dfa.DFA_EPI_SWIGLU,
+           "residual_coupled": dfa.DFA_EPI_RESIDUAL_COUPLED if flows == 2 else dfa.DFA_EPI_RESIDUAL}
+    stream = torch.cuda.current_stream()
+    gen = torch.Generator(device="cuda").manual_seed(2024)
+    shapes, total_w, total_ms = {}, 0, 0.0
+    for name, n, k, kind, exact in GEMV_SHAPES:
+        mats = 2 if kind == "swiglu" else 1
+        wbytes = mats * n * k * 2
+        copies = max(1, -(-(768 << 20) // wbytes))
+        log(f"gemv {name}: {n} x {k}{' x 2' if mats == 2 else ''}, {flows} flow(s), {copies} weight copies")
+        ws_ = []
+        for _ in range(copies):  # random bf16 weights (a layout change only: values do not matter here)
+            pair = []
+            for _ in range(mats):
+                w = (torch.randn((n, k), device="cuda", generator=gen) * 0.02).to(torch.bfloat16).view(torch.int16)
+                wt = torch.empty_like(w)
+                dfa.dfa_pack_weight(w, wt, n, k, stream)
+                pair.append(wt)
+                del w
+            ws_.append(pair)
+        x = [torch.randn((batch, k), device="cuda", generator=gen) for _ in range(flows)]
+        if exact:
+            x = [t.to(torch.bfloat16).float() for t in x]
+        res = [torch.randn((batch, n), device="cuda", generator=gen) for _ in range(flows)]
+        couple = torch.randn(n, device="cuda", generator=gen) * 0.1 if flows == 2 and kind != "none" else None
+        y = [torch.empty((batch, n), device="cuda") for _ in range(flows)]
+        d = dfa.GemvDesc(batch=batch, n=n, k=k, num_flows=flows, epilogue=epi[kind], x_exact_bf16=exact, k_split=0,
+                         rows_per_wg=0)
+        wsb = dfa.dfa_dual_gemv_workspace_size(d)
+        work = torch.empty(max(wsb // 4, 4), dtype=torch.float32, device="cuda") if wsb else None
+        two = flows == 2
+        use_res = kind in ("residual", "residual_coupled")
+
+        def step(i):
+            w = ws_[i % copies]
+            dfa.dfa_dual_gemv(d, w[0], w[1] if mats == 2 else None, x[0], x[1] if two else None, couple,
+                              res[0] if use_res else None, res[1] if (use_res and two) else None, y[0],
+                              y[1] if two else None, None, work, stream)
+        for i in range(max(args.warmup, 2 * copies)):
+            step(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(args.steps):
+            step(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        act = 4 * batch * flows * (k + n * (1 + (1 if use_res else 0)))
+        gbps = (wbytes + act) / (ms * 1e-3) / 1e9
+        shapes[name] = {"n": n, "k": k, "matrices": mats, "epilogue": kind, "us": ms * 1e3, "weight_bytes": wbytes,
+                        "algorithmic_bytes": wbytes + act, "gbps": gbps, "frac": gbps / HBM_PEAK_GBPS,
+                        "k_split": int(wsb > 0)}
+        log(f"gemv {name}: {ms * 1e3:.1f} us per launch, {gbps:.0f} GB/s")
+        total_w += wbytes + act
+        total_ms += ms
+        del ws_, x, res, y, work
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    gbps = total_w / (total_ms * 1e-3) / 1e9
+    rec = {"metric": "dual GEMV on the layer's weight streams: achieved HBM GB/s vs peak", "value": gbps,
+           "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": total_ms,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": f"dual GEMV, batch 32, {flows} flow(s): [Wq; Wk; Wv] 6144 x 4096, Wo 4096 x 4096, "
+                                  "SwiGLU pair 2 x 14336 x 4096, down 4096 x 14336", "batch": batch,
+                      "num_flows": flows},
+           "frac_of_peak": gbps / HBM_PEAK_GBPS, "shapes": shapes}
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        rec["copy_calibration_bytes"] = n
+    print(json.dumps(rec), flush=True)
 
 
 def bench_head(args):
@@ -658,14 +754,16 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="c4", choices=["c2", "c3", "c4", "c5", "head", "moe", "prefill", "stack"],
+    ap.add_argument("--config", default="c4",
+                    choices=["c2", "c3", "c4", "c5", "gemv", "head", "moe", "prefill", "stack"],
                     help="c4 (default): the largest attention workload, the headline; c2, c3: the other attention "
-                         "workloads alone; c5: a whole layer step; head: the dual output head and mixture sampling; "
+                         "workloads alone; c5: a whole layer step; gemv: the dual GEMV on the layer's four weight "
+                         "streams; head: the dual output head and mixture sampling; "
                          "moe: the MoE FFN with router replay; prefill: the primary-only prefill and the first "
                          "auxiliary step; stack: 4 layers with RMSNorm and rotary embeddings in a HIP graph")
     ap.add_argument("--flows", type=int, default=2, choices=[1, 2],
-                    help="flows of the timed attention steps (1: the single-flow run of the same kernel, for "
-                         "counter comparisons)")
+                    help="flows of the timed attention (or gemv) steps (1: the single-flow run of the same "
+                         "kernels, for counter comparisons)")
     ap.add_argument("--split", type=int, default=0, help="positions per split (0: library choice)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -684,7 +782,8 @@ def main():
     import dual_flow_shared_decode_amd as dfa
 
     torch.cuda.set_device(0)
-    other = {"c5": bench_layer, "head": bench_head, "moe": bench_moe, "prefill": bench_prefill, "stack": bench_stack}
+    other = {"c5": bench_layer, "gemv": bench_gemv, "head": bench_head, "moe": bench_moe, "prefill": bench_prefill,
+             "stack": bench_stack}
     if args.config in other:
         other[args.config](args)
         return

@@ -23,8 +23,9 @@ the committed counter summary of the workload (both flows and one flow), the
 measured stream-read ceiling, the auxiliary flow's increment over a one-flow
 run of the same kernel, the same figures for the two other attention
 workloads (`other_workloads`: batch 16 x 4096 positions; batch 64 with ragged
-lengths in a shuffled paged cache), and the CPU oracle's rate on a bounded
-sample (context only).
+lengths in a shuffled paged cache) and of a model with 16 query heads per kv
+head (128/8 heads, batch 8 x 16384 positions: 32 query rows per kv head with
+both flows), and the CPU oracle's rate on a bounded sample (context only).
 
     python bench.py [--steps K] [--warmup W] [--flows 1|2]
                     [--config c2|c3|c4|c5|gemv|head|moe|prefill|stack]
@@ -728,8 +729,10 @@ def attn_measure(name, args, flows=2, one_flow=True, log_prefix=""):
 
 def kernel_name_of(cfg, flows):
     rows = cfg.num_q_heads // cfg.num_kv_heads * flows
-    return (f"attn_bf16_kernel<{cfg.head_dim}, {8 if rows <= 8 else 16}, false>" if cfg.dtype == "bf16"
-            else f"attn_f32_kernel<{cfg.head_dim}>")
+    if cfg.dtype != "bf16":
+        return f"attn_f32_kernel<{cfg.head_dim}>"
+    return (f"attn_bf16_kernel<{cfg.head_dim}, {8 if rows <= 8 else 16}, false, 1>" if rows <= 16
+            else f"attn_bf16_kernel<{cfg.head_dim}, 16, false, 2>")
 
 
 def summary_of(m):
@@ -755,9 +758,10 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="c4",
-                    choices=["c2", "c3", "c4", "c5", "gemv", "head", "moe", "prefill", "stack"],
+                    choices=["c2", "c3", "c4", "g16", "c5", "gemv", "head", "moe", "prefill", "stack"],
                     help="c4 (default): the largest attention workload, the headline; c2, c3: the other attention "
-                         "workloads alone; c5: a whole layer step; gemv: the dual GEMV on the layer's four weight "
+                         "workloads alone; g16: attention with 16 query heads per kv head (128/8 heads, 32 rows per kv head "
+                         "with both flows), batch 8 x 16384 positions; c5: a whole layer step; gemv: the dual GEMV on the layer's four weight "
                          "streams; head: the dual output head and mixture sampling; "
                          "moe: the MoE FFN with router replay; prefill: the primary-only prefill and the first "
                          "auxiliary step; stack: 4 layers with RMSNorm and rotary embeddings in a HIP graph")
@@ -854,9 +858,9 @@ def main():
         rec["frac_of_stream_read"] = kern_gbps / ceil_gbps
         del buf
         log(f"stream-read ceiling {ceil_gbps:.0f} GB/s")
-        # the other attention workloads of the metric, timed the same way (the headline is the largest)
+        # the other attention workloads, timed the same way
         rec["other_workloads"] = {}
-        for name in ("c2", "c3", "c4"):
+        for name in ("c2", "c3", "c4", "g16"):
             if name == cfg.name:
                 continue
             rec["other_workloads"][name] = summary_of(attn_measure(name, args, flows=2, one_flow=True,

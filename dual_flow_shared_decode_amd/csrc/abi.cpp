@@ -57,8 +57,8 @@ dfa_status validate_attn(const dfa_attn_desc* d, int32_t* split_out) {
   if (d->head_dim < 1) return fail(DFA_ERR_SHAPE, "head_dim must be positive");
   if (d->head_dim != 64 && d->head_dim != 128) return fail(DFA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
   const int64_t group = d->num_q_heads / d->num_kv_heads;
-  if (group * d->num_flows > dfa::kMaxRows)
-    return fail(DFA_ERR_UNSUPPORTED, "(num_q_heads / num_kv_heads) * num_flows must be <= 16");
+  if (group * d->num_flows > dfa::kMaxRowsBf16)
+    return fail(DFA_ERR_UNSUPPORTED, "(num_q_heads / num_kv_heads) * num_flows must be <= 32");
   if (!is_pow2(d->block_size) || d->block_size < 16)
     return fail(DFA_ERR_SHAPE, "block_size must be a power of two >= 16");
   if (d->max_blocks_per_seq < 1) return fail(DFA_ERR_SHAPE, "max_blocks_per_seq must be >= 1");
@@ -73,6 +73,8 @@ dfa_status validate_attn(const dfa_attn_desc* d, int32_t* split_out) {
   const bool q_ok = d->q_dtype == DFA_BF16 || d->q_dtype == DFA_F32;
   if (!(kv_bf16 || kv_f32) || !q_ok) return fail(DFA_ERR_DTYPE, "unknown dtype");
   if (kv_f32 && d->q_dtype != DFA_F32) return fail(DFA_ERR_DTYPE, "a float32 cache needs float32 queries");
+  if (kv_f32 && group * d->num_flows > dfa::kMaxRows)
+    return fail(DFA_ERR_UNSUPPORTED, "with a float32 cache, (num_q_heads / num_kv_heads) * num_flows must be <= 16");
   int64_t split = d->split_len > 0 ? d->split_len : auto_split_len(d);
   // the block-table slice of one split must fit the staging buffer
   if ((split - 1) / d->block_size + 2 > dfa::kMaxTableSlice) {
@@ -146,7 +148,7 @@ dfa_status launch_split_stage(const dfa_attn_desc* d, const dfa::AttnParams& p, 
     e = dfa::launch_attn_f32(p, d->head_dim, st, ev);
   } else {
     const int rows = (d->num_q_heads / d->num_kv_heads) * d->num_flows;
-    e = dfa::launch_attn_bf16(p, d->head_dim, rows <= 8 ? 8 : 16, st, ev);
+    e = dfa::launch_attn_bf16(p, d->head_dim, rows <= 8 ? 8 : (rows <= 16 ? 16 : 32), st, ev);
   }
   if (e != hipSuccess) return fail(DFA_ERR_HIP, std::string("attention launch: ") + hipGetErrorString(e));
   return DFA_OK;
@@ -220,13 +222,13 @@ dfa_status attn_impl(const dfa_attn_desc* desc, const void* q1, const void* q2, 
 // ------------------------------------------------------------------ dual GEMV
 struct GemvPlan {
   int32_t cbf, m_pad, k_split, k_range, mats, rows_per_wg;
+  int32_t slice;  // sequences per launch: the kernels take at most 64 activation rows (both flows)
 };
 
 dfa_status validate_gemv(const dfa_gemv_desc* d, GemvPlan* plan) {
   if (!d) return fail(DFA_ERR_NULL, "desc is NULL");
   if (d->num_flows != 1 && d->num_flows != 2) return fail(DFA_ERR_SHAPE, "num_flows must be 1 or 2");
-  if (d->batch < 1 || d->batch * d->num_flows > 64)
-    return fail(DFA_ERR_UNSUPPORTED, "batch must be in [1, 32] with two flows, [1, 64] with one");
+  if (d->batch < 1 || d->batch > 65535) return fail(DFA_ERR_SHAPE, "batch must be in [1, 65535]");
   if (d->n < 64 || d->n % 64 != 0) return fail(DFA_ERR_SHAPE, "n must be a positive multiple of 64");
   if (d->k < 128 || d->k % 128 != 0) return fail(DFA_ERR_SHAPE, "k must be a positive multiple of 128");
   if (d->epilogue < DFA_EPI_NONE || d->epilogue > DFA_EPI_KV_APPEND) return fail(DFA_ERR_SHAPE, "unknown epilogue");
@@ -237,7 +239,11 @@ dfa_status validate_gemv(const dfa_gemv_desc* d, GemvPlan* plan) {
     return fail(DFA_ERR_SHAPE, "rows_per_wg must be 0, 64 or 128");
   if (d->rows_per_wg == 128 && d->n % 128 != 0) return fail(DFA_ERR_SHAPE, "rows_per_wg 128 needs n % 128 == 0");
   GemvPlan pl;
-  pl.cbf = (d->batch + 15) / 16;  // 16-row activation blocks per flow; kernels exist for 1, 2, 4 blocks in all
+  // Larger batches run in slices of 32 sequences (two flows) or 64 (one flow),
+  // one launch (and reduction) per slice, each reading the weights again.
+  pl.slice = 64 / d->num_flows;
+  const int32_t rows = std::min(d->batch, pl.slice);
+  pl.cbf = (rows + 15) / 16;  // 16-row activation blocks per flow; kernels exist for 1, 2, 4 blocks in all
   if (d->num_flows * pl.cbf > 4) return fail(DFA_ERR_UNSUPPORTED, "too many activation rows");
   if (pl.cbf == 3) pl.cbf = 4;    // one flow, 33..48 rows: padded to 64
   pl.m_pad = d->num_flows * pl.cbf * 16;
@@ -339,11 +345,35 @@ dfa_status gemv_impl(const dfa_gemv_desc* d, const uint16_t* w, const uint16_t* 
     p.rows_per_wg = pl.rows_per_wg;
     p.w_seg1 = p.w_seg2 = w;  // one matrix
     p.seg1_row = p.seg2_row = d->n;
-    hipError_t e = dfa::launch_gemv(p, hs);
-    if (e != hipSuccess) return fail(DFA_ERR_HIP, std::string("gemv launch: ") + hipGetErrorString(e));
-    if (pl.k_split > 1) {
-      e = dfa::launch_gemv_finalize(p, hs);
-      if (e != hipSuccess) return fail(DFA_ERR_HIP, std::string("gemv epilogue launch: ") + hipGetErrorString(e));
+    // slices of at most pl.slice sequences, in order on the stream (they share the workspace)
+    for (int32_t b0 = 0; b0 < d->batch; b0 += pl.slice) {
+      dfa::GemvParams q = p;
+      dfa_gemv_desc ds = *d;
+      ds.batch = std::min(pl.slice, d->batch - b0);
+      GemvPlan ps;
+      validate_gemv(&ds, &ps);
+      q.batch = ds.batch;
+      q.cbf = ps.cbf;
+      q.m_pad = ps.m_pad;
+      q.k_split = ps.k_split;
+      q.k_range = ps.k_range;
+      auto row = [b0](const float* base, int32_t cols) { return base ? base + size_t(b0) * cols : nullptr; };
+      q.x1 = row(p.x1, d->k);
+      q.x2 = row(p.x2, d->k);
+      q.res1 = row(p.res1, d->n);
+      q.res2 = row(p.res2, d->n);
+      q.y1 = const_cast<float*>(row(p.y1, d->n));
+      q.y2 = const_cast<float*>(row(p.y2, d->n));
+      if (kvapp) {
+        q.kv_table = p.kv_table + size_t(b0) * p.kv_max_blocks;
+        q.kv_ctx = p.kv_ctx + b0;
+      }
+      hipError_t e = dfa::launch_gemv(q, hs);
+      if (e != hipSuccess) return fail(DFA_ERR_HIP, std::string("gemv launch: ") + hipGetErrorString(e));
+      if (ps.k_split > 1) {
+        e = dfa::launch_gemv_finalize(q, hs);
+        if (e != hipSuccess) return fail(DFA_ERR_HIP, std::string("gemv epilogue launch: ") + hipGetErrorString(e));
+      }
     }
     return DFA_OK;
   }
@@ -429,9 +459,26 @@ dfa_status qkv_impl(const dfa_layer_desc* d, const GemvPlan& pl, const dfa_layer
   p.kv_bs_log2 = log2i(kv.block_size);
   p.kv_max_blocks = kv.max_blocks_per_seq;
   p.kv_num_blocks = kv.num_blocks;
-  hipError_t e = dfa::launch_gemv(p, hs);
-  if (e == hipSuccess) e = dfa::launch_gemv_finalize(p, hs);
-  if (e != hipSuccess) return fail(DFA_ERR_HIP, std::string("qkv gemv launch: ") + hipGetErrorString(e));
+  // slices of at most pl.slice sequences, in order on the stream (they share the workspace)
+  for (int32_t b0 = 0; b0 < d->batch; b0 += pl.slice) {
+    dfa::GemvParams q = p;
+    dfa_gemv_desc ds{std::min(pl.slice, d->batch - b0), p.n, p.k, 2, DFA_EPI_NONE, x_exact ? 1 : 0, 0, 0};
+    const GemvPlan ps = plan_qkv(ds);
+    q.batch = ds.batch;
+    q.cbf = ps.cbf;
+    q.m_pad = ps.m_pad;
+    q.k_split = ps.k_split;
+    q.k_range = ps.k_range;
+    q.x1 = x1 + size_t(b0) * d->hidden;
+    q.x2 = x2 + size_t(b0) * d->hidden;
+    q.y1 = q1 + size_t(b0) * qd;
+    q.y2 = q2 + size_t(b0) * qd;
+    q.kv_table = kv.block_table + size_t(b0) * kv.max_blocks_per_seq;
+    q.kv_ctx = kv.ctx_lens + b0;
+    hipError_t e = dfa::launch_gemv(q, hs);
+    if (e == hipSuccess) e = dfa::launch_gemv_finalize(q, hs);
+    if (e != hipSuccess) return fail(DFA_ERR_HIP, std::string("qkv gemv launch: ") + hipGetErrorString(e));
+  }
   return DFA_OK;
 }
 

@@ -3,11 +3,14 @@
 // Dual-Flow Transformers", section "Mecanismos Chave"; the shared cache read
 // once for both flows: section "Custos de Inferência vs. Treinamento").
 //
-// Workgroup = (split s, kv head g, sequence b), 4 waves. The query rows of the
-// workgroup are the G query heads of kv head g times the flows: row r is flow
-// r / G, head g*G + r % G. Waves take 32-position chunks of the split in turn
-// and each keeps its own online-softmax state; a merge in LDS ends the
-// workgroup.
+// Workgroup = (split s, kv head g, sequence b), 4 waves per row set of at most
+// 16 rows. The query rows of the workgroup are the G query heads of kv head g
+// times the flows: row r is flow r / G, head g*G + r % G. Waves take
+// 32-position chunks of the split in turn and each keeps its own
+// online-softmax state; a merge in LDS ends the workgroup. More than 16 rows
+// (16 heads per kv head with two flows) take a second set of four waves for
+// rows 16-31, which walks the same chunks in step with the first: the second
+// set's loads of a chunk follow the first set's closely and are served by L2.
 //
 // Cache layout (see include/dfa.h): keys [block][kv head][position/16][D/8][16][8],
 // values [block][kv head][position/16][D][16]: a 16-position tile of either is
@@ -75,10 +78,9 @@ constexpr int kNT = 2;
 // weighted: the weights 2^(s - m_run) stay at most 2^kLazyRescale.
 constexpr float kLazyRescale = 8.f;
 
-// Waves per workgroup (8 measured no faster: the cache stream, not the
+// Waves per row set (8 measured no faster: the cache stream, not the
 // arithmetic between loads, sets the pace).
 constexpr int kAttnWaves = 4;
-constexpr int kAttnThreads = 64 * kAttnWaves;
 
 // Loads one chunk through buffer resources: a tile's base address is
 // wave-uniform (scalar registers), each lane's byte offsets within the tile
@@ -153,20 +155,31 @@ struct QRaw<true> {
   }
 };
 
-template <int D, int NRP, bool QF32>
-__global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(AttnParams p) {
+template <int D, int NRP, bool QF32, int RS = 1>
+__global__ __launch_bounds__(64 * kAttnWaves * RS) void attn_bf16_kernel(AttnParams p) {
+  static_assert(RS == 1 || NRP == 16, "a second row set follows a full first one");
+  constexpr int NT = 64 * kAttnWaves * RS;
   constexpr int KS = D / 32;
   constexpr int DB = D / 16;
   constexpr bool PACKED = (NRP == 8);
+  constexpr int NR = NRP * RS;  // rows of the workgroup, padded
+  // With two row sets, chunks pass from the first set to the second through
+  // LDS: per wave of a set two slots of kPieces 16-byte pieces per lane (the
+  // chunk as that lane holds it), in the space the final merge uses after the loop.
+  constexpr int kPieces = 2 * KS + DB;
+  constexpr int kSoFloats = kAttnWaves * NR * D;
+  constexpr int kXchgFloats = RS == 1 ? 0 : kAttnWaves * 2 * kPieces * 64 * 4;
   __shared__ int tbl[kMaxTableSlice];
-  __shared__ __attribute__((aligned(16))) float sm[kAttnWaves * NRP];
-  __shared__ __attribute__((aligned(16))) float sl[kAttnWaves * NRP];
-  __shared__ __attribute__((aligned(16))) float so[kAttnWaves * NRP * D];
+  __shared__ __attribute__((aligned(16))) float sm[kAttnWaves * NR];
+  __shared__ __attribute__((aligned(16))) float sl[kAttnWaves * NR];
+  __shared__ __attribute__((aligned(16))) float so[kSoFloats > kXchgFloats ? kSoFloats : kXchgFloats];
 
   const int s = blockIdx.x, g = blockIdx.y;
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, wave_all = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rs = RS == 1 ? 0 : wave_all / kAttnWaves;  // row set of the wave
+  const int wave = RS == 1 ? wave_all : wave_all - rs * kAttnWaves;
   const int n = lane & 15, grp = lane >> 4;
-  const int row = PACKED ? (n & 7) : n;
+  const int row = PACKED ? (n & 7) : n + NRP * rs;
   const int nr = p.flows * p.group;
   const bool two = p.flows == 2;
 
@@ -191,7 +204,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(AttnParams p) {
         ar[st][1] = av[1];
       }
     }
-    jb0 = stage_split_table<kAttnThreads>(p, bb, s, tbl);
+    jb0 = stage_split_table<NT>(p, bb, s, tbl);
   };
   // With longest-first order the loads for sequence blockIdx.z go out while
   // the lengths are ranked, and are issued again only if the ranking picks
@@ -209,7 +222,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(AttnParams p) {
   const int len_raw = p.ctx[b];
   __syncthreads();  // the table slice is read by every wave
   SplitRange r;
-  if (!split_bounds<D, kAttnThreads>(p, b, g, s, len_raw, r)) return;
+  if (!split_bounds<D, NT>(p, b, g, s, len_raw, r)) return;
 
   // ---- first chunk's loads, then the query operands while they are in flight ----
   const int bs = 1 << p.bs_log2;
@@ -219,7 +232,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(AttnParams p) {
   const uint32_t koff = (grp * 16 + n) * 16, voff = (n * 16 + 4 * grp) * 2;  // bytes within a tile
   Chunk<D> ca, cb;
   int c = wave;
-  if (c < nchunks) load_chunk<D>(p, kc, vc, tbl, jb0, r.start + 32 * c, r.end, koff, voff, ca);
+  if (c < nchunks && rs == 0) load_chunk<D>(p, kc, vc, tbl, jb0, r.start + 32 * c, r.end, koff, voff, ca);
 
   // scaled (and for flow 2 coupled) query rows, split hi/lo
   bf16x8 qa[KS], qb[KS];
@@ -347,14 +360,69 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(AttnParams p) {
 
   // Wave w takes chunks w, w + kAttnWaves, ...; two register buffers alternate so
   // that the next chunk's loads are in flight while the current one is used.
-  for (; c < nchunks; c += 2 * kAttnWaves) {
-    if (c + kAttnWaves < nchunks)
-      load_chunk<D>(p, kc, vc, tbl, jb0, r.start + 32 * (c + kAttnWaves), r.end, koff, voff, cb);
-    process(ca, c);
-    if (c + kAttnWaves >= nchunks) break;
-    if (c + 2 * kAttnWaves < nchunks)
-      load_chunk<D>(p, kc, vc, tbl, jb0, r.start + 32 * (c + 2 * kAttnWaves), r.end, koff, voff, ca);
-    process(cb, c + kAttnWaves);
+  if constexpr (RS == 1) {
+    for (; c < nchunks; c += 2 * kAttnWaves) {
+      if (c + kAttnWaves < nchunks)
+        load_chunk<D>(p, kc, vc, tbl, jb0, r.start + 32 * (c + kAttnWaves), r.end, koff, voff, cb);
+      process(ca, c);
+      if (c + kAttnWaves >= nchunks) break;
+      if (c + 2 * kAttnWaves < nchunks)
+        load_chunk<D>(p, kc, vc, tbl, jb0, r.start + 32 * (c + 2 * kAttnWaves), r.end, koff, voff, ca);
+      process(cb, c + kAttnWaves);
+    }
+  } else {
+    // Two row sets: wave w of the first set loads chunk w + kAttnWaves * it (the
+    // next one in flight, as above), copies it to its LDS slot it % 2 and
+    // processes it; wave w of the second set processes it one step later, from
+    // the slot. The cache is thus read once from HBM and once through L2 for
+    // all 32 rows, and the second set works while the first waits for its
+    // loads. One barrier opens every step, the same number of steps in every
+    // wave (nchunks is uniform in the workgroup): a slot written in step it
+    // (after its barrier) is read in step it + 1 (after the next barrier) and
+    // rewritten in step it + 2, after the second set has passed that step's
+    // barrier, i.e. finished reading it.
+    uint4* xchg = reinterpret_cast<uint4*>(so) + (size_t)wave * 2 * kPieces * 64 + lane;
+    const int steps = (nchunks + kAttnWaves - 1) / kAttnWaves;
+    // The two sets run separate loops (rs is uniform in a wave), so that each
+    // holds only its own registers; both pass steps + 1 barriers.
+    if (rs == 0) {
+      auto step0 = [&](Chunk<D>& cur, Chunk<D>& nxt, int it) __attribute__((always_inline)) {
+        __syncthreads();
+        const int cc = wave + kAttnWaves * it;
+        if (cc + kAttnWaves < nchunks)
+          load_chunk<D>(p, kc, vc, tbl, jb0, r.start + 32 * (cc + kAttnWaves), r.end, koff, voff, nxt);
+        if (cc < nchunks) {
+          uint4* slot = xchg + (it & 1) * kPieces * 64;
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int st = 0; st < KS; ++st) slot[(u * KS + st) * 64] = __builtin_bit_cast(uint4, cur.k[u][st]);
+#pragma unroll
+          for (int db = 0; db < DB; ++db) slot[(2 * KS + db) * 64] = __builtin_bit_cast(uint4, cur.v[db]);
+          process(cur, cc);
+        }
+      };
+      for (int it = 0; it <= steps; it += 2) {
+        step0(ca, cb, it);
+        if (it + 1 <= steps) step0(cb, ca, it + 1);
+      }
+    } else {
+      for (int it = 0; it <= steps; ++it) {
+        __syncthreads();
+        const int cc = wave + kAttnWaves * (it - 1);
+        if (it > 0 && cc < nchunks) {
+          const uint4* slot = xchg + ((it - 1) & 1) * kPieces * 64;
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int st = 0; st < KS; ++st) ca.k[u][st] = __builtin_bit_cast(bf16x8, slot[(u * KS + st) * 64]);
+#pragma unroll
+          for (int db = 0; db < DB; ++db) ca.v[db] = __builtin_bit_cast(u32x4, slot[(2 * KS + db) * 64]);
+          process(ca, cc);
+        }
+      }
+    }
+    __syncthreads();  // the last slots are read before the merge reuses their space
   }
 
   // ---- wave state to LDS, then merge the waves ----
@@ -367,7 +435,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(AttnParams p) {
       for (int i = 0; i < 4; ++i) oacc[db][i] += dpp_ror8(oacc[db][i]);
   }
   if ((!PACKED || n < 8) && row < nr) {
-    float* dst = so + (wave * NRP + row) * D + 4 * grp;
+    float* dst = so + (wave * NR + row) * D + 4 * grp;
 #pragma unroll
     for (int db = 0; db < DB; ++db) *(f32x4*)(dst + 16 * db) = oacc[db];
     if (grp == 0) {
@@ -376,7 +444,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(AttnParams p) {
     }
   }
   __syncthreads();
-  merge_waves<D, NRP, kAttnWaves>(p, b, g, s, sm, sl, so);
+  merge_waves<D, NR, kAttnWaves, NT>(p, b, g, s, sm, sl, so);
 }
 
 // LDS a workgroup of attn_bf16_kernel<D, NRP> declares, and the dynamic LDS
@@ -385,23 +453,26 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(AttnParams p) {
 // one when it finishes, which balances ragged sequence lengths (two resident
 // workgroups per CU were measured 4% slower on lengths U[1024, 8192] and no
 // faster on uniform ones).
-template <int D, int NRP>
+template <int D, int NR, int RS>
 constexpr size_t one_per_cu_lds() {
   constexpr size_t kCuLds = 160 * 1024;
-  constexpr size_t stat = kMaxTableSlice * 4 + 2 * kAttnWaves * NRP * 4 + kAttnWaves * NRP * D * 4;
+  constexpr size_t so = kAttnWaves * NR * D * 4;
+  constexpr size_t xchg = RS == 1 ? 0 : kAttnWaves * 2 * (D / 16 + D / 16) * 64 * 16;  // two slots of 2*KS + DB pieces
+  constexpr size_t stat = kMaxTableSlice * 4 + 2 * kAttnWaves * NR * 4 + (so > xchg ? so : xchg);
   return stat > kCuLds / 2 ? 0 : kCuLds / 2 + 256 - stat;
 }
 
 hipError_t launch_attn_bf16(const AttnParams& p, int head_dim, int rows_padded, hipStream_t stream,
                             const KernelEvents& ev) {
-  const dim3 grid(p.n_splits, p.hkv, p.batch), block(kAttnThreads);
-#define DFA_ATTN_CASE(D_, NRP_)                                                                              \
-  if (head_dim == D_ && rows_padded == NRP_)                                                                 \
-    return p.q_f32 ? launch_kernel(attn_bf16_kernel<D_, NRP_, true>, grid, block, stream, ev, p,              \
-                                   one_per_cu_lds<D_, NRP_>())                                                \
-                   : launch_kernel(attn_bf16_kernel<D_, NRP_, false>, grid, block, stream, ev, p,             \
-                                   one_per_cu_lds<D_, NRP_>());
-  DFA_ATTN_CASE(128, 8) DFA_ATTN_CASE(128, 16) DFA_ATTN_CASE(64, 8) DFA_ATTN_CASE(64, 16)
+  const dim3 grid(p.n_splits, p.hkv, p.batch);
+#define DFA_ATTN_CASE(D_, NRP_, RS_)                                                                         \
+  if (head_dim == D_ && rows_padded == NRP_ * RS_)                                                           \
+    return p.q_f32 ? launch_kernel(attn_bf16_kernel<D_, NRP_, true, RS_>, grid, dim3(64 * kAttnWaves * RS_), \
+                                   stream, ev, p, one_per_cu_lds<D_, NRP_ * RS_, RS_>())                           \
+                   : launch_kernel(attn_bf16_kernel<D_, NRP_, false, RS_>, grid, dim3(64 * kAttnWaves * RS_), \
+                                   stream, ev, p, one_per_cu_lds<D_, NRP_ * RS_, RS_>());
+  DFA_ATTN_CASE(128, 8, 1) DFA_ATTN_CASE(128, 16, 1) DFA_ATTN_CASE(64, 8, 1) DFA_ATTN_CASE(64, 16, 1)
+  DFA_ATTN_CASE(128, 16, 2) DFA_ATTN_CASE(64, 16, 2)
 #undef DFA_ATTN_CASE
   return hipErrorInvalidValue;
 }

@@ -118,21 +118,21 @@ __device__ __forceinline__ bool split_bounds(const AttnParams& p, int b, int g, 
   return false;
 }
 
-// Cross-wave merge. Each wave w left, for each of its rows, the running max
-// sm[row*NW+w], sum sl[row*NW+w] and unnormalised output so[(w*NRP+row)*D+d]
-// (all in base-2 units), for waves w < NW. Writes the normalised output in
+// Cross-wave merge. Each of the NW waves w that served a row left, for that
+// row, the running max sm[row*NW+w], sum sl[row*NW+w] and unnormalised output
+// so[(w*NRP+row)*D+d] (all in base-2 units); NT threads take part. Writes the normalised output in
 // direct mode (one split per sequence), otherwise the split record (O, m, l)
 // of each row. A thread takes four consecutive dimensions of a row, so every
 // LDS read and global store moves 16 bytes. A wave that took no position
 // left (m, l, O) = (-inf, 0, 0) and gets weight 0; some wave holds a position
 // of a non-empty split, so the row max is finite.
-template <int D, int NRP, int NW = kWaves>
+template <int D, int NRP, int NW = kWaves, int NT = 64 * NW>
 __device__ __forceinline__ void merge_waves(const AttnParams& p, int b, int g, int s,
                                             const float* sm, const float* sl, const float* so) {
   static_assert(NW == 4, "the four waves' (m, l) of a row are read as one float4");
   constexpr int D4 = D / 4;
   const int nr = p.flows * p.group;
-  for (int idx = threadIdx.x; idx < nr * D4; idx += 64 * NW) {
+  for (int idx = threadIdx.x; idx < nr * D4; idx += NT) {
     const int row = idx / D4, d = 4 * (idx - row * D4);
     const float4 m4 = *(const float4*)(sm + row * NW);
     const float4 l4 = *(const float4*)(sl + row * NW);

@@ -14,7 +14,8 @@ namespace dfa {
 
 constexpr int kWaves = 4;          // waves per attention workgroup
 constexpr int kThreads = 64 * kWaves;
-constexpr int kMaxRows = 16;       // query rows (heads x flows) served per workgroup
+constexpr int kMaxRows = 16;       // query rows (heads x flows) per float32-cache workgroup and per row set
+constexpr int kMaxRowsBf16 = 32;   // query rows per bf16-cache workgroup (two row sets)
 constexpr int kRecPad = 4;         // partial record = head_dim + kRecPad floats
 constexpr int kMaxTableSlice = 1024;  // block-table entries staged per split
 

@@ -85,7 +85,8 @@ typedef enum dfa_dtype { DFA_F32 = 0, DFA_BF16 = 1 } dfa_dtype;
 /* Shape and policy of one decode-attention call (one layer). */
 typedef struct dfa_attn_desc {
   int32_t batch;              /* sequences, >= 1 */
-  int32_t num_q_heads;        /* Hq, multiple of num_kv_heads */
+  int32_t num_q_heads;        /* Hq, multiple of num_kv_heads; (Hq / Hkv) * num_flows <= 32
+                                 with a bf16 cache, <= 16 with a float32 cache */
   int32_t num_kv_heads;       /* Hkv >= 1 */
   int32_t head_dim;           /* D: 64 or 128 */
   int32_t block_size;         /* positions per cache block: power of two >= 16 */
@@ -256,7 +257,9 @@ typedef enum dfa_epilogue {
 } dfa_epilogue;
 
 typedef struct dfa_gemv_desc {
-  int32_t batch;         /* sequences = rows per flow: 1..32 (two flows), 1..64 (one flow) */
+  int32_t batch;         /* sequences = rows per flow, 1..65535; one launch (and reduction) per
+                            slice of 32 sequences with two flows, 64 with one: a larger batch
+                            reads the weights once per slice */
   int32_t n;             /* output columns = rows of W, multiple of 64 */
   int32_t k;             /* input columns = columns of W, multiple of 128 */
   int32_t num_flows;     /* 1 (primary only) or 2 */
@@ -315,11 +318,11 @@ DFA_API dfa_status dfa_pack_weight(const uint16_t* w, uint16_t* w_tiled, int32_t
  * [Wq; Wk; Wv] (the matrices stay separate in memory) whose split-K reduction
  * stores the queries and appends the keys and values; each other GEMV is one
  * launch plus, when its plan splits k, a reduction launch (at the benchmark
- * shape: 8 launches). Every weight is read once for both flows. The caller
- * advances ctx_lens afterwards. Requirements: those of
- * dfa_decode_attn (max_ctx_len >= every ctx_lens[b] + 1) and of dfa_dual_gemv
- * (batch <= 32; hidden, mlp, num_q_heads * head_dim and num_kv_heads *
- * head_dim multiples of 128). x1, x2, out1, out2: float32 [batch, hidden].
+ * shape: 8 launches). Every weight is read once for both flows (once per
+ * slice of 32 sequences beyond 32). The caller advances ctx_lens afterwards.
+ * Requirements: those of dfa_decode_attn (max_ctx_len >= every ctx_lens[b] +
+ * 1) and of dfa_dual_gemv (hidden, mlp, num_q_heads * head_dim and
+ * num_kv_heads * head_dim multiples of 128). x1, x2, out1, out2: float32 [batch, hidden].
  * The auxiliary flow's inputs (x2, a, b, c) never affect out1 or the cache.
  */
 typedef struct dfa_layer_desc {

@@ -60,12 +60,25 @@ def test_split_plan_and_workspace_size():
     assert dfa.dfa_decode_attn_split_len(c2_desc(split_len=96)) == 96
 
 
+def test_row_limits():
+    """Up to 32 query rows (heads per kv head x flows) with a bf16 cache, 16 with a float32 cache."""
+    plan = lambda **kw: _lib.lib().dfa_decode_attn_split_len(ctypes.byref(c2_desc(**kw)))
+    for hq, flows in ((128, 2), (256, 1), (72, 2), (64, 2)):
+        assert plan(num_q_heads=hq, num_flows=flows) > 0
+    assert _lib.STATUS[-plan(num_q_heads=256, num_flows=2)] == "DFA_ERR_UNSUPPORTED"
+    f32 = dict(q_dtype=dfa.DFA_F32, kv_dtype=dfa.DFA_F32)
+    assert plan(num_q_heads=64, **f32) > 0
+    assert plan(num_q_heads=128, num_flows=1, **f32) > 0
+    assert _lib.STATUS[-plan(num_q_heads=128, **f32)] == "DFA_ERR_UNSUPPORTED"
+
+
 @pytest.mark.parametrize("change,status", [
     (dict(batch=0), "DFA_ERR_SHAPE"),
     (dict(num_q_heads=30), "DFA_ERR_SHAPE"),
     (dict(num_flows=3), "DFA_ERR_SHAPE"),
     (dict(head_dim=96), "DFA_ERR_UNSUPPORTED"),
-    (dict(num_q_heads=72), "DFA_ERR_UNSUPPORTED"),  # 9 heads per kv head x 2 flows > 16 rows
+    (dict(num_q_heads=136), "DFA_ERR_UNSUPPORTED"),  # 17 heads per kv head x 2 flows > 32 rows
+    (dict(num_q_heads=72, q_dtype=dfa.DFA_F32, kv_dtype=dfa.DFA_F32), "DFA_ERR_UNSUPPORTED"),  # > 16 rows, f32 cache
     (dict(block_size=48), "DFA_ERR_SHAPE"),
     (dict(block_size=8, max_blocks_per_seq=512), "DFA_ERR_SHAPE"),
     (dict(max_ctx_len=0), "DFA_ERR_SHAPE"),

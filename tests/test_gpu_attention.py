@@ -2,8 +2,8 @@
 
 Element-by-element against the float64 oracle on reduced shapes of each
 workload (several 32-position chunks, several splits, ragged tails, paged and
-contiguous caches, G in {1, 2, 4, 8, 16}); sampled (sequence, kv head) pairs at
-the full workload sizes in the benchmark's launch configuration; and the
+contiguous caches, G in {1, 2, 4, 8, 12, 16, 32}, up to 32 query rows per kv head); every
+(sequence, kv head) pair at the full workload sizes in the benchmark's launch configuration; and the
 invariants the method fixes (primary independence, the cache is never written,
 aux == primary without coupling, one position returns its value, paging and
 split plans do not change the result). Unused cache slots hold NaN, so any read
@@ -41,6 +41,13 @@ SMALL = {
                                 ctx_lens=(513, 96), block_size=32, shuffle_blocks=True), 2015),
     "f32q_rows16": (W.AttnConfig("f32qr16", batch=2, num_q_heads=16, num_kv_heads=2, head_dim=128, dtype="bf16",
                                  ctx_lens=(1025, 40), capacity=2048, q_dtype="f32"), 2016),
+    # more than 16 rows per kv head: a second row set of waves (16 heads x 2 flows; 12 heads x 2 flows)
+    "g16_paged": (W.AttnConfig("g16p", batch=3, num_q_heads=32, num_kv_heads=2, head_dim=128, dtype="bf16",
+                               ctx_lens=(600, 4097, 33), block_size=32, shuffle_blocks=True), 2018),
+    "g16_d64_f32q": (W.AttnConfig("g16d64", batch=2, num_q_heads=16, num_kv_heads=1, head_dim=64, dtype="bf16",
+                                  ctx_lens=(257, 1000), q_dtype="f32"), 2019),
+    "g12": (W.AttnConfig("g12", batch=2, num_q_heads=36, num_kv_heads=3, head_dim=128, dtype="bf16",
+                         ctx_lens=(100, 513)), 2020),
     # more than 64 sequences: one split each, taken in batch order (no length ranking)
     "batch70": (W.AttnConfig("b70", batch=70, num_q_heads=8, num_kv_heads=4, head_dim=128, dtype="bf16",
                              ctx_range=(1, 300), block_size=16, shuffle_blocks=True), 2017),
@@ -75,22 +82,36 @@ def test_parity_small(name, flows, split):
         assert_close(o2, ref["o2"], what=f"{name} o2")
 
 
-def test_group_of_16_single_flow():
+def test_groups_of_16_and_32():
+    """16 heads per kv head: one row set with one flow, two with both flows, and the primary bit for bit
+    the same either way; 32 heads per kv head with one flow (32 rows); 64 rows are refused."""
     cfg = W.AttnConfig("g16", batch=2, num_q_heads=32, num_kv_heads=2, head_dim=128, dtype="bf16",
                        ctx_lens=(77, 300))
     case = W.make_attn_case(cfg, 2010)
-    say("case g16 one flow")
-    o1, _ = run_attn(case, num_flows=1, split_len=64)
-    assert_close(o1, oracle_attn(case, num_flows=1)["o1"], what="g16 o1")
-    with pytest.raises(dfa.DfaError):  # 16 heads x 2 flows exceed one workgroup's 16 rows
-        run_attn(case, num_flows=2)
+    say("case g16 one flow, two flows")
+    ref = oracle_attn(case)
+    for split in (64, 0):
+        p1, _ = run_attn(case, num_flows=1, split_len=split)
+        o1, o2 = run_attn(case, num_flows=2, split_len=split)
+        assert_close(p1, ref["o1"], what=f"g16 split {split} one-flow o1")
+        assert_close(o1, ref["o1"], what=f"g16 split {split} o1")
+        assert_close(o2, ref["o2"], what=f"g16 split {split} o2")
+        assert np.array_equal(p1, o1), "the primary must not depend on the second row set"
+    cfg32 = W.AttnConfig("g32", batch=2, num_q_heads=32, num_kv_heads=1, head_dim=64, dtype="bf16",
+                         ctx_lens=(129, 40))
+    case32 = W.make_attn_case(cfg32, 2011)
+    say("case g32 one flow")
+    o1, _ = run_attn(case32, num_flows=1, split_len=64)
+    assert_close(o1, oracle_attn(case32, num_flows=1)["o1"], what="g32 o1")
+    with pytest.raises(dfa.DfaError):  # 32 heads x 2 flows exceed a workgroup's 32 rows
+        run_attn(case32, num_flows=2)
 
 
 # ---------------------------------------------------------------- full sizes
-FULL = {"c2": W.C2, "c3": W.C3, "c4": W.C4}
+FULL = {"c2": W.C2, "c3": W.C3, "c4": W.C4, "g16": W.G16}
 
 
-@pytest.mark.parametrize("name", ["c2", "c3", "c4"])
+@pytest.mark.parametrize("name", ["c2", "c3", "c4", "g16"])
 def test_full_size_all_pairs(name):
     """Every output row of the full workload, in the benchmark's launch configuration (the
     library's plan), against the oracle."""

@@ -70,7 +70,9 @@ def rand_w(rng, n, k, std=0.02):
 
 
 @pytest.mark.parametrize("batch,k_split,rows", [(1, 0, 0), (17, 0, 0), (32, 1, 0), (32, 2, 0), (5, 3, 0),
-                                               (32, 1, 128), (17, 2, 128), (1, 3, 128)])
+                                               (32, 1, 128), (17, 2, 128), (1, 3, 128),
+                                               # beyond 32 sequences: slices of 32 (the last one ragged)
+                                               (40, 0, 0), (70, 2, 0), (64, 1, 128)])
 def test_gemv_epilogues(batch, k_split, rows):
     rng = np.random.default_rng(batch * 10 + k_split)
     n, k = 256, 384
@@ -130,7 +132,7 @@ def test_gemv_rows_multiple_of_64(k_split):
     assert_close(y2, LY.linear(x2.astype(np.float64), w), what="n=192 y2")
 
 
-@pytest.mark.parametrize("batch", [40, 64])
+@pytest.mark.parametrize("batch", [40, 64, 100])
 def test_gemv_one_flow_wide_batch(batch):
     rng = np.random.default_rng(batch)
     x1 = rng.standard_normal((batch, 256)).astype(np.float32)
@@ -165,17 +167,18 @@ def test_exact_bf16_activations_skip_low_halves():
     assert_close(b1, LY.linear(x1.astype(np.float64), w), what="exact y1")
 
 
-@pytest.mark.parametrize("k_split", [1, 2])
-def test_gemv_kv_append(k_split):
-    """The primary-only append, in the GEMV kernel (one k-range) and after the split reduction."""
-    cfg = SMALL_LAYER.replace(num_kv_heads=2, hidden=384)
-    case = W.make_layer_case(cfg, 40 + k_split)
+@pytest.mark.parametrize("k_split,batch", [(1, 5), (2, 5), (2, 70)])
+def test_gemv_kv_append(k_split, batch):
+    """The primary-only append, in the GEMV kernel (one k-range) and after the split reduction; 70
+    sequences run in slices of 64."""
+    cfg = SMALL_LAYER.replace(num_kv_heads=2, hidden=384, batch=batch)
+    case = W.make_layer_case(cfg, 40 + k_split + batch)
     kd = cfg.num_kv_heads * cfg.head_dim
     k_cache, v_cache = to_device(case.k_cache), to_device(case.v_cache)
     table, ctx = to_device(case.block_table), to_device(case.ctx_lens)  # kept alive: kv holds raw addresses
     kv = dfa.kv_target(k_cache, v_cache, table, ctx, cfg.num_kv_heads, cfg.head_dim, case.block_size,
                        case.max_blocks_per_seq, case.k_cache.shape[0])
-    say(f"case gemv kv append k_split={k_split}")
+    say(f"case gemv kv append k_split={k_split} batch={batch}")
     y1, y2 = gemv(dfa.DFA_EPI_KV_APPEND, case.w["wk"], case.x1, w2_bits=case.w["wv"], x_exact=1, k_split=k_split,
                   kv=kv, y_kv=True)
     k_lin, v_lin = LY.linear(case.x1, case.w["wk"]), LY.linear(case.x1, case.w["wv"])
@@ -196,7 +199,7 @@ def test_gemv_kv_append(k_split):
 
 
 def test_gemv_rejects_bad_shapes():
-    d = dfa.GemvDesc(batch=33, n=128, k=128, num_flows=2, epilogue=0, x_exact_bf16=0, k_split=0)
+    d = dfa.GemvDesc(batch=65536, n=128, k=128, num_flows=2, epilogue=0, x_exact_bf16=0, k_split=0)
     assert dfa.dfa_dual_gemv_workspace_size(d) == 0
     d = dfa.GemvDesc(batch=4, n=96, k=128, num_flows=2, epilogue=0, x_exact_bf16=0, k_split=2)
     assert dfa.dfa_dual_gemv_workspace_size(d) == 0
@@ -275,6 +278,23 @@ def test_layer_small_paged():
     packed, dev, desc = layer_inputs(case)
     say("case layer small paged")
     check_layer(case, run_layer(case, packed, dev, desc), oracle_layer(case), "small layer")
+
+
+def test_layer_batch_beyond_32():
+    """40 sequences: the GEMVs (and the fused QKV append) run in slices of 32, attention over all 40."""
+    case = W.make_layer_case(SMALL_LAYER.replace(batch=40), 32)
+    packed, dev, desc = layer_inputs(case)
+    say("case layer batch 40")
+    check_layer(case, run_layer(case, packed, dev, desc), oracle_layer(case), "batch-40 layer")
+
+
+def test_layer_sixteen_heads_per_kv_head():
+    """16 query heads per kv head: attention runs 32 query rows (both flows) per kv head."""
+    cfg = SMALL_LAYER.replace(num_q_heads=32, num_kv_heads=2, head_dim=64, hidden=512, batch=3)
+    case = W.make_layer_case(cfg, 33)
+    packed, dev, desc = layer_inputs(case)
+    say("case layer 16 heads per kv head")
+    check_layer(case, run_layer(case, packed, dev, desc), oracle_layer(case), "g16 layer")
 
 
 @pytest.mark.slow

@@ -125,8 +125,12 @@ C3 = AttnConfig("c3", batch=64, num_q_heads=64, num_kv_heads=8, head_dim=128, dt
                 ctx_range=(1024, 8192), block_size=16, shuffle_blocks=True)
 C4 = AttnConfig("c4", batch=4, num_q_heads=32, num_kv_heads=8, head_dim=128, dtype="bf16",
                 ctx_lens=(131072,) * 4, peaky_fraction=0.01, peaky_factor=8.0)
-ATTN_CONFIGS = {"c1": C1, "c2": C2, "c3": C3, "c4": C4}
-SEEDS = {"c1": 1001, "c2": 1002, "c3": 1003, "c4": 1004, "c5": 1005, "head": 1006, "mix": 1007, "moe": 1008, "prefill": 1009, "stack": 1010}
+# 16 query heads per kv head (a 128/8-head model): 32 query rows per kv head with both flows
+G16 = AttnConfig("g16", batch=8, num_q_heads=128, num_kv_heads=8, head_dim=128, dtype="bf16",
+                 ctx_lens=(16384,) * 8)
+ATTN_CONFIGS = {"c1": C1, "c2": C2, "c3": C3, "c4": C4, "g16": G16}
+SEEDS = {"c1": 1001, "c2": 1002, "c3": 1003, "c4": 1004, "c5": 1005, "head": 1006, "mix": 1007, "moe": 1008,
+         "prefill": 1009, "stack": 1010, "g16": 1011}
 
 
 def draw_ctx_lens(cfg: AttnConfig, seed: int) -> np.ndarray:

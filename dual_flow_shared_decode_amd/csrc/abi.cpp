@@ -782,7 +782,7 @@ dfa_status dfa_mixture_sample(const dfa_mixture_desc* d, const float* logits1, c
 
 static dfa_status validate_moe(const dfa_moe_desc* d) {
   if (!d) return fail(DFA_ERR_NULL, "desc is NULL");
-  if (d->batch < 1 || d->batch > 32) return fail(DFA_ERR_SHAPE, "batch must be in [1, 32]");
+  if (d->batch < 1 || d->batch > 65535) return fail(DFA_ERR_SHAPE, "batch must be in [1, 65535]");
   if (d->hidden < 128 || d->hidden % 128 != 0 || d->mlp < 128 || d->mlp % 128 != 0)
     return fail(DFA_ERR_SHAPE, "hidden and mlp must be positive multiples of 128");
   if (d->num_experts < 1 || d->num_experts > dfa::kMoeMaxExperts)
@@ -791,6 +791,10 @@ static dfa_status validate_moe(const dfa_moe_desc* d) {
     return fail(DFA_ERR_SHAPE, "fan-outs must satisfy 1 <= k1 <= k2 <= min(num_experts, 32)");
   return DFA_OK;
 }
+
+// Sequences per pass of the expert GEMVs (their activation blocks hold 64 rows of both flows); a
+// larger batch runs in slices, each reading its selected experts again.
+constexpr int kMoeSlice = 32;
 
 // Weight rows per workgroup of the grouped expert GEMVs.
 constexpr int kMoeRowsUp = 128;
@@ -817,8 +821,9 @@ size_t dfa_moe_routing_size(const dfa_moe_desc* d) {
 
 size_t dfa_moe_workspace_size(const dfa_moe_desc* d) {
   if (validate_moe(d) != DFA_OK) return 0;
-  // both flows' expert intermediates [batch][k2][2][mlp], then expert outputs [batch][k2][2][hidden]
-  return size_t(d->batch) * d->k2 * 2 * (size_t(d->mlp) + d->hidden) * sizeof(float);
+  // both flows' expert intermediates [slice][k2][2][mlp], then expert outputs [slice][k2][2][hidden],
+  // slice = min(batch, kMoeSlice) sequences (the slices of a larger batch reuse them in turn)
+  return size_t(std::min(d->batch, kMoeSlice)) * d->k2 * 2 * (size_t(d->mlp) + d->hidden) * sizeof(float);
 }
 
 dfa_status dfa_moe_route(const dfa_moe_desc* d, const float* r1, const float* r2, void* routing,
@@ -866,83 +871,88 @@ dfa_status dfa_moe_ffn(const dfa_moe_desc* d, const uint16_t* w_gate, const uint
     if (!workspace || workspace_bytes < need) return fail(DFA_ERR_WORKSPACE, "workspace smaller than dfa_moe_workspace_size()");
     const MoeRouting lay = moe_routing_layout(d);
     const char* rb = static_cast<const char*>(routing);
-    const int32_t* sel = reinterpret_cast<const int32_t*>(rb);
-    float* z = static_cast<float*>(workspace);
-    float* y = z + size_t(d->batch) * d->k2 * 2 * d->mlp;
     const hipStream_t hs = static_cast<hipStream_t>(stream);
+    // slices of at most kMoeSlice sequences, in order on the stream (they share the workspace)
+    for (int32_t b0 = 0; b0 < d->batch; b0 += kMoeSlice) {
+      const int32_t nb = std::min(kMoeSlice, d->batch - b0);
+      const int32_t* sel = reinterpret_cast<const int32_t*>(rb) + size_t(b0) * d->k2;
+      float* z = static_cast<float*>(workspace);
+      float* y = z + size_t(nb) * d->k2 * 2 * d->mlp;
+      const size_t xo = size_t(b0) * d->hidden;  // row offset of the slice in [batch, hidden] tensors
 
-    // gate and up projections of every selected expert, SwiGLU and b in the epilogue
-    dfa::GemvParams g{};
-    g.batch = d->batch;
-    g.flows = 2;
-    g.cbf = (d->batch + 15) / 16;
-    g.m_pad = 2 * g.cbf * 16;
-    g.k_split = 1;
-    g.moe_sel = sel;
-    g.moe_k1 = d->k1;
-    g.moe_k2 = d->k2;
-    g.moe_experts = d->num_experts;
-    dfa::GemvParams up = g;
-    up.w = w_gate;
-    up.w2 = w_up;
-    up.x1 = h1;
-    up.x2 = h2;
-    up.couple = b;
-    up.y1 = up.y2 = z;
-    up.n = d->mlp;
-    up.k = d->hidden;
-    up.k_range = d->hidden;
-    up.pair = 1;
-    up.x_exact = d->x_exact_bf16 != 0;
-    up.epilogue = dfa::kEpiSwiglu;
-    up.w_seg1 = up.w_seg2 = w_gate;
-    up.seg1_row = up.seg2_row = d->mlp;
-    up.moe_wstride = int64_t(d->mlp) * d->hidden;
-    up.rows_per_wg = d->mlp % kMoeRowsUp == 0 ? kMoeRowsUp : 64;
-    up.moe_rgs = d->mlp / up.rows_per_wg;
-    up.moe_row_s = 1;
-    hipError_t e = dfa::launch_gemv(up, hs);
-    if (e != hipSuccess) return fail(DFA_ERR_HIP, std::string("moe gate/up launch: ") + hipGetErrorString(e));
-    // down projection of every selected expert, from the intermediates [batch][k2][2][mlp]
-    // (the two halves of each expert's matrix as the two matrices of one
-    // workgroup where they tile evenly: twice the weight bytes per stage)
-    dfa::GemvParams dn = g;
-    const bool halves = (d->hidden / 2) % kMoeRowsDown == 0;
-    dn.w = w_down;
-    dn.x1 = dn.x2 = z;
-    dn.y1 = dn.y2 = y;
-    dn.n = halves ? d->hidden / 2 : d->hidden;
-    dn.k = d->mlp;
-    dn.k_range = d->mlp;
-    dn.pair = halves ? 1 : 0;
-    dn.w2 = halves ? w_down + size_t(dn.n) * d->mlp : nullptr;  // packed by 16-row tiles: rows [n, 2n)
-    dn.x_exact = 0;
-    dn.epilogue = halves ? dfa::kEpiSplitPair : dfa::kEpiNone;
-    dn.w_seg1 = dn.w_seg2 = w_down;
-    dn.seg1_row = dn.seg2_row = dn.n;
-    dn.moe_wstride = int64_t(d->hidden) * d->mlp;
-    dn.rows_per_wg = dn.n % kMoeRowsDown == 0 ? kMoeRowsDown : 64;
-    dn.moe_rgs = dn.n / dn.rows_per_wg;
-    dn.moe_row_s = 2 * d->k2;
-    dn.moe_row_slot = 2;
-    dn.moe_row_f = 1;
-    e = dfa::launch_gemv(dn, hs);
-    if (e != hipSuccess) return fail(DFA_ERR_HIP, std::string("moe down launch: ") + hipGetErrorString(e));
-    dfa::MoeCombineParams cp{};
-    cp.y = y;
-    cp.g1 = reinterpret_cast<const float*>(rb + lay.g1_off);
-    cp.g2 = reinterpret_cast<const float*>(rb + lay.g2_off);
-    cp.res1 = res1;
-    cp.res2 = res2;
-    cp.c = c;
-    cp.out1 = out1;
-    cp.out2 = out2;
-    cp.batch = d->batch;
-    cp.hidden = d->hidden;
-    cp.k1 = d->k1;
-    cp.k2 = d->k2;
-    e = dfa::launch_moe_combine(cp, hs);
-    if (e != hipSuccess) return fail(DFA_ERR_HIP, std::string("moe combine launch: ") + hipGetErrorString(e));
+      // gate and up projections of every selected expert, SwiGLU and b in the epilogue
+      dfa::GemvParams g{};
+      g.batch = nb;
+      g.flows = 2;
+      g.cbf = (nb + 15) / 16;
+      g.m_pad = 2 * g.cbf * 16;
+      g.k_split = 1;
+      g.moe_sel = sel;
+      g.moe_k1 = d->k1;
+      g.moe_k2 = d->k2;
+      g.moe_experts = d->num_experts;
+      dfa::GemvParams up = g;
+      up.w = w_gate;
+      up.w2 = w_up;
+      up.x1 = h1 + xo;
+      up.x2 = h2 + xo;
+      up.couple = b;
+      up.y1 = up.y2 = z;
+      up.n = d->mlp;
+      up.k = d->hidden;
+      up.k_range = d->hidden;
+      up.pair = 1;
+      up.x_exact = d->x_exact_bf16 != 0;
+      up.epilogue = dfa::kEpiSwiglu;
+      up.w_seg1 = up.w_seg2 = w_gate;
+      up.seg1_row = up.seg2_row = d->mlp;
+      up.moe_wstride = int64_t(d->mlp) * d->hidden;
+      up.rows_per_wg = d->mlp % kMoeRowsUp == 0 ? kMoeRowsUp : 64;
+      up.moe_rgs = d->mlp / up.rows_per_wg;
+      up.moe_row_s = 1;
+      hipError_t e = dfa::launch_gemv(up, hs);
+      if (e != hipSuccess) return fail(DFA_ERR_HIP, std::string("moe gate/up launch: ") + hipGetErrorString(e));
+      // down projection of every selected expert, from the intermediates [batch][k2][2][mlp]
+      // (the two halves of each expert's matrix as the two matrices of one
+      // workgroup where they tile evenly: twice the weight bytes per stage)
+      dfa::GemvParams dn = g;
+      const bool halves = (d->hidden / 2) % kMoeRowsDown == 0;
+      dn.w = w_down;
+      dn.x1 = dn.x2 = z;
+      dn.y1 = dn.y2 = y;
+      dn.n = halves ? d->hidden / 2 : d->hidden;
+      dn.k = d->mlp;
+      dn.k_range = d->mlp;
+      dn.pair = halves ? 1 : 0;
+      dn.w2 = halves ? w_down + size_t(dn.n) * d->mlp : nullptr;  // packed by 16-row tiles: rows [n, 2n)
+      dn.x_exact = 0;
+      dn.epilogue = halves ? dfa::kEpiSplitPair : dfa::kEpiNone;
+      dn.w_seg1 = dn.w_seg2 = w_down;
+      dn.seg1_row = dn.seg2_row = dn.n;
+      dn.moe_wstride = int64_t(d->hidden) * d->mlp;
+      dn.rows_per_wg = dn.n % kMoeRowsDown == 0 ? kMoeRowsDown : 64;
+      dn.moe_rgs = dn.n / dn.rows_per_wg;
+      dn.moe_row_s = 2 * d->k2;
+      dn.moe_row_slot = 2;
+      dn.moe_row_f = 1;
+      e = dfa::launch_gemv(dn, hs);
+      if (e != hipSuccess) return fail(DFA_ERR_HIP, std::string("moe down launch: ") + hipGetErrorString(e));
+      dfa::MoeCombineParams cp{};
+      cp.y = y;
+      cp.g1 = reinterpret_cast<const float*>(rb + lay.g1_off) + size_t(b0) * d->k1;
+      cp.g2 = reinterpret_cast<const float*>(rb + lay.g2_off) + size_t(b0) * d->k2;
+      cp.res1 = res1 ? res1 + xo : nullptr;
+      cp.res2 = res2 ? res2 + xo : nullptr;
+      cp.c = c;
+      cp.out1 = out1 + xo;
+      cp.out2 = out2 + xo;
+      cp.batch = nb;
+      cp.hidden = d->hidden;
+      cp.k1 = d->k1;
+      cp.k2 = d->k2;
+      e = dfa::launch_moe_combine(cp, hs);
+      if (e != hipSuccess) return fail(DFA_ERR_HIP, std::string("moe combine launch: ") + hipGetErrorString(e));
+    }
     return DFA_OK;
   } catch (...) {
     return fail(DFA_ERR_HIP, "unexpected host exception");

@@ -462,7 +462,8 @@ DFA_API dfa_status dfa_mixture_sample(const dfa_mixture_desc* desc, const float*
  * flow's inputs (h2, r2, res2, b, c).
  */
 typedef struct dfa_moe_desc {
-  int32_t batch;         /* sequences: 1..32 */
+  int32_t batch;         /* sequences: 1..65535 (the expert GEMVs run slices of 32 sequences,
+                            each reading its selected experts again) */
   int32_t hidden;        /* model width: multiple of 128 */
   int32_t mlp;           /* expert width: multiple of 128 */
   int32_t num_experts;   /* 1..1024 */
@@ -488,7 +489,7 @@ DFA_API size_t dfa_moe_routing_size(const dfa_moe_desc* desc);
 DFA_API dfa_status dfa_moe_route(const dfa_moe_desc* desc, const float* r1, const float* r2, void* routing,
                                  size_t routing_bytes, void* stream);
 
-/* Workspace bytes of dfa_moe_ffn: 4 * batch * k2 * 2 * (mlp + hidden); 0 if invalid. */
+/* Workspace bytes of dfa_moe_ffn: 4 * min(batch, 32) * k2 * 2 * (mlp + hidden); 0 if invalid. */
 DFA_API size_t dfa_moe_workspace_size(const dfa_moe_desc* desc);
 
 /*

@@ -226,7 +226,11 @@ def test_moe_sizes_and_validation():
     assert dfa.dfa_moe_routing_size(d) == 32 * 8 * 4 + 32 * 4 * 4 + 32 * 8 * 4
     assert dfa.dfa_moe_routing_size(moe_desc(batch=3, k1=1, k2=3)) == 48 + 16 + 48
     assert dfa.dfa_moe_workspace_size(d) == 4 * 32 * 8 * 2 * (1024 + 4096)
-    for bad in (dict(batch=0), dict(batch=33), dict(hidden=4000), dict(mlp=64), dict(num_experts=0),
+    # larger batches: the routing grows with the batch, the workspace holds one slice of 32 sequences
+    assert dfa.dfa_moe_routing_size(moe_desc(batch=70)) == 70 * 8 * 4 + 70 * 4 * 4 + 70 * 8 * 4
+    assert dfa.dfa_moe_workspace_size(moe_desc(batch=70)) == 4 * 32 * 8 * 2 * (1024 + 4096)
+    assert dfa.dfa_moe_workspace_size(moe_desc(batch=5)) == 4 * 5 * 8 * 2 * (1024 + 4096)
+    for bad in (dict(batch=0), dict(batch=65536), dict(hidden=4000), dict(mlp=64), dict(num_experts=0),
                 dict(num_experts=1025), dict(k1=0), dict(k1=9), dict(k2=65), dict(num_experts=40, k2=33, k1=1)):
         bd = moe_desc(**bad)
         assert dfa.dfa_moe_routing_size(bd) == 0 and dfa.dfa_moe_workspace_size(bd) == 0, bad

@@ -4,9 +4,9 @@ Routing: the selection is compared exactly (integer work), the mixing weights to
 outputs: the row-normalised max relative error of the other GPU tests (2e-3) against the float64
 oracle run on the same routing. Invariants: the primary flow is bit for bit independent of the
 auxiliary flow's inputs; with equal flows, equal fan-outs and no coupling the flows agree bit for
-bit. Edge cases: one sequence, ragged batches (17: two activation blocks per flow), one expert,
-every expert selected, an expert chosen by every sequence, experts chosen by none, inputs that are
-not exact bf16 values, NULL couplings and residuals. The full workload (batch 32, hidden 4096, 64
+bit. Edge cases: one sequence, ragged batches (17: two activation blocks per flow; 70: slices of
+32), one expert, every expert selected, an expert chosen by every sequence, experts chosen by none,
+inputs that are not exact bf16 values, NULL couplings and residuals. The full workload (batch 32, hidden 4096, 64
 experts of width 1024, fan-outs 4 and 8) is checked on every sequence.
 """
 import numpy as np
@@ -111,6 +111,8 @@ SMALL = {
     "one_expert": W.MoeConfig("one", batch=9, hidden=256, mlp=256, experts=1, k1=1, k2=1, w_std=0.05),
     "max_fanout": W.MoeConfig("wide", batch=3, hidden=128, mlp=128, experts=40, k1=1, k2=32, w_std=0.05),
     "max_experts": W.MoeConfig("e1024", batch=6, hidden=128, mlp=128, experts=1024, k1=2, k2=8, w_std=0.05),
+    # beyond 32 sequences: the expert GEMVs and the combination run in slices of 32 (the last one ragged)
+    "b70": W.MoeConfig("b70", batch=70, hidden=256, mlp=128, experts=8, k1=2, k2=4, w_std=0.05),
 }
 
 

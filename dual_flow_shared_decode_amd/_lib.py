@@ -23,7 +23,7 @@ EXPORTS = ["dfa_decode_attn_split_len", "dfa_decode_attn_num_splits", "dfa_decod
            "dfa_dual_gemv_workspace_size", "dfa_dual_gemv", "dfa_pack_weight",
            "dfa_decode_layer_workspace_size", "dfa_decode_layer", "dfa_decode_stack_workspace_size",
            "dfa_decode_stack",
-           "dfa_mixture_workspace_size", "dfa_mixture_sample",
+           "dfa_mixture_workspace_size", "dfa_mixture_sample", "dfa_output_head_workspace_size", "dfa_output_head",
            "dfa_moe_routing_size", "dfa_moe_route", "dfa_moe_workspace_size", "dfa_moe_ffn", "dfa_prefill",
            "dfa_status_string", "dfa_last_error", "dfa_version", "dfa_stream_read", "dfa_stream_read_sink_bytes"]
 
@@ -99,6 +99,13 @@ class MixtureDesc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("vocab", ctypes.c_int32)]
 
 
+class HeadDesc(ctypes.Structure):
+    """Mirror of dfa_head_desc."""
+
+    _fields_ = [("batch", ctypes.c_int32), ("vocab", ctypes.c_int32), ("hidden", ctypes.c_int32),
+                ("x_exact_bf16", ctypes.c_int32)]
+
+
 class MoeDesc(ctypes.Structure):
     """Mirror of dfa_moe_desc."""
 
@@ -152,6 +159,9 @@ def lib() -> ctypes.CDLL:
             "dfa_mixture_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(MixtureDesc)]),
             "dfa_mixture_sample": (ctypes.c_int, [ctypes.POINTER(MixtureDesc), _P, _P, _P, _P, _P, _P, _P, _P,
                                                   ctypes.c_size_t, _P]),
+            "dfa_output_head_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(HeadDesc)]),
+            "dfa_output_head": (ctypes.c_int, [ctypes.POINTER(HeadDesc), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                               ctypes.c_size_t, _P]),
             "dfa_moe_routing_size": (ctypes.c_size_t, [ctypes.POINTER(MoeDesc)]),
             "dfa_moe_route": (ctypes.c_int, [ctypes.POINTER(MoeDesc), _P, _P, _P, ctypes.c_size_t, _P]),
             "dfa_moe_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(MoeDesc)]),
@@ -329,6 +339,17 @@ def dfa_mixture_sample(desc, logits1, logits2, u, token, greedy, alpha, p_mix, w
     _check(lib().dfa_mixture_sample(ctypes.byref(desc), _ptr(logits1), _ptr(logits2), _ptr(u), _ptr(token),
                                     _ptr(greedy), _ptr(alpha), _ptr(p_mix), _ptr(workspace), ws_bytes,
                                     _stream(stream)))
+
+
+def dfa_output_head_workspace_size(desc: HeadDesc) -> int:
+    return lib().dfa_output_head_workspace_size(ctypes.byref(desc))
+
+
+def dfa_output_head(desc, w_vocab, h1, h2, u, logits1, logits2, token, greedy, alpha, p_mix, workspace, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().dfa_output_head(ctypes.byref(desc), _ptr(w_vocab), _ptr(h1), _ptr(h2), _ptr(u), _ptr(logits1),
+                                 _ptr(logits2), _ptr(token), _ptr(greedy), _ptr(alpha), _ptr(p_mix), _ptr(workspace),
+                                 ws_bytes, _stream(stream)))
 
 
 def dfa_moe_routing_size(desc: MoeDesc) -> int:

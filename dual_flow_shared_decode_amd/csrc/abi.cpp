@@ -282,7 +282,8 @@ size_t gemv_workspace(const dfa_gemv_desc* d, const GemvPlan& pl) {
 
 dfa_status gemv_impl(const dfa_gemv_desc* d, const uint16_t* w, const uint16_t* w2, const float* x1,
                      const float* x2, const float* couple, const float* res1, const float* res2, float* y1,
-                     float* y2, const dfa_kv_target* kv, void* workspace, size_t ws_bytes, hipStream_t hs) {
+                     float* y2, const dfa_kv_target* kv, void* workspace, size_t ws_bytes, hipStream_t hs,
+                     float* head_rec = nullptr) {
   {
     GemvPlan pl;
     dfa_status st = validate_gemv(d, &pl);
@@ -367,6 +368,10 @@ dfa_status gemv_impl(const dfa_gemv_desc* d, const uint16_t* w, const uint16_t* 
       if (kvapp) {
         q.kv_table = p.kv_table + size_t(b0) * p.kv_max_blocks;
         q.kv_ctx = p.kv_ctx + b0;
+      }
+      if (head_rec) {  // the output head's tile statistics (one k-range)
+        q.head_nrec = d->n / ps.rows_per_wg;
+        q.head_rec = head_rec + size_t(b0) * q.head_nrec * dfa::kMixRec;
       }
       hipError_t e = dfa::launch_gemv(q, hs);
       if (e != hipSuccess) return fail(DFA_ERR_HIP, std::string("gemv launch: ") + hipGetErrorString(e));
@@ -774,6 +779,84 @@ dfa_status dfa_mixture_sample(const dfa_mixture_desc* d, const float* logits1, c
     p.crec = reinterpret_cast<uint32_t*>(p.rec + size_t(p.batch) * p.chunks * dfa::kMixRec);
     const hipError_t e = dfa::launch_mixture(p, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(DFA_ERR_HIP, std::string("mixture launch: ") + hipGetErrorString(e));
+    return DFA_OK;
+  } catch (...) {
+    return fail(DFA_ERR_HIP, "unexpected host exception");
+  }
+}
+
+// ------------------------------------------------------------------ fused output head
+struct HeadPlan {
+  dfa_gemv_desc gemv;
+  GemvPlan gp;
+  bool fused;           // the GEMV writes tile statistics (one k-range)
+  int32_t nrec, chunks;
+  size_t gemv_off, rec_off, crec_off, total;
+};
+
+static dfa_status plan_head(const dfa_head_desc* d, HeadPlan* hp) {
+  if (!d) return fail(DFA_ERR_NULL, "desc is NULL");
+  if (d->batch < 1 || d->batch > 65535) return fail(DFA_ERR_SHAPE, "batch must be in [1, 65535]");
+  if (d->vocab < 64 || d->vocab % 64 != 0 || d->vocab > (1 << 20))
+    return fail(DFA_ERR_SHAPE, "vocab must be a multiple of 64 in [64, 2^20]");
+  if (d->hidden < 128 || d->hidden % 128 != 0) return fail(DFA_ERR_SHAPE, "hidden must be a positive multiple of 128");
+  HeadPlan h{};
+  h.gemv = dfa_gemv_desc{d->batch, d->vocab, d->hidden, 2, DFA_EPI_NONE, d->x_exact_bf16 ? 1 : 0, 0, 0};
+  const dfa_status st = validate_gemv(&h.gemv, &h.gp);
+  if (st != DFA_OK) return st;
+  h.fused = h.gp.k_split == 1;
+  h.nrec = d->vocab / h.gp.rows_per_wg;
+  h.chunks = int32_t(dfa::mixture_chunks(d->vocab));
+  const size_t B = size_t(d->batch);
+  h.gemv_off = 0;
+  h.rec_off = align256(gemv_workspace(&h.gemv, h.gp));
+  h.crec_off = h.rec_off + align256(B * (h.fused ? h.nrec : h.chunks) * dfa::kMixRec * sizeof(float));
+  h.total = h.crec_off + align256(B * h.chunks * 4 * sizeof(uint32_t));
+  if (hp) *hp = h;
+  return DFA_OK;
+}
+
+size_t dfa_output_head_workspace_size(const dfa_head_desc* d) {
+  HeadPlan h;
+  return plan_head(d, &h) == DFA_OK ? h.total : 0;
+}
+
+dfa_status dfa_output_head(const dfa_head_desc* d, const uint16_t* w_vocab, const float* h1, const float* h2,
+                           const float* u, float* logits1, float* logits2, int32_t* token, int32_t* greedy,
+                           float* alpha, float* p_mix, void* workspace, size_t ws_bytes, void* stream) {
+  try {
+    HeadPlan h;
+    dfa_status st = plan_head(d, &h);
+    if (st != DFA_OK) return st;
+    if (!w_vocab || !h1 || !h2 || !u || !logits1 || !logits2 || !token || !greedy || !alpha)
+      return fail(DFA_ERR_NULL, "w_vocab, h1, h2, u, logits1, logits2, token, greedy and alpha are required");
+    const void* ptrs[] = {w_vocab, h1, h2, logits1, logits2, p_mix, workspace};
+    for (const void* q : ptrs)
+      if (q && !aligned16(q)) return fail(DFA_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
+    if (!workspace || ws_bytes < h.total)
+      return fail(DFA_ERR_WORKSPACE, "workspace smaller than dfa_output_head_workspace_size()");
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(workspace);
+    float* rec = reinterpret_cast<float*>(ws + h.rec_off);
+    st = gemv_impl(&h.gemv, w_vocab, nullptr, h1, h2, nullptr, nullptr, nullptr, logits1, logits2, nullptr,
+                   ws + h.gemv_off, h.rec_off - h.gemv_off, hs, h.fused ? rec : nullptr);
+    if (st != DFA_OK) return st;
+    dfa::MixParams p{};
+    p.logits1 = logits1;
+    p.logits2 = logits2;
+    p.u = u;
+    p.token = token;
+    p.greedy = greedy;
+    p.alpha = alpha;
+    p.p_mix = p_mix;
+    p.batch = d->batch;
+    p.vocab = d->vocab;
+    p.chunks = h.chunks;
+    p.nrec = h.fused ? h.nrec : 0;
+    p.rec = rec;
+    p.crec = reinterpret_cast<uint32_t*>(ws + h.crec_off);
+    const hipError_t e = h.fused ? dfa::launch_mixture_tiles(p, hs) : dfa::launch_mixture(p, hs);
+    if (e != hipSuccess) return fail(DFA_ERR_HIP, std::string("output head mixture launch: ") + hipGetErrorString(e));
     return DFA_OK;
   } catch (...) {
     return fail(DFA_ERR_HIP, "unexpected host exception");

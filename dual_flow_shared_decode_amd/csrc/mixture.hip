@@ -91,15 +91,17 @@ __device__ __forceinline__ Norm merge_records(const float* rec, int chunks) {
 
 // p_mix of the four tokens v..v+3 (explicit fused operations: the same bits in
 // every kernel that evaluates them).
-__device__ __forceinline__ float4 mix4(const float* l1, const float* l2, int v, const Norm& n) {
-  const float4 a = *(const float4*)(l1 + v);
-  const float4 c = *(const float4*)(l2 + v);
+__device__ __forceinline__ float4 mix4v(const float4& a, const float4& c, const Norm& n) {
   float4 q;
   q.x = __builtin_fmaf(n.w1, ex2((a.x - n.m1) * kLog2e), n.w2 * ex2((c.x - n.m2) * kLog2e));
   q.y = __builtin_fmaf(n.w1, ex2((a.y - n.m1) * kLog2e), n.w2 * ex2((c.y - n.m2) * kLog2e));
   q.z = __builtin_fmaf(n.w1, ex2((a.z - n.m1) * kLog2e), n.w2 * ex2((c.z - n.m2) * kLog2e));
   q.w = __builtin_fmaf(n.w1, ex2((a.w - n.m1) * kLog2e), n.w2 * ex2((c.w - n.m2) * kLog2e));
   return q;
+}
+
+__device__ __forceinline__ float4 mix4(const float* l1, const float* l2, int v, const Norm& n) {
+  return mix4v(*(const float4*)(l1 + v), *(const float4*)(l2 + v), n);
 }
 
 // Integer mass of a probability: q * 2^35 truncated; 0 for NaN (a row with a
@@ -180,6 +182,81 @@ __device__ __forceinline__ float block_reduce(float v, float* sh, bool is_max) {
   for (int w = 1; w < kMixWaves; ++w) r = is_max ? fmaxf(r, sh[w]) : r + sh[w];
   return r;
 }
+
+// The sequence's softmax normalisers and alpha from nrec records of the
+// output-head GEMV's tiles (global memory, same fields as the chunk records):
+// each thread folds records t, t + kMixThreads, ... in order (a running max,
+// its sums rescaled when it moves), then fixed-order workgroup reductions (the
+// two maxima together, then the three sums together), so every workgroup
+// computes the same values.
+__device__ __forceinline__ Norm merge_tile_records(const float* rec, int nrec, float* sh) {
+  float m1 = -INFINITY, m2 = -INFINITY, s1 = 0.f, q1 = 0.f, s2 = 0.f;
+  for (int t = threadIdx.x; t < nrec; t += kMixThreads) {
+    const float* r = rec + (size_t)t * kMixRec;
+    const float4 a = *(const float4*)r;  // m1, s1, q1, m2
+    const float b = r[4];                // s2
+    const float n1 = fmaxf(m1, a.x), n2 = fmaxf(m2, a.w);
+    if (n1 > -INFINITY) {
+      const float c = ex2((m1 - n1) * kLog2e), e = ex2((a.x - n1) * kLog2e);
+      s1 = __builtin_fmaf(a.y, e, s1 * c);
+      q1 = __builtin_fmaf(a.z, e * e, q1 * (c * c));
+    }
+    if (n2 > -INFINITY) s2 = __builtin_fmaf(b, ex2((a.w - n2) * kLog2e), s2 * ex2((m2 - n2) * kLog2e));
+    m1 = n1;
+    m2 = n2;
+  }
+  // maxima of both flows: lanes, then waves in order
+  float x1 = m1, x2 = m2;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    x1 = fmaxf(x1, __shfl_xor(x1, m));
+    x2 = fmaxf(x2, __shfl_xor(x2, m));
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) {
+    sh[2 * wave] = x1;
+    sh[2 * wave + 1] = x2;
+  }
+  __syncthreads();
+  Norm n;
+  n.m1 = sh[0];
+  n.m2 = sh[1];
+#pragma unroll
+  for (int w = 1; w < kMixWaves; ++w) {
+    n.m1 = fmaxf(n.m1, sh[2 * w]);
+    n.m2 = fmaxf(n.m2, sh[2 * w + 1]);
+  }
+  // this thread's sums at the row maxima, then the three sums: lanes, then waves in order
+  const float c1 = m1 > -INFINITY ? ex2((m1 - n.m1) * kLog2e) : 0.f;
+  const float c2 = m2 > -INFINITY ? ex2((m2 - n.m2) * kLog2e) : 0.f;
+  float y1 = s1 * c1, y2 = q1 * (c1 * c1), y3 = s2 * c2;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    y1 += __shfl_xor(y1, m);
+    y2 += __shfl_xor(y2, m);
+    y3 += __shfl_xor(y3, m);
+  }
+  __syncthreads();
+  if (lane == 0) {
+    sh[4 * wave] = y1;
+    sh[4 * wave + 1] = y2;
+    sh[4 * wave + 2] = y3;
+  }
+  __syncthreads();
+  float t1 = sh[0], t2 = sh[1], t3 = sh[2];
+#pragma unroll
+  for (int w = 1; w < kMixWaves; ++w) {
+    t1 += sh[4 * w];
+    t2 += sh[4 * w + 1];
+    t3 += sh[4 * w + 2];
+  }
+  const float collision = t2 / (t1 * t1);
+  n.alpha = __builtin_fmaf(0.5f, collision, 0.5f);
+  n.w1 = n.alpha / t1;
+  n.w2 = (1.f - n.alpha) / t3;
+  return n;
+}
 }  // namespace
 
 // rec[b][chunk][0..4] = {m1, s1, q1, m2, s2}: m = the chunk's largest logit,
@@ -226,19 +303,35 @@ __global__ __launch_bounds__(kMixThreads) void mix_stats_kernel(MixParams p) {
 }
 
 // crec[b][chunk] = {mass (low, high word), first maximum's value bits, its token};
-// alpha[b] from chunk 0.
+// alpha[b] from chunk 0. TILES: the statistics are the output-head GEMV's
+// nrec tile records per sequence rather than the chunk records.
+template <bool TILES>
 __global__ __launch_bounds__(kMixThreads) void mix_chunk_kernel(MixParams p) {
+  __shared__ float shr[TILES ? 4 * kMixWaves : 1];
   __shared__ uint64_t shm[kMixWaves];
   __shared__ float shv[kMixWaves];
   __shared__ int shi[kMixWaves];
-  __shared__ float srec[kMixMaxChunks][kMixRec];
+  __shared__ float srec[TILES ? 1 : kMixMaxChunks][kMixRec];
   const int chunk = blockIdx.x, b = blockIdx.y;
-  stage_records(p.rec + (size_t)b * p.chunks * kMixRec, p.chunks, srec);
-  const Norm n = merge_records(&srec[0][0], p.chunks);
+  // the chunk's logits are loaded first: their round trip overlaps the records'
   const float* l1 = p.logits1 + (size_t)b * p.vocab;
   const float* l2 = p.logits2 + (size_t)b * p.vocab;
-  float* pm = p.p_mix ? p.p_mix + (size_t)b * p.vocab : nullptr;
   const int v0 = chunk * kMixChunk + threadIdx.x * kRun;
+  float4 la[kRun / 4], lc[kRun / 4];
+#pragma unroll
+  for (int i = 0; i < kRun / 4; ++i) {
+    const int v = v0 + 4 * i;
+    la[i] = v < p.vocab ? *(const float4*)(l1 + v) : make_float4(0.f, 0.f, 0.f, 0.f);
+    lc[i] = v < p.vocab ? *(const float4*)(l2 + v) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  Norm n;
+  if constexpr (TILES) {
+    n = merge_tile_records(p.rec + (size_t)b * p.nrec * kMixRec, p.nrec, shr);
+  } else {
+    stage_records(p.rec + (size_t)b * p.chunks * kMixRec, p.chunks, srec);
+    n = merge_records(&srec[0][0], p.chunks);
+  }
+  float* pm = p.p_mix ? p.p_mix + (size_t)b * p.vocab : nullptr;
   uint64_t mass = 0;
   float bv = -1.f;
   int bi = p.vocab;
@@ -246,7 +339,7 @@ __global__ __launch_bounds__(kMixThreads) void mix_chunk_kernel(MixParams p) {
   for (int i = 0; i < kRun / 4; ++i) {
     const int v = v0 + 4 * i;
     if (v < p.vocab) {
-      const float4 q = mix4(l1, l2, v, n);
+      const float4 q = mix4v(la[i], lc[i], n);
       if (pm) *(float4*)(pm + v) = q;
       const float qs[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
@@ -269,13 +362,15 @@ __global__ __launch_bounds__(kMixThreads) void mix_chunk_kernel(MixParams p) {
   }
 }
 
+template <bool TILES>
 __global__ __launch_bounds__(kMixThreads) void mix_pick_kernel(MixParams p) {
+  __shared__ float shr[TILES ? 4 * kMixWaves : 1];
   __shared__ uint64_t shm[kMixWaves];
   __shared__ float shv[kMixWaves];
   __shared__ int shi[kMixWaves];
   __shared__ int sel_chunk, sel_tok;
   __shared__ uint64_t sel_base;
-  __shared__ float srec[kMixMaxChunks][kMixRec];
+  __shared__ float srec[TILES ? 1 : kMixMaxChunks][kMixRec];
   const int b = blockIdx.x, t = threadIdx.x;
   // ---- chunk level: one chunk record per thread (loaded with the statistics) ----
   uint64_t mass = 0;
@@ -283,8 +378,13 @@ __global__ __launch_bounds__(kMixThreads) void mix_pick_kernel(MixParams p) {
   int bi = p.vocab;
   uint4 r = make_uint4(0u, 0u, 0u, 0u);
   if (t < p.chunks) r = *(const uint4*)(p.crec + ((size_t)b * p.chunks + t) * 4);
-  stage_records(p.rec + (size_t)b * p.chunks * kMixRec, p.chunks, srec);
-  const Norm n = merge_records(&srec[0][0], p.chunks);
+  Norm n;
+  if constexpr (TILES) {
+    n = merge_tile_records(p.rec + (size_t)b * p.nrec * kMixRec, p.nrec, shr);
+  } else {
+    stage_records(p.rec + (size_t)b * p.chunks * kMixRec, p.chunks, srec);
+    n = merge_records(&srec[0][0], p.chunks);
+  }
   if (t < p.chunks) {
     mass = ((uint64_t)r.y << 32) | r.x;
     bv = __uint_as_float(r.z);
@@ -580,10 +680,18 @@ hipError_t launch_mixture(const MixParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(mix_stats_kernel, dim3(p.chunks, p.batch), dim3(kMixThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(mix_chunk_kernel, dim3(p.chunks, p.batch), dim3(kMixThreads), 0, stream, p);
+  hipLaunchKernelGGL(mix_chunk_kernel<false>, dim3(p.chunks, p.batch), dim3(kMixThreads), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(mix_pick_kernel, dim3(p.batch), dim3(kMixThreads), 0, stream, p);
+  hipLaunchKernelGGL(mix_pick_kernel<false>, dim3(p.batch), dim3(kMixThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_mixture_tiles(const MixParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL(mix_chunk_kernel<true>, dim3(p.chunks, p.batch), dim3(kMixThreads), 0, stream, p);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(mix_pick_kernel<true>, dim3(p.batch), dim3(kMixThreads), 0, stream, p);
   return hipGetLastError();
 }
 

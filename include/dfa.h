@@ -445,6 +445,42 @@ DFA_API dfa_status dfa_mixture_sample(const dfa_mixture_desc* desc, const float*
                                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * ------------------------------------------------------ fused output head
+ * Both flows' logits from one read of the shared vocabulary matrix, then the
+ * mixture decoding above ("Mecanismos Chave", mixture objective; one output
+ * matrix shared by the flows, "Arquitetura Central"):
+ *     logits_f = h_f W^T  (W: bf16 [vocab, hidden], tiled by dfa_pack_weight)
+ * and token, greedy, alpha and (optionally) p_mix exactly as
+ * dfa_mixture_sample defines them for these logits. The GEMV writes, besides
+ * the logits, the softmax statistics of each of its vocabulary tiles, so the
+ * mixture reads the logits once (spread over (chunk, sequence) workgroups)
+ * instead of a statistics pass first. When the GEMV plan splits k (vocab
+ * below 24576 at hidden 4096) the statistics are not fused: the GEMV and
+ * its reduction run, then the kernels of dfa_mixture_sample.
+ *  h1, h2:          float32 [batch, hidden] final hidden states of the flows
+ *  u:               float32 [batch] uniforms
+ *  logits1, logits2: float32 [batch, vocab] outputs (required: the mixture
+ *                   reads them back)
+ *  token, greedy, alpha, p_mix: as dfa_mixture_sample (p_mix may be NULL)
+ *  workspace:       dfa_output_head_workspace_size bytes, 16-byte aligned
+ * Limits: batch 1..65535 (the GEMV in slices of 32 sequences); vocab a
+ * multiple of 64 in [64, 2^20]; hidden a multiple of 128.
+ */
+typedef struct dfa_head_desc {
+  int32_t batch;
+  int32_t vocab;
+  int32_t hidden;
+  int32_t x_exact_bf16;  /* 1: h1 and h2 hold exact bf16 values */
+} dfa_head_desc;
+
+DFA_API size_t dfa_output_head_workspace_size(const dfa_head_desc* desc);
+
+DFA_API dfa_status dfa_output_head(const dfa_head_desc* desc, const uint16_t* w_vocab, const float* h1,
+                                   const float* h2, const float* u, float* logits1, float* logits2, int32_t* token,
+                                   int32_t* greedy, float* alpha, float* p_mix, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/*
  * ------------------------------------------- mixture-of-experts FFN (router replay)
  * A SwiGLU mixture-of-experts FFN for both flows at one decode step ("Mecanismos
  * Chave", router replay: the auxiliary flow reuses the experts the primary

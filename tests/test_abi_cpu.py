@@ -361,3 +361,33 @@ def test_table_check_validation():
         with pytest.raises(dfa.DfaError) as e:
             call(c2_desc(**kw), **args)
         assert _lib.STATUS[e.value.status] == status, (kw, args)
+
+
+def test_output_head_plans_and_validation():
+    """dfa_output_head: the workspace of the fused plan (tile records + chunk records) and of the
+    split-k plan (GEMV partials + mixture records); every error on the host."""
+    head = lambda **kw: dfa.HeadDesc(**{**dict(batch=32, vocab=32000, hidden=4096, x_exact_bf16=1), **kw})
+    up = lambda x: (x + 255) // 256 * 256
+    # 32000 x 4096: 250 tiles of 128 rows, one k-range; 8 chunks of 4096 tokens
+    assert dfa.dfa_output_head_workspace_size(head()) == up(32 * 250 * 8 * 4) + up(32 * 8 * 16)
+    # 4160 x 512: 65 row groups of 64 split k (4 ranges of 128 columns): partials, then chunk records
+    gd = dfa.GemvDesc(batch=3, n=4160, k=512, num_flows=2, epilogue=0, x_exact_bf16=1, k_split=0, rows_per_wg=0)
+    g = dfa.dfa_dual_gemv_workspace_size(gd)
+    assert g > 0
+    assert dfa.dfa_output_head_workspace_size(head(batch=3, vocab=4160, hidden=512)) == up(g) + up(3 * 2 * 8 * 4) + \
+        up(3 * 2 * 16)
+    for bad in (dict(batch=0), dict(batch=65536), dict(vocab=32001), dict(vocab=0), dict(vocab=(1 << 20) + 64),
+                dict(hidden=100)):
+        assert dfa.dfa_output_head_workspace_size(head(**bad)) == 0, bad
+    call = lambda d, **kw: _lib._check(_lib.lib().dfa_output_head(
+        ctypes.byref(d), *[kw.get(n, FAKE) for n in ("w", "h1", "h2", "u", "l1", "l2", "tok", "gr", "al")],
+        kw.get("pm"), kw.get("ws", FAKE), kw.get("wsb", 1 << 30), None))
+    for kw, status in ((dict(w=None), "DFA_ERR_NULL"), (dict(l2=None), "DFA_ERR_NULL"),
+                       (dict(h1=FAKE + 4), "DFA_ERR_ALIGNMENT"), (dict(ws=None), "DFA_ERR_WORKSPACE"),
+                       (dict(wsb=16), "DFA_ERR_WORKSPACE")):
+        with pytest.raises(dfa.DfaError) as e:
+            call(head(), **kw)
+        assert _lib.STATUS[e.value.status] == status, kw
+    with pytest.raises(dfa.DfaError) as e:
+        call(head(vocab=100))
+    assert _lib.STATUS[e.value.status] == "DFA_ERR_SHAPE"

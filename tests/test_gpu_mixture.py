@@ -14,6 +14,12 @@ the inverse-CDF token for the caller's uniform u. Bars:
   cumulative bounds of the returned token contain u up to 1e-4, and that the
   token is the oracle's own wherever u is farther than that from a boundary.
 
+The fused output head (dfa_output_head: the GEMV writes each vocabulary tile's
+softmax statistics, the mixture merges them) is held to the same bars, on
+128- and 64-row tiles, sliced batches, more than one chunk, and the plan that
+falls back to the separate kernels; against the two-call path its logits are
+bit for bit the same and alpha and p_mix agree to rounding.
+
 Exact properties of the library's own outputs (bit for bit): the token is the
 inverse-CDF token of the returned p_mix under the library's stated integer
 masses (each value scaled by 2^35 and truncated; target = floor(u * total)),
@@ -200,6 +206,71 @@ def test_dual_output_head(cfg):
     assert_close(g1, r1, TOL, "logits 1")
     assert_close(g2, r2, TOL, "logits 2")
     check_against_oracle(got, r1, r2, u, "head")
+
+
+def run_fused_head(cfg, seed, with_p_mix=True):
+    """dfa_output_head: both flows' logits and, from the GEMV's tile statistics, the mixture."""
+    h1, h2, w_bits, u = W.make_head_case(cfg, seed)
+    wdev = to_device(w_bits)
+    wt = torch.empty_like(wdev)
+    dfa.dfa_pack_weight(wdev, wt, cfg.vocab, cfg.hidden)
+    del wdev
+    d = dfa.HeadDesc(batch=cfg.batch, vocab=cfg.vocab, hidden=cfg.hidden, x_exact_bf16=1)
+    ws = torch.full((dfa.dfa_output_head_workspace_size(d) // 4,), float("nan"), device="cuda")
+    b, v = cfg.batch, cfg.vocab
+    y1 = torch.full((b, v), float("nan"), device="cuda")
+    y2 = torch.full_like(y1, float("nan"))
+    tok = torch.full((b,), -7, dtype=torch.int32, device="cuda")
+    gr = torch.full((b,), -7, dtype=torch.int32, device="cuda")
+    al = torch.full((b,), float("nan"), device="cuda")
+    pm = torch.full((b, v), float("nan"), device="cuda") if with_p_mix else None
+    dfa.dfa_output_head(d, wt, to_device(h1), to_device(h2), to_device(u), y1, y2, tok, gr, al, pm, ws)
+    torch.cuda.synchronize()
+    got = {"token": tok.cpu().numpy(), "greedy": gr.cpu().numpy(), "alpha": al.cpu().numpy()}
+    if with_p_mix:
+        got["p_mix"] = pm.cpu().numpy()
+    return h1, h2, w_bits, u, (y1.cpu().numpy(), y2.cpu().numpy()), got
+
+
+HEADS = {
+    # 32000 x 4096: 128-row tiles, one k-range -> 250 tile records per sequence (statistics fused)
+    "head": W.HEAD,
+    # 64-row tiles (a matrix under 48 Mi elements), 192 and 625 tiles, the latter over ten 4096-token chunks
+    "tiles64": W.HEAD.replace(batch=5, hidden=1024, vocab=12288),
+    "chunks10": W.HEAD.replace(batch=3, hidden=512, vocab=40000),
+    # 40 sequences: the GEMV in slices of 32, the mixture over all 40
+    "batch40": W.HEAD.replace(batch=40, hidden=1024, vocab=32000),
+    # a plan that splits k (too few row groups): GEMV, reduction, then the mixture's own kernels
+    "split": W.HEAD.replace(batch=3, hidden=512, vocab=4096 + 64),
+}
+
+
+@pytest.mark.parametrize("name", list(HEADS))
+def test_fused_output_head(name):
+    cfg = HEADS[name]
+    say(f"case fused output head {name}: batch {cfg.batch} hidden {cfg.hidden} vocab {cfg.vocab}")
+    h1, h2, w_bits, u, (g1, g2), got = run_fused_head(cfg, W.SEEDS["head"])
+    r1, r2 = LY.linear(h1, w_bits), LY.linear(h2, w_bits)
+    assert_close(g1, r1, TOL, "logits 1")
+    assert_close(g2, r2, TOL, "logits 2")
+    check_against_oracle(got, r1, r2, u, name)
+    # without p_mix: the same tokens and alpha
+    *_, got2 = run_fused_head(cfg, W.SEEDS["head"], with_p_mix=False)
+    for k in ("token", "greedy", "alpha"):
+        assert np.array_equal(got2[k], got[k]), k
+
+
+def test_fused_head_matches_the_two_call_path():
+    """The fused head and dfa_dual_gemv + dfa_mixture_sample compute the same logits bit for bit; alpha
+    and p_mix agree to rounding (normalisers merged from 128-token tiles instead of in one pass), and
+    each path's tokens are exact for its own p_mix."""
+    cfg = W.HEAD.replace(batch=8)
+    say("case fused head vs two calls")
+    *_, (f1, f2), fused = run_fused_head(cfg, 91)
+    *_, (t1, t2), two = run_head(cfg, 91)
+    assert np.array_equal(f1, t1) and np.array_equal(f2, t2)
+    assert np.max(np.abs(fused["alpha"] - two["alpha"])) <= 1e-6
+    assert_close(fused["p_mix"], two["p_mix"], 1e-5, "p_mix fused vs two calls")
 
 
 @pytest.mark.parametrize("vocab", [32000, 40000])

@@ -31,12 +31,21 @@ std::atomic<void*> g_scratch_ptr[kMaxDevices];
 std::mutex g_init_mu;
 
 // Device address of the current device's copy of `scratch`, looked up on the
-// first call on that device.
-dfa_status scratch_of_current_device(void** out) {
+// first call on that device. A stream of another device is refused: its
+// kernels would read this device's copy.
+dfa_status scratch_of_current_device(hipStream_t stream, void** out) {
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return dfa::report_error(DFA_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
   if (dev < 0 || dev >= kMaxDevices) return dfa::report_error(DFA_ERR_UNSUPPORTED, "device index above 63");
+  if (stream) {
+    hipDevice_t sdev = -1;
+    e = hipStreamGetDevice(stream, &sdev);
+    if (e != hipSuccess) return dfa::report_error(DFA_ERR_HIP, std::string("hipStreamGetDevice: ") + hipGetErrorString(e));
+    if (sdev != dev)
+      return dfa::report_error(DFA_ERR_UNSUPPORTED, "dfa_decode_attn_noalloc: the stream belongs to another device "
+                                                    "than the current one");
+  }
   void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
   if (!p) {
     std::lock_guard<std::mutex> lock(g_init_mu);
@@ -75,7 +84,7 @@ extern "C" dfa_status dfa_decode_attn_noalloc(const dfa_attn_desc* desc, const v
                                    std::to_string(DFA_NOALLOC_SCRATCH_BYTES) +
                                    " bytes; use dfa_decode_attn with a workspace");
     void* ws = nullptr;
-    const dfa_status st = scratch_of_current_device(&ws);
+    const dfa_status st = scratch_of_current_device(static_cast<hipStream_t>(stream), &ws);
     if (st != DFA_OK) return st;
     return dfa_decode_attn(desc, q1, q2, a, k_cache, v_cache, block_table, ctx_lens, ws, DFA_NOALLOC_SCRATCH_BYTES,
                            o1, o2, stream);

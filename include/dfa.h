@@ -176,8 +176,9 @@ DFA_API dfa_status dfa_check_kv_table(const dfa_attn_desc* desc, const int32_t* 
  * current); no call allocates or frees memory.
  * Limit: dfa_decode_attn_workspace_size(desc) <= DFA_NOALLOC_SCRATCH_BYTES
  * whenever more than one split runs (checked on the host: DFA_ERR_WORKSPACE,
- * nothing enqueued). Calls on one GPU share the array: calls that overlap in
- * time (on different streams) race and must not be issued.
+ * nothing enqueued). `stream` must belong to the current device
+ * (DFA_ERR_UNSUPPORTED otherwise). Calls on one GPU share the array: calls
+ * that overlap in time (on different streams) race and must not be issued.
  */
 #define DFA_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
 DFA_API dfa_status dfa_decode_attn_noalloc(const dfa_attn_desc* desc, const void* q1, const void* q2,

@@ -60,6 +60,10 @@ __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f3
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return min(max(x, lo), hi); }
 
+// Larger of two scores, NaN-propagating (IEEE maximum): no quieting of its
+// inputs first, unlike fmaxf under the IEEE mode kernels run in.
+__device__ __forceinline__ float max2(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // Max over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four k-groups of an MFMA
 // column). A register swapped with itself by v_permlane16_swap (odd 16-lane
 // rows against even ones) or v_permlane32_swap (upper 32 lanes against lower)
@@ -67,9 +71,9 @@ __device__ __forceinline__ int clampi(int x, int lo, int hi) { return min(max(x,
 // are VALU operations, no trip through LDS.
 __device__ __forceinline__ float max_over_groups(float x) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  x = max2(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return max2(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 // Physical block of position t of prompt b (clamped into the cache).
@@ -167,7 +171,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillParams 
   }
   const int b = pair / p.hkv, g = pair - b * p.hkv;
   const int qb = nqb - 1 - rank;  // longest blocks first
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, grp = lane >> 4;
   const int gl2 = p.g_log2;
   const int pos_per_wg = kPfRows >> gl2;
@@ -205,7 +209,9 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillParams 
   const int nblk = (last_tile >> p.bs_log2) + 1;  // at most kPfTable (checked on the host)
   for (int i = threadIdx.x; i < nblk; i += kPfThreads) tbl[i] = block_of(p, b, i << p.bs_log2);
   auto tile_of = [&](int tt) __attribute__((always_inline)) {
-    return (size_t)tbl[tt >> p.bs_log2] * p.blk_stride + head_off + (size_t)((tt & (bs - 1)) >> 4) * kTile;
+    // the block id is the same in every lane: scalar address arithmetic
+    const int blk = __builtin_amdgcn_readfirstlane(tbl[tt >> p.bs_log2]);
+    return (size_t)blk * p.blk_stride + head_off + (size_t)((tt & (bs - 1)) >> 4) * kTile;
   };
   // Every thread issues the same loads on every path (threads past a tile's
   // pieces read its last piece again), so the compiler's count of loads in
@@ -300,7 +306,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillParams 
         }
         float cmax = sc[0];
 #pragma unroll
-        for (int j = 1; j < 8; ++j) cmax = fmaxf(cmax, sc[j]);
+        for (int j = 1; j < 8; ++j) cmax = max2(cmax, sc[j]);
         cmax = max_over_groups(cmax) * p.qscale;  // base-2 units (qscale > 0)
         const bool moves = cmax > m_run[cb] + kPfLazy;  // this row's own decision
         if (__builtin_amdgcn_ballot_w64(moves) != 0) {

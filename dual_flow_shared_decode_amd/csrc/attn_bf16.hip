@@ -54,6 +54,21 @@ __device__ __forceinline__ float dpp_ror8(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false));
 }
 
+// Larger of two scores, NaN-propagating (IEEE maximum): no quieting of its
+// inputs first, unlike fmaxf under the IEEE mode kernels run in.
+__device__ __forceinline__ float score_max(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+// Max over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four k-groups of an MFMA
+// column): v_permlane16_swap / v_permlane32_swap of a register with itself
+// leave each lane its own value and its partner's, vector ALU operations with
+// no trip through LDS.
+__device__ __forceinline__ float max_over_groups(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = score_max(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return score_max(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -315,9 +330,8 @@ __global__ __launch_bounds__(64 * kAttnWaves * RS) void attn_bf16_kernel(AttnPar
     }
     float cmax = sc[0];
 #pragma unroll
-    for (int j = 1; j < 8; ++j) cmax = fmaxf(cmax, sc[j]);
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+    for (int j = 1; j < 8; ++j) cmax = score_max(cmax, sc[j]);
+    cmax = max_over_groups(cmax);
     const bool moves = cmax > m_run + kLazyRescale;  // the same in every lane of a row
     if (__builtin_amdgcn_ballot_w64(moves) != 0) {
       const float m_new = moves ? cmax : m_run;

@@ -282,8 +282,7 @@ size_t gemv_workspace(const dfa_gemv_desc* d, const GemvPlan& pl) {
 
 dfa_status gemv_impl(const dfa_gemv_desc* d, const uint16_t* w, const uint16_t* w2, const float* x1,
                      const float* x2, const float* couple, const float* res1, const float* res2, float* y1,
-                     float* y2, const dfa_kv_target* kv, void* workspace, size_t ws_bytes, hipStream_t hs,
-                     float* head_rec = nullptr) {
+                     float* y2, const dfa_kv_target* kv, void* workspace, size_t ws_bytes, hipStream_t hs) {
   {
     GemvPlan pl;
     dfa_status st = validate_gemv(d, &pl);
@@ -368,10 +367,6 @@ dfa_status gemv_impl(const dfa_gemv_desc* d, const uint16_t* w, const uint16_t* 
       if (kvapp) {
         q.kv_table = p.kv_table + size_t(b0) * p.kv_max_blocks;
         q.kv_ctx = p.kv_ctx + b0;
-      }
-      if (head_rec) {  // the output head's tile statistics (one k-range)
-        q.head_nrec = d->n / ps.rows_per_wg;
-        q.head_rec = head_rec + size_t(b0) * q.head_nrec * dfa::kMixRec;
       }
       hipError_t e = dfa::launch_gemv(q, hs);
       if (e != hipSuccess) return fail(DFA_ERR_HIP, std::string("gemv launch: ") + hipGetErrorString(e));
@@ -785,12 +780,13 @@ dfa_status dfa_mixture_sample(const dfa_mixture_desc* d, const float* logits1, c
   }
 }
 
-// ------------------------------------------------------------------ fused output head
+// ------------------------------------------------------------------ output head
+// One call: both flows' logits (the dual GEMV over the vocabulary matrix), then the mixture
+// kernels of dfa_mixture_sample on them, sharing one workspace.
 struct HeadPlan {
   dfa_gemv_desc gemv;
   GemvPlan gp;
-  bool fused;           // the GEMV writes tile statistics (one k-range)
-  int32_t nrec, chunks;
+  int32_t chunks;
   size_t gemv_off, rec_off, crec_off, total;
 };
 
@@ -804,13 +800,11 @@ static dfa_status plan_head(const dfa_head_desc* d, HeadPlan* hp) {
   h.gemv = dfa_gemv_desc{d->batch, d->vocab, d->hidden, 2, DFA_EPI_NONE, d->x_exact_bf16 ? 1 : 0, 0, 0};
   const dfa_status st = validate_gemv(&h.gemv, &h.gp);
   if (st != DFA_OK) return st;
-  h.fused = h.gp.k_split == 1;
-  h.nrec = d->vocab / h.gp.rows_per_wg;
   h.chunks = int32_t(dfa::mixture_chunks(d->vocab));
   const size_t B = size_t(d->batch);
   h.gemv_off = 0;
   h.rec_off = align256(gemv_workspace(&h.gemv, h.gp));
-  h.crec_off = h.rec_off + align256(B * (h.fused ? h.nrec : h.chunks) * dfa::kMixRec * sizeof(float));
+  h.crec_off = h.rec_off + align256(B * h.chunks * dfa::kMixRec * sizeof(float));
   h.total = h.crec_off + align256(B * h.chunks * 4 * sizeof(uint32_t));
   if (hp) *hp = h;
   return DFA_OK;
@@ -837,9 +831,8 @@ dfa_status dfa_output_head(const dfa_head_desc* d, const uint16_t* w_vocab, cons
       return fail(DFA_ERR_WORKSPACE, "workspace smaller than dfa_output_head_workspace_size()");
     const hipStream_t hs = static_cast<hipStream_t>(stream);
     char* ws = static_cast<char*>(workspace);
-    float* rec = reinterpret_cast<float*>(ws + h.rec_off);
     st = gemv_impl(&h.gemv, w_vocab, nullptr, h1, h2, nullptr, nullptr, nullptr, logits1, logits2, nullptr,
-                   ws + h.gemv_off, h.rec_off - h.gemv_off, hs, h.fused ? rec : nullptr);
+                   ws + h.gemv_off, h.rec_off - h.gemv_off, hs);
     if (st != DFA_OK) return st;
     dfa::MixParams p{};
     p.logits1 = logits1;
@@ -852,10 +845,9 @@ dfa_status dfa_output_head(const dfa_head_desc* d, const uint16_t* w_vocab, cons
     p.batch = d->batch;
     p.vocab = d->vocab;
     p.chunks = h.chunks;
-    p.nrec = h.fused ? h.nrec : 0;
-    p.rec = rec;
+    p.rec = reinterpret_cast<float*>(ws + h.rec_off);
     p.crec = reinterpret_cast<uint32_t*>(ws + h.crec_off);
-    const hipError_t e = h.fused ? dfa::launch_mixture_tiles(p, hs) : dfa::launch_mixture(p, hs);
+    const hipError_t e = dfa::launch_mixture(p, hs);
     if (e != hipSuccess) return fail(DFA_ERR_HIP, std::string("output head mixture launch: ") + hipGetErrorString(e));
     return DFA_OK;
   } catch (...) {

@@ -272,11 +272,7 @@ __device__ __forceinline__ void put_x(const XStage<NCB>& xr, uint16_t* xs) {
 // the workgroup multiplies its expert's matrices (moe_wstride elements apart)
 // with the rows of the sequences that selected the expert (moe_sel), found
 // here in sequence order, and exits at once if there are none. One k-range.
-//
-// STATS (output head, two flows, one k-range, no epilogue): besides the
-// logits, each workgroup writes per sequence the softmax statistics of its
-// kRowsPerWg vocabulary rows (head_rec), for the mixture's normalisers.
-template <int NCB, bool PAIR, bool LO, int TILES, bool GROUPED, bool STATS = false>
+template <int NCB, bool PAIR, bool LO, int TILES, bool GROUPED>
 __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvParams p) {
   constexpr int kTiles = TILES;                  // 16-row weight tiles per workgroup (4 or 8)
   constexpr int kGroups = kGemvWaves / kTiles;   // wave groups sharing the tiles (2 or 1)
@@ -496,51 +492,6 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvParams p) {
       apply_epilogue(p, j, o, o, n0, y);
     }
   }
-  if constexpr (STATS) {
-    // eight threads per (sequence, flow) pair: each folds kRowsPerWg / 8 of the pair's logits of
-    // this tile (staged above), then three xor steps within the eight (fixed order: the same
-    // bits in every run)
-    constexpr float kLog2e = 1.4426950408889634f;
-    constexpr int kPer = kRowsPerWg / 8;
-    const int sub = threadIdx.x & 7;
-    for (int pr = threadIdx.x >> 3; pr < ((2 * p.batch + 63) & ~63); pr += kGemvThreads / 8) {
-      const bool live = pr < 2 * p.batch;  // every lane of a wave takes part in the exchanges
-      const int j = live ? pr >> 1 : 0, f = pr & 1;
-      const float* v = res + (size_t)((f * p.cbf + (j >> 4)) * 16 + (j & 15)) * kRowsPerWg;
-      float x[kPer];
-      float mx = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        x[i] = v[sub + 8 * i];
-        mx = fmaxf(mx, x[i]);
-      }
-#pragma unroll
-      for (int m = 4; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
-      float se = 0.f, sq = 0.f;
-#pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        const float e = __builtin_amdgcn_exp2f((x[i] - mx) * kLog2e);
-        se += e;
-        sq += e * e;
-      }
-#pragma unroll
-      for (int m = 4; m >= 1; m >>= 1) {
-        se += __shfl_xor(se, m);
-        sq += __shfl_xor(sq, m);
-      }
-      if (live && sub == 0) {
-        float* r = p.head_rec + ((size_t)j * p.head_nrec + rg) * kMixRec;
-        if (f == 0) {
-          r[0] = mx;
-          r[1] = se;
-          r[2] = sq;
-        } else {
-          r[3] = mx;
-          r[4] = se;
-        }
-      }
-    }
-  }
 }
 
 // One thread per (sequence s, 4 columns): both flows' sums over the k-splits
@@ -680,19 +631,6 @@ hipError_t launch_gemv(const GemvParams& p, hipStream_t stream) {
     return hipErrorInvalidValue;
   }
   const dim3 grid(p.k_split, p.n / p.rows_per_wg), block(kGemvThreads);
-  if (p.head_rec) {  // output head: two flows, one matrix, one k-range, no epilogue
-    if (p.flows != 2 || p.pair || p.k_split != 1 || p.epilogue != kEpiNone || (tiles != 4 && tiles != 8))
-      return hipErrorInvalidValue;
-#define DFA_HEAD_CASE(NCB_, LO_)                                                                                 \
-  if (ncb == NCB_ && lo == LO_) {                                                                                \
-    if (tiles == 8) hipLaunchKernelGGL((gemv_kernel<NCB_, false, LO_, 8, false, true>), grid, block, 0, stream, p); \
-    else hipLaunchKernelGGL((gemv_kernel<NCB_, false, LO_, 4, false, true>), grid, block, 0, stream, p);            \
-    return hipGetLastError();                                                                                    \
-  }
-    DFA_HEAD_CASE(2, false) DFA_HEAD_CASE(2, true) DFA_HEAD_CASE(4, false) DFA_HEAD_CASE(4, true)
-#undef DFA_HEAD_CASE
-    return hipErrorInvalidValue;
-  }
 #define DFA_GEMV_CASE(NCB_, PAIR_, LO_)                                                                      \
   if (ncb == NCB_ && p.pair == PAIR_ && lo == LO_) {                                                         \
     if (tiles == 8) hipLaunchKernelGGL((gemv_kernel<NCB_, PAIR_, LO_, 8, false>), grid, block, 0, stream, p); \

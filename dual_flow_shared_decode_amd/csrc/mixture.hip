@@ -108,6 +108,80 @@ __device__ __forceinline__ float4 mix4(const float* l1, const float* l2, int v, 
 // non-finite logit), so no conversion of a non-finite value happens.
 __device__ __forceinline__ uint64_t fixed(float q) { return q > 0.f ? (uint64_t)(fminf(q, 1.f) * kFix) : 0; }
 
+// Wave all-reductions through vector ALU lane exchanges (no LDS). Step S
+// gives each lane its own word and its partner's (in some order: the
+// combining operation is symmetric): quad_perm xor 1 and xor 2, then the
+// half-row and row mirrors -- which pair quads and half-rows as xor 4 and
+// xor 8 would, once quads and then half-rows hold one value -- then the 16-
+// and 32-lane permlane swaps. The combination tree is fixed: every lane ends
+// with the same bits, run after run.
+template <int S>
+__device__ __forceinline__ void xpair(uint32_t x, uint32_t& a, uint32_t& b) {
+  if constexpr (S < 4) {
+    constexpr int kCtrl = S == 0 ? 0xB1 : (S == 1 ? 0x4E : (S == 2 ? 0x141 : 0x140));
+    a = x;
+    b = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kCtrl, 0xF, 0xF, false);
+  } else if constexpr (S == 4) {
+    const auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    a = p[0];
+    b = p[1];
+  } else {
+    const auto p = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    a = p[0];
+    b = p[1];
+  }
+}
+
+template <int S>
+__device__ __forceinline__ float xsum_step(float x) {
+  uint32_t a, b;
+  xpair<S>(__float_as_uint(x), a, b);
+  return __uint_as_float(a) + __uint_as_float(b);
+}
+template <int S>
+__device__ __forceinline__ float xmax_step(float x) {
+  uint32_t a, b;
+  xpair<S>(__float_as_uint(x), a, b);
+  return fmaxf(__uint_as_float(a), __uint_as_float(b));
+}
+
+__device__ __forceinline__ float wave_allsum(float x) {
+  x = xsum_step<0>(x); x = xsum_step<1>(x); x = xsum_step<2>(x);
+  x = xsum_step<3>(x); x = xsum_step<4>(x); return xsum_step<5>(x);
+}
+__device__ __forceinline__ float wave_allmax(float x) {
+  x = xmax_step<0>(x); x = xmax_step<1>(x); x = xmax_step<2>(x);
+  x = xmax_step<3>(x); x = xmax_step<4>(x); return xmax_step<5>(x);
+}
+
+template <int S>
+__device__ __forceinline__ uint64_t xsum64_step(uint64_t x) {
+  uint32_t al, bl, ah, bh;
+  xpair<S>((uint32_t)x, al, bl);
+  xpair<S>((uint32_t)(x >> 32), ah, bh);
+  return (((uint64_t)ah << 32) | al) + (((uint64_t)bh << 32) | bl);
+}
+__device__ __forceinline__ uint64_t wave_allsum_u64(uint64_t x) {
+  x = xsum64_step<0>(x); x = xsum64_step<1>(x); x = xsum64_step<2>(x);
+  x = xsum64_step<3>(x); x = xsum64_step<4>(x); return xsum64_step<5>(x);
+}
+
+// (value, index) pair: the larger value, the smaller index on ties.
+template <int S>
+__device__ __forceinline__ void xfirstmax_step(float& v, int& i) {
+  uint32_t va, vb, ia, ib;
+  xpair<S>(__float_as_uint(v), va, vb);
+  xpair<S>((uint32_t)i, ia, ib);
+  const float fa = __uint_as_float(va), fb = __uint_as_float(vb);
+  const bool take_b = fb > fa || (fb == fa && (int)ib < (int)ia);
+  v = take_b ? fb : fa;
+  i = take_b ? (int)ib : (int)ia;
+}
+__device__ __forceinline__ void wave_first_max(float& v, int& i) {
+  xfirstmax_step<0>(v, i); xfirstmax_step<1>(v, i); xfirstmax_step<2>(v, i);
+  xfirstmax_step<3>(v, i); xfirstmax_step<4>(v, i); xfirstmax_step<5>(v, i);
+}
+
 __device__ __forceinline__ uint64_t shfl_up_u64(uint64_t x, int d) {
   const uint32_t lo = __shfl_up((uint32_t)x, d), hi = __shfl_up((uint32_t)(x >> 32), d);
   return ((uint64_t)hi << 32) | lo;
@@ -141,15 +215,7 @@ __device__ __forceinline__ uint64_t block_excl_scan(uint64_t x, uint64_t* sh, ui
 template <int NW>
 __device__ __forceinline__ void block_first_max(float& v, int& i, float* shv, int* shi) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const float ov = __shfl_xor(v, m);
-    const int oi = __shfl_xor(i, m);
-    if (ov > v || (ov == v && oi < i)) {
-      v = ov;
-      i = oi;
-    }
-  }
+  wave_first_max(v, i);
   __syncthreads();
   if (lane == 0) {
     shv[wave] = v;
@@ -169,11 +235,7 @@ __device__ __forceinline__ void block_first_max(float& v, int& i, float* shv, in
 // Max (is_max) or sum over the workgroup, lanes then waves in a fixed order.
 __device__ __forceinline__ float block_reduce(float v, float* sh, bool is_max) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const float o = __shfl_xor(v, m);
-    v = is_max ? fmaxf(v, o) : v + o;
-  }
+  v = is_max ? wave_allmax(v) : wave_allsum(v);
   __syncthreads();
   if (lane == 0) sh[wave] = v;
   __syncthreads();
@@ -183,80 +245,6 @@ __device__ __forceinline__ float block_reduce(float v, float* sh, bool is_max) {
   return r;
 }
 
-// The sequence's softmax normalisers and alpha from nrec records of the
-// output-head GEMV's tiles (global memory, same fields as the chunk records):
-// each thread folds records t, t + kMixThreads, ... in order (a running max,
-// its sums rescaled when it moves), then fixed-order workgroup reductions (the
-// two maxima together, then the three sums together), so every workgroup
-// computes the same values.
-__device__ __forceinline__ Norm merge_tile_records(const float* rec, int nrec, float* sh) {
-  float m1 = -INFINITY, m2 = -INFINITY, s1 = 0.f, q1 = 0.f, s2 = 0.f;
-  for (int t = threadIdx.x; t < nrec; t += kMixThreads) {
-    const float* r = rec + (size_t)t * kMixRec;
-    const float4 a = *(const float4*)r;  // m1, s1, q1, m2
-    const float b = r[4];                // s2
-    const float n1 = fmaxf(m1, a.x), n2 = fmaxf(m2, a.w);
-    if (n1 > -INFINITY) {
-      const float c = ex2((m1 - n1) * kLog2e), e = ex2((a.x - n1) * kLog2e);
-      s1 = __builtin_fmaf(a.y, e, s1 * c);
-      q1 = __builtin_fmaf(a.z, e * e, q1 * (c * c));
-    }
-    if (n2 > -INFINITY) s2 = __builtin_fmaf(b, ex2((a.w - n2) * kLog2e), s2 * ex2((m2 - n2) * kLog2e));
-    m1 = n1;
-    m2 = n2;
-  }
-  // maxima of both flows: lanes, then waves in order
-  float x1 = m1, x2 = m2;
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    x1 = fmaxf(x1, __shfl_xor(x1, m));
-    x2 = fmaxf(x2, __shfl_xor(x2, m));
-  }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  __syncthreads();
-  if (lane == 0) {
-    sh[2 * wave] = x1;
-    sh[2 * wave + 1] = x2;
-  }
-  __syncthreads();
-  Norm n;
-  n.m1 = sh[0];
-  n.m2 = sh[1];
-#pragma unroll
-  for (int w = 1; w < kMixWaves; ++w) {
-    n.m1 = fmaxf(n.m1, sh[2 * w]);
-    n.m2 = fmaxf(n.m2, sh[2 * w + 1]);
-  }
-  // this thread's sums at the row maxima, then the three sums: lanes, then waves in order
-  const float c1 = m1 > -INFINITY ? ex2((m1 - n.m1) * kLog2e) : 0.f;
-  const float c2 = m2 > -INFINITY ? ex2((m2 - n.m2) * kLog2e) : 0.f;
-  float y1 = s1 * c1, y2 = q1 * (c1 * c1), y3 = s2 * c2;
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    y1 += __shfl_xor(y1, m);
-    y2 += __shfl_xor(y2, m);
-    y3 += __shfl_xor(y3, m);
-  }
-  __syncthreads();
-  if (lane == 0) {
-    sh[4 * wave] = y1;
-    sh[4 * wave + 1] = y2;
-    sh[4 * wave + 2] = y3;
-  }
-  __syncthreads();
-  float t1 = sh[0], t2 = sh[1], t3 = sh[2];
-#pragma unroll
-  for (int w = 1; w < kMixWaves; ++w) {
-    t1 += sh[4 * w];
-    t2 += sh[4 * w + 1];
-    t3 += sh[4 * w + 2];
-  }
-  const float collision = t2 / (t1 * t1);
-  n.alpha = __builtin_fmaf(0.5f, collision, 0.5f);
-  n.w1 = n.alpha / t1;
-  n.w2 = (1.f - n.alpha) / t3;
-  return n;
-}
 }  // namespace
 
 // rec[b][chunk][0..4] = {m1, s1, q1, m2, s2}: m = the chunk's largest logit,
@@ -303,15 +291,12 @@ __global__ __launch_bounds__(kMixThreads) void mix_stats_kernel(MixParams p) {
 }
 
 // crec[b][chunk] = {mass (low, high word), first maximum's value bits, its token};
-// alpha[b] from chunk 0. TILES: the statistics are the output-head GEMV's
-// nrec tile records per sequence rather than the chunk records.
-template <bool TILES>
+// alpha[b] from chunk 0.
 __global__ __launch_bounds__(kMixThreads) void mix_chunk_kernel(MixParams p) {
-  __shared__ float shr[TILES ? 4 * kMixWaves : 1];
   __shared__ uint64_t shm[kMixWaves];
   __shared__ float shv[kMixWaves];
   __shared__ int shi[kMixWaves];
-  __shared__ float srec[TILES ? 1 : kMixMaxChunks][kMixRec];
+  __shared__ float srec[kMixMaxChunks][kMixRec];
   const int chunk = blockIdx.x, b = blockIdx.y;
   // the chunk's logits are loaded first: their round trip overlaps the records'
   const float* l1 = p.logits1 + (size_t)b * p.vocab;
@@ -324,13 +309,8 @@ __global__ __launch_bounds__(kMixThreads) void mix_chunk_kernel(MixParams p) {
     la[i] = v < p.vocab ? *(const float4*)(l1 + v) : make_float4(0.f, 0.f, 0.f, 0.f);
     lc[i] = v < p.vocab ? *(const float4*)(l2 + v) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  Norm n;
-  if constexpr (TILES) {
-    n = merge_tile_records(p.rec + (size_t)b * p.nrec * kMixRec, p.nrec, shr);
-  } else {
-    stage_records(p.rec + (size_t)b * p.chunks * kMixRec, p.chunks, srec);
-    n = merge_records(&srec[0][0], p.chunks);
-  }
+  stage_records(p.rec + (size_t)b * p.chunks * kMixRec, p.chunks, srec);
+  const Norm n = merge_records(&srec[0][0], p.chunks);
   float* pm = p.p_mix ? p.p_mix + (size_t)b * p.vocab : nullptr;
   uint64_t mass = 0;
   float bv = -1.f;
@@ -362,15 +342,13 @@ __global__ __launch_bounds__(kMixThreads) void mix_chunk_kernel(MixParams p) {
   }
 }
 
-template <bool TILES>
 __global__ __launch_bounds__(kMixThreads) void mix_pick_kernel(MixParams p) {
-  __shared__ float shr[TILES ? 4 * kMixWaves : 1];
   __shared__ uint64_t shm[kMixWaves];
   __shared__ float shv[kMixWaves];
   __shared__ int shi[kMixWaves];
   __shared__ int sel_chunk, sel_tok;
   __shared__ uint64_t sel_base;
-  __shared__ float srec[TILES ? 1 : kMixMaxChunks][kMixRec];
+  __shared__ float srec[kMixMaxChunks][kMixRec];
   const int b = blockIdx.x, t = threadIdx.x;
   // ---- chunk level: one chunk record per thread (loaded with the statistics) ----
   uint64_t mass = 0;
@@ -378,13 +356,8 @@ __global__ __launch_bounds__(kMixThreads) void mix_pick_kernel(MixParams p) {
   int bi = p.vocab;
   uint4 r = make_uint4(0u, 0u, 0u, 0u);
   if (t < p.chunks) r = *(const uint4*)(p.crec + ((size_t)b * p.chunks + t) * 4);
-  Norm n;
-  if constexpr (TILES) {
-    n = merge_tile_records(p.rec + (size_t)b * p.nrec * kMixRec, p.nrec, shr);
-  } else {
-    stage_records(p.rec + (size_t)b * p.chunks * kMixRec, p.chunks, srec);
-    n = merge_records(&srec[0][0], p.chunks);
-  }
+  stage_records(p.rec + (size_t)b * p.chunks * kMixRec, p.chunks, srec);
+  const Norm n = merge_records(&srec[0][0], p.chunks);
   if (t < p.chunks) {
     mass = ((uint64_t)r.y << 32) | r.x;
     bv = __uint_as_float(r.z);
@@ -461,14 +434,7 @@ constexpr int kFuseWaves = kFuseThreads / 64;
 constexpr int kFuseRows = 8;  // float4 groups per lane and flow
 static_assert(kFuseWaves * 64 * kFuseRows * 4 == kMixFusedMaxVocab, "one token per register slot");
 
-__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const uint32_t lo = __shfl_xor((uint32_t)x, m), hi = __shfl_xor((uint32_t)(x >> 32), m);
-    x += ((uint64_t)hi << 32) | lo;
-  }
-  return x;
-}
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t x) { return wave_allsum_u64(x); }
 
 __device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t x) {
   const int lane = threadIdx.x & 63;
@@ -480,17 +446,9 @@ __device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t x) {
   return x;
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
-  return v;
-}
+__device__ __forceinline__ float wave_max(float v) { return wave_allmax(v); }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-  return v;
-}
+__device__ __forceinline__ float wave_sum(float v) { return wave_allsum(v); }
 }  // namespace
 
 // The whole mixture of one sequence in one workgroup, for vocabularies of at
@@ -680,18 +638,10 @@ hipError_t launch_mixture(const MixParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(mix_stats_kernel, dim3(p.chunks, p.batch), dim3(kMixThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(mix_chunk_kernel<false>, dim3(p.chunks, p.batch), dim3(kMixThreads), 0, stream, p);
+  hipLaunchKernelGGL(mix_chunk_kernel, dim3(p.chunks, p.batch), dim3(kMixThreads), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(mix_pick_kernel<false>, dim3(p.batch), dim3(kMixThreads), 0, stream, p);
-  return hipGetLastError();
-}
-
-hipError_t launch_mixture_tiles(const MixParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(mix_chunk_kernel<true>, dim3(p.chunks, p.batch), dim3(kMixThreads), 0, stream, p);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(mix_pick_kernel<true>, dim3(p.batch), dim3(kMixThreads), 0, stream, p);
+  hipLaunchKernelGGL(mix_pick_kernel, dim3(p.batch), dim3(kMixThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -52,11 +52,6 @@ struct GemvParams {
   const float* rope_cos;
   const float* rope_sin;
   int32_t rope, rope_max_pos;
-  // Output head: per workgroup tile (kRowsPerWg vocabulary rows) and sequence, a
-  // softmax-statistics record of both flows' logits, laid out as the mixture's
-  // chunk records: head_rec[s][tile][kMixRec] = {m1, s1, q1, m2, s2}.
-  float* head_rec;
-  int32_t head_nrec;   // tiles per sequence (n / rows_per_wg)
   uint16_t* kv_k;      // KV append target
   uint16_t* kv_v;
   const int32_t* kv_table;
@@ -80,11 +75,9 @@ struct MixParams {
   int32_t* greedy;       // [batch] first most likely token
   float* alpha;          // [batch]
   float* p_mix;          // [batch, vocab] or null
-  float* rec;            // workspace: [batch][chunks][kMixRec] softmax statistics (or [batch][nrec][kMixRec]
-                         // tile records of the output-head GEMV, for launch_mixture_tiles)
+  float* rec;            // workspace: [batch][chunks][kMixRec] softmax statistics
   uint32_t* crec;        // workspace: [batch][chunks][4] mass (2 words), first maximum (value, token)
   int32_t batch, vocab, chunks;
-  int32_t nrec;          // tile records per sequence (launch_mixture_tiles)
 };
 
 // Mixture-of-experts routing and output combination.
@@ -160,9 +153,6 @@ hipError_t launch_gemv_finalize(const GemvParams& p, hipStream_t s);
 hipError_t launch_pack_weight(const uint16_t* w, uint16_t* wt, int n, int k, hipStream_t s);
 size_t gemv_chunk();
 hipError_t launch_mixture(const MixParams& p, hipStream_t s);
-// The mixture from tile records written by the output-head GEMV: p_mix, masses and maxima per
-// chunk, then the draw (two launches; the logits are read once).
-hipError_t launch_mixture_tiles(const MixParams& p, hipStream_t s);
 hipError_t launch_moe_route(const MoeRouteParams& p, hipStream_t s);
 hipError_t launch_moe_combine(const MoeCombineParams& p, hipStream_t s);
 size_t mixture_chunks(int vocab);

@@ -446,18 +446,15 @@ DFA_API dfa_status dfa_mixture_sample(const dfa_mixture_desc* desc, const float*
                                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * ------------------------------------------------------ fused output head
- * Both flows' logits from one read of the shared vocabulary matrix, then the
- * mixture decoding above ("Mecanismos Chave", mixture objective; one output
- * matrix shared by the flows, "Arquitetura Central"):
+ * ------------------------------------------------------------ output head
+ * The output head in one call: both flows' logits from one read of the
+ * shared vocabulary matrix ("Arquitetura Central": one output matrix shared by
+ * the flows), then the mixture decoding above ("Mecanismos Chave", mixture
+ * objective):
  *     logits_f = h_f W^T  (W: bf16 [vocab, hidden], tiled by dfa_pack_weight)
  * and token, greedy, alpha and (optionally) p_mix exactly as
- * dfa_mixture_sample defines them for these logits. The GEMV writes, besides
- * the logits, the softmax statistics of each of its vocabulary tiles, so the
- * mixture reads the logits once (spread over (chunk, sequence) workgroups)
- * instead of a statistics pass first. When the GEMV plan splits k (vocab
- * below 24576 at hidden 4096) the statistics are not fused: the GEMV and
- * its reduction run, then the kernels of dfa_mixture_sample.
+ * dfa_mixture_sample defines them for these logits: the kernels of
+ * dfa_dual_gemv, then those of dfa_mixture_sample, sharing one workspace.
  *  h1, h2:          float32 [batch, hidden] final hidden states of the flows
  *  u:               float32 [batch] uniforms
  *  logits1, logits2: float32 [batch, vocab] outputs (required: the mixture

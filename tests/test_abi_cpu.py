@@ -364,12 +364,15 @@ def test_table_check_validation():
 
 
 def test_output_head_plans_and_validation():
-    """dfa_output_head: the workspace of the fused plan (tile records + chunk records) and of the
-    split-k plan (GEMV partials + mixture records); every error on the host."""
+    """dfa_output_head: its workspace (GEMV partials when the plan splits k, then the mixture's chunk
+    records); every error on the host."""
     head = lambda **kw: dfa.HeadDesc(**{**dict(batch=32, vocab=32000, hidden=4096, x_exact_bf16=1), **kw})
     up = lambda x: (x + 255) // 256 * 256
-    # 32000 x 4096: 250 tiles of 128 rows, one k-range; 8 chunks of 4096 tokens
-    assert dfa.dfa_output_head_workspace_size(head()) == up(32 * 250 * 8 * 4) + up(32 * 8 * 16)
+    # 32000 tokens: the one-launch mixture (8 chunk records of 4096 tokens per sequence)
+    assert dfa.dfa_output_head_workspace_size(head()) == up(32 * 8 * 8 * 4) + up(32 * 8 * 16)
+    # 40960 tokens: 10 chunks
+    assert dfa.dfa_output_head_workspace_size(head(vocab=40960, hidden=2048)) == up(32 * 10 * 8 * 4) + \
+        up(32 * 10 * 16)
     # 4160 x 512: 65 row groups of 64 split k (4 ranges of 128 columns): partials, then chunk records
     gd = dfa.GemvDesc(batch=3, n=4160, k=512, num_flows=2, epilogue=0, x_exact_bf16=1, k_split=0, rows_per_wg=0)
     g = dfa.dfa_dual_gemv_workspace_size(gd)

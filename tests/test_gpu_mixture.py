@@ -14,11 +14,10 @@ the inverse-CDF token for the caller's uniform u. Bars:
   cumulative bounds of the returned token contain u up to 1e-4, and that the
   token is the oracle's own wherever u is farther than that from a boundary.
 
-The fused output head (dfa_output_head: the GEMV writes each vocabulary tile's
-softmax statistics, the mixture merges them) is held to the same bars, on
-128- and 64-row tiles, sliced batches, more than one chunk, and the plan that
-falls back to the separate kernels; against the two-call path its logits are
-bit for bit the same and alpha and p_mix agree to rounding.
+The one-call output head (dfa_output_head) is held to the same bars, below and
+above 32768 tokens (one-launch and chunked mixture), up to 128256 tokens, with
+128- and 64-row GEMV plans, sliced batches and a split-k plan; against the
+two-call path every output is bit for bit the same.
 
 Exact properties of the library's own outputs (bit for bit): the token is the
 inverse-CDF token of the returned p_mix under the library's stated integer
@@ -209,7 +208,7 @@ def test_dual_output_head(cfg):
 
 
 def run_fused_head(cfg, seed, with_p_mix=True):
-    """dfa_output_head: both flows' logits and, from the GEMV's tile statistics, the mixture."""
+    """dfa_output_head: both flows' logits and the mixture in one call."""
     h1, h2, w_bits, u = W.make_head_case(cfg, seed)
     wdev = to_device(w_bits)
     wt = torch.empty_like(wdev)
@@ -233,13 +232,14 @@ def run_fused_head(cfg, seed, with_p_mix=True):
 
 
 HEADS = {
-    # 32000 x 4096: 128-row tiles, one k-range -> 250 tile records per sequence (statistics fused)
+    # up to 32768 tokens: the GEMV, then the one-launch mixture
     "head": W.HEAD,
-    # 64-row tiles (a matrix under 48 Mi elements), 192 and 625 tiles, the latter over ten 4096-token chunks
-    "tiles64": W.HEAD.replace(batch=5, hidden=1024, vocab=12288),
-    "chunks10": W.HEAD.replace(batch=3, hidden=512, vocab=40000),
+    # above: the chunked mixture (64-row GEMV plan; 128-row plan; 32 chunks)
+    "rows64": W.HEAD.replace(batch=3, hidden=512, vocab=40000),
+    "rows128": W.HEAD.replace(batch=5, hidden=2048, vocab=40960),
+    "vocab128k": W.HEAD.replace(batch=4, hidden=512, vocab=128256),
     # 40 sequences: the GEMV in slices of 32, the mixture over all 40
-    "batch40": W.HEAD.replace(batch=40, hidden=1024, vocab=32000),
+    "batch40": W.HEAD.replace(batch=40, hidden=2048, vocab=40960),
     # a plan that splits k (too few row groups): GEMV, reduction, then the mixture's own kernels
     "split": W.HEAD.replace(batch=3, hidden=512, vocab=4096 + 64),
 }
@@ -260,17 +260,16 @@ def test_fused_output_head(name):
         assert np.array_equal(got2[k], got[k]), k
 
 
-def test_fused_head_matches_the_two_call_path():
-    """The fused head and dfa_dual_gemv + dfa_mixture_sample compute the same logits bit for bit; alpha
-    and p_mix agree to rounding (normalisers merged from 128-token tiles instead of in one pass), and
-    each path's tokens are exact for its own p_mix."""
-    cfg = W.HEAD.replace(batch=8)
-    say("case fused head vs two calls")
+@pytest.mark.parametrize("vocab", [32000, 40960])
+def test_fused_head_matches_the_two_call_path(vocab):
+    """dfa_output_head and dfa_dual_gemv + dfa_mixture_sample: every output bit for bit the same."""
+    cfg = W.HEAD.replace(batch=8, hidden=2048, vocab=vocab)
+    say(f"case one-call head vs two calls, vocab {vocab}")
     *_, (f1, f2), fused = run_fused_head(cfg, 91)
     *_, (t1, t2), two = run_head(cfg, 91)
     assert np.array_equal(f1, t1) and np.array_equal(f2, t2)
-    assert np.max(np.abs(fused["alpha"] - two["alpha"])) <= 1e-6
-    assert_close(fused["p_mix"], two["p_mix"], 1e-5, "p_mix fused vs two calls")
+    for k in ("token", "greedy", "alpha", "p_mix"):
+        assert np.array_equal(fused[k], two[k]), k
 
 
 @pytest.mark.parametrize("vocab", [32000, 40000])

@@ -4,8 +4,9 @@ The variant runs the same split plan and kernels with its split records in the
 library's fixed device scratch instead of a caller workspace, so its outputs
 must equal dfa_decode_attn's bit for bit, and both must meet the oracle's
 2e-3 bar. Two calls in a row, the second with a smaller input (the scratch
-keeps the first call's records; every record is rewritten), then a call whose
-records exceed the scratch: refused on the host, nothing written.
+keeps the first call's records; every record is rewritten), a third with 32
+query rows per kv head, then a call whose records exceed the scratch: refused
+on the host, nothing written.
 """
 import numpy as np
 import pytest
@@ -36,6 +37,9 @@ CASES = [
     ("first", W.C2.replace(batch=6, ctx_lens=(4096, 3000, 17, 4000, 2049, 1), capacity=4096), 3101, 512),
     # a smaller input next: fewer sequences, fewer splits, paged and shuffled
     ("second", W.C3.replace(batch=3, num_q_heads=32, ctx_range=None, ctx_lens=(700, 33, 1500)), 3102, 256),
+    # 32 query rows per kv head (two row sets), paged
+    ("rows32", W.AttnConfig("r32", batch=2, num_q_heads=32, num_kv_heads=2, head_dim=128, dtype="bf16",
+                            ctx_lens=(900, 2000), block_size=32, shuffle_blocks=True), 3103, 256),
 ]
 
 

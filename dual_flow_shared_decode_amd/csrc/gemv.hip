@@ -21,19 +21,23 @@
 // s % 16 (each flow padded to CBF*16 rows), so the two flows of a sequence end
 // up in the same lane and register.
 //
-// Workgroup = 8 waves = 64 weight rows (four 16-row tiles, of each matrix;
-// two wave groups split the k-steps of every stage, so each SIMD runs two
-// waves that share the stage's B operands) or 128 rows (eight tiles, one wave
-// each) x one k-range (split-K). A tile takes its weights from one of up to
-// three matrices by row range, so one launch can cover stacked matrices
-// (the layer's [Wq; Wk; Wv]). The k-range
-// is streamed in 128-column stages, three in flight: a stage's weights (in
-// registers) and raw activations (in registers, first touched when they are
-// converted) are fetched together, and per stage the workgroup converts the
-// next stage's activations to hi/lo bf16 in LDS (double-buffered; per column
-// block, row r's 8-column groups are stored in slot group ^ r so that both
-// the conversion's writes and the MFMA operand reads are free of bank
-// conflicts). With one k-range the epilogue runs
+// Workgroup = 8 math waves + 8 loader waves. The math waves cover 64 weight
+// rows (four 16-row tiles, of each matrix; two wave groups split the k-steps
+// of every stage, so each SIMD runs two math waves that share the stage's B
+// operands) or 128 rows (eight tiles, one wave each) x one k-range
+// (split-K). A tile takes its weights from one of up to three matrices by row
+// range, so one launch can cover stacked matrices (the layer's [Wq; Wk; Wv]).
+// The k-range is streamed in 128-column stages. The math waves keep three
+// stages of weights in flight in registers (two for paired 128-row tiles)
+// and only wait for their own loads; the loader waves keep three stages of
+// raw activations in flight and, per stage, convert the next stage's
+// activations to hi/lo bf16 in LDS (double-buffered; per column block, row
+// r's 8-column groups are stored in slot group ^ r so that both the
+// conversion's writes and the MFMA operand reads are free of bank
+// conflicts). One barrier per stage hands the buffers over. Loads complete in
+// issue order within a wave, so a wave that fetched both would wait for its
+// weights before it could convert activations; split this way the GEMVs of
+// the layer shapes run 4-8% faster. With one k-range the epilogue runs
 // in the same kernel; otherwise partial sums go to the workspace
 // [k-split][matrix][row][n] and gemv_finalize adds them in a fixed order and
 // applies the epilogue (so the primary flow's results never depend on the
@@ -72,8 +76,11 @@ hipError_t launch_pack_weight(const uint16_t* w, uint16_t* wt, int n, int k, hip
 
 // ---------------------------------------------------------------- GEMV
 namespace {
-constexpr int kGemvWaves = 8;
-constexpr int kGemvThreads = 64 * kGemvWaves;
+constexpr int kGemvWaves = 8;  // waves on the weights and MFMAs
+constexpr int kLoadWaves = 8;  // waves fetching and converting activations (4: no faster; 2: spills)
+constexpr int kMathThreads = 64 * kGemvWaves;
+constexpr int kLoadThreads = 64 * kLoadWaves;
+constexpr int kGemvThreads = kMathThreads + kLoadThreads;
 constexpr int kStage = 128;                    // k columns per pipeline stage
 constexpr int kSteps = kStage / 32;            // MFMA k-steps per stage
 static_assert(kStage / 8 == 16, "the LDS swizzle pairs 16 column groups with 16 rows");
@@ -185,12 +192,13 @@ __device__ __forceinline__ void apply_epilogue(const GemvParams& p, int s, size_
   }
 }
 
-// Raw activations of one stage held by one thread: the stage has NCB*16 rows
-// x kStage/8 groups of 8 columns; thread t takes groups t, t + threads, ...
+// Raw activations of one stage held by one loader thread: the stage has
+// NCB*16 rows x kStage/8 groups of 8 columns; loader thread t takes groups t,
+// t + kLoadThreads, ...
 template <int NCB>
 struct XStage {
   static constexpr int kTotal = NCB * 16 * (kStage / 8);  // 8-column groups of one stage
-  static constexpr int kItems = (kTotal + kGemvThreads - 1) / kGemvThreads;
+  static constexpr int kItems = (kTotal + kLoadThreads - 1) / kLoadThreads;
   float4 v[kItems][2];
   bool live[kItems];  // false: the group is padding and converts to zeros
 };
@@ -205,7 +213,7 @@ __device__ __forceinline__ void fetch_x(const GemvParams& p, int k_begin, int st
   const int kc = k_begin + st * kStage;
 #pragma unroll
   for (int it = 0; it < XStage<NCB>::kItems; ++it) {
-    const int item = threadIdx.x + it * kGemvThreads;
+    const int item = (threadIdx.x - kMathThreads) + it * kLoadThreads;
     const int kg = item % (kStage / 8), m = item / (kStage / 8);
     const int cb = m >> 4, f = cb / p.cbf, j = (cb - f * p.cbf) * 16 + (m & 15);
     // groups past the stage (fewer than threads), past the batch or past the
@@ -236,7 +244,7 @@ template <int NCB, int NH>
 __device__ __forceinline__ void put_x(const XStage<NCB>& xr, uint16_t* xs) {
 #pragma unroll
   for (int it = 0; it < XStage<NCB>::kItems; ++it) {
-    const int item = threadIdx.x + it * kGemvThreads;
+    const int item = (threadIdx.x - kMathThreads) + it * kLoadThreads;
     const int kg = item % (kStage / 8), m = item / (kStage / 8);
     const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
     const float4 q0 = xr.live[it] ? xr.v[it][0] : z, q1 = xr.live[it] ? xr.v[it][1] : z;
@@ -264,9 +272,10 @@ __device__ __forceinline__ void put_x(const XStage<NCB>& xr, uint16_t* xs) {
 // NCB: activation column blocks (flows * CBF); PAIR: a second matrix (w2) on the
 // same activations; LO: split activations into hi + lo.
 //
-// Wave w works on tile w % 4 with the k-steps of wave group w / 4: group g
-// takes k-steps 2g, 2g + 1 of every stage, so two waves per SIMD share the
-// stage's B operands and each holds half of the weights in flight.
+// Math wave w works on tile w % 4 with the k-steps of wave group w / 4: group
+// g takes k-steps 2g, 2g + 1 of every stage, so two waves per SIMD share the
+// stage's B operands and each holds half of the weights in flight. Waves 8 to
+// 15 are the loader waves.
 //
 // GROUPED (mixture of experts): grid row index = expert * moe_rgs + row group;
 // the workgroup multiplies its expert's matrices (moe_wstride elements apart)
@@ -280,7 +289,12 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvParams p) {
   constexpr int kHalfSteps = kSteps / kGroups;   // k-steps of one wave group per stage
   constexpr int NH = LO ? 2 : 1;
   constexpr int MATS = PAIR ? 2 : 1;
-  constexpr int DEPTH = 3;  // stages in flight: weights and activations of each are fetched together
+  // weight stages in flight per math wave (deeper measured no faster; paired
+  // 128-row tiles take two to stay within the 128 registers of a 16-wave
+  // workgroup) and activation stages in flight per loader wave
+  constexpr int WDEPTH = (PAIR && TILES == 8) ? 2 : 3;
+  constexpr int XDEPTH = 2;
+  static_assert(XDEPTH >= 2 && WDEPTH >= 1, "the loader converts stage st + 1 while stage st is multiplied");
   // LDS: the double-buffered B operands, reused after the loop to stage the
   // results for the epilogue (whichever is larger sets the size)
   constexpr size_t kXsBytes = 2 * NH * NCB * (kStage / 8) * 16 * 8 * sizeof(uint16_t);
@@ -360,75 +374,84 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvParams p) {
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) acc[mat][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Loads complete in issue order: a stage's activations and weights are
-  // fetched together DEPTH stages ahead, and the activations of stage st + 1
-  // are converted (waiting for stage st + 1 only) while later stages stay in
-  // flight.
-  WStage w0, w1, w2;  // three separately named buffers stay in registers
-  XStage<NCB> x0, x1, x2;
-  if (nst > 0) {
-    fetch_x<NCB, GROUPED>(p, k_begin, 0, x0, ent, cnt);
-    fetch_w(0, w0);
-  }
-  if (nst > 1) {
-    fetch_x<NCB, GROUPED>(p, k_begin, 1, x1, ent, cnt);
-    fetch_w(1, w1);
-  }
-  if (nst > 2) {
-    fetch_x<NCB, GROUPED>(p, k_begin, 2, x2, ent, cnt);
-    fetch_w(2, w2);
-  }
-  if (nst > 0) put_x<NCB, NH>(x0, &xs[0][0][0][0][0][0]);
-  __syncthreads();
-  // stage st: multiply with weights wj (B operands in xs[st & 1]); meanwhile
-  // convert stage st + 1 from xn and fetch stage st + DEPTH into wj, xj
-  auto step = [&](int st, WStage& wj, XStage<NCB>& xj, const XStage<NCB>& xn, bool fetch) __attribute__((always_inline)) {
-    const int buf = st & 1;
-    if (st + 1 < nst) put_x<NCB, NH>(xn, &xs[buf ^ 1][0][0][0][0][0]);
-    bf16x8 xb[kHalfSteps][NCB][NH];
+  // The loader waves fetch every stage's activations three stages ahead and
+  // convert stage st + 1 into xs[(st + 1) & 1] while the math waves multiply
+  // stage st; one barrier per stage hands the buffers over. The math waves
+  // only ever wait for their own weights (loads complete in issue order, so a
+  // wave that also fetched activations would wait for both), and the loader
+  // waves only for activations, which the L2 serves.
+  const bool loader = wave >= kGemvWaves;  // wave-uniform
+  if (loader) {
+    // the conversion gates every stage's barrier: the loader waves' instructions
+    // go first on their SIMDs (the GEMVs of the layer shapes 3-9% faster)
+    __builtin_amdgcn_s_setprio(2);
+    XStage<NCB> x[XDEPTH];
 #pragma unroll
-    for (int k2 = 0; k2 < kHalfSteps; ++k2)
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-        for (int h = 0; h < NH; ++h)
-          xb[k2][cb][h] = *(const bf16x8*)&xs[buf][h][cb][col][(4 * (wg * kHalfSteps + k2) + grp) ^ col][0];
-#pragma unroll
-    for (int k2 = 0; k2 < kHalfSteps; ++k2)
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-        for (int h = 0; h < NH; ++h)
-#pragma unroll
-          for (int mat = 0; mat < MATS; ++mat)
-            acc[mat][cb] = mfma(wj.a[mat][k2], xb[k2][cb][h], acc[mat][cb]);
-    if (fetch) {
-      fetch_x<NCB, GROUPED>(p, k_begin, st + DEPTH, xj, ent, cnt);
-      fetch_w(st + DEPTH, wj);
-    }
+    for (int j = 0; j < XDEPTH; ++j)
+      if (j < nst) fetch_x<NCB, GROUPED>(p, k_begin, j, x[j], ent, cnt);
+    if (nst > 0) put_x<NCB, NH>(x[0], &xs[0][0][0][0][0][0]);
     __syncthreads();
-  };
-  static_assert(DEPTH == 3, "the loops below rotate three stage buffers");
-  // Steady state: every step fetches, so each iteration issues the same loads
-  // and the waits before a stage's first use cover only that stage's loads
-  // (with fetches that may or may not happen, the counts differ between
-  // paths and the compiler must wait for all outstanding loads).
-  int s0 = 0;
-  for (; s0 + 2 + DEPTH < nst; s0 += 3) {
-    step(s0, w0, x0, x1, true);
-    step(s0 + 1, w1, x1, x2, true);
-    step(s0 + 2, w2, x2, x0, true);
-  }
-  for (; s0 < nst; s0 += 3) {  // the last stages: fetch while stages remain
-    step(s0, w0, x0, x1, s0 + DEPTH < nst);
-    if (s0 + 1 >= nst) break;
-    step(s0 + 1, w1, x1, x2, s0 + 1 + DEPTH < nst);
-    if (s0 + 2 >= nst) break;
-    step(s0 + 2, w2, x2, x0, s0 + 2 + DEPTH < nst);
+    // stage st: convert stage st + 1 (buffer xn) into xs[(st + 1) & 1], then
+    // fetch stage st + XDEPTH into xj (stage st's buffer, converted before)
+    auto lstep = [&](int st, XStage<NCB>& xj, const XStage<NCB>& xn, bool fetch) __attribute__((always_inline)) {
+      if (st + 1 < nst) put_x<NCB, NH>(xn, &xs[(st + 1) & 1][0][0][0][0][0]);
+      if (fetch) fetch_x<NCB, GROUPED>(p, k_begin, st + XDEPTH, xj, ent, cnt);
+      __syncthreads();
+    };
+    int s0 = 0;
+    for (; s0 + 2 * XDEPTH - 1 < nst; s0 += XDEPTH) {
+#pragma unroll
+      for (int j = 0; j < XDEPTH; ++j) lstep(s0 + j, x[j], x[(j + 1) % XDEPTH], true);
+    }
+    for (; s0 < nst; s0 += XDEPTH) {
+#pragma unroll
+      for (int j = 0; j < XDEPTH; ++j)
+        if (s0 + j < nst) lstep(s0 + j, x[j], x[(j + 1) % XDEPTH], s0 + j + XDEPTH < nst);
+    }
+  } else {
+    WStage w[WDEPTH];
+#pragma unroll
+    for (int j = 0; j < WDEPTH; ++j)
+      if (j < nst) fetch_w(j, w[j]);
+    __syncthreads();
+    // stage st: multiply with weights wj (B operands in xs[st & 1]), then fetch stage st + WDEPTH into wj
+    auto mstep = [&](int st, WStage& wj, bool fetch) __attribute__((always_inline)) {
+      const int buf = st & 1;
+#pragma unroll
+      for (int k2 = 0; k2 < kHalfSteps; ++k2) {
+        bf16x8 xb[NCB][NH];
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+          for (int h = 0; h < NH; ++h)
+            xb[cb][h] = *(const bf16x8*)&xs[buf][h][cb][col][(4 * (wg * kHalfSteps + k2) + grp) ^ col][0];
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+          for (int h = 0; h < NH; ++h)
+#pragma unroll
+            for (int mat = 0; mat < MATS; ++mat)
+              acc[mat][cb] = mfma(wj.a[mat][k2], xb[cb][h], acc[mat][cb]);
+      }
+      if (fetch) fetch_w(st + WDEPTH, wj);
+      __syncthreads();
+    };
+    // Steady state: every step fetches, so each iteration issues the same
+    // loads and the wait before a stage's first use covers only that stage.
+    int s0 = 0;
+    for (; s0 + 2 * WDEPTH - 1 < nst; s0 += WDEPTH) {
+#pragma unroll
+      for (int j = 0; j < WDEPTH; ++j) mstep(s0 + j, w[j], true);
+    }
+    for (; s0 < nst; s0 += WDEPTH) {  // the last stages: fetch while stages remain
+#pragma unroll
+      for (int j = 0; j < WDEPTH; ++j)
+        if (s0 + j < nst) mstep(s0 + j, w[j], s0 + j + WDEPTH < nst);
+    }
   }
 
   // group 1 hands its sums to group 0 (fixed order: group 0 + group 1)
-  if (kGroups == 2 && wg == 1) {
+  if (kGroups == 2 && wg == 1 && !loader) {
 #pragma unroll
     for (int mat = 0; mat < MATS; ++mat)
 #pragma unroll
@@ -437,14 +460,14 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvParams p) {
   __syncthreads();
   // lane of group 0 holds Y[m = cb*16 + col][n = tile*16 + 4*grp + i] in acc[mat][cb][i]
   const int n0 = tile * 16 + 4 * grp;
-  if (kGroups == 2 && wg == 0) {
+  if (kGroups == 2 && wg == 0 && !loader) {
 #pragma unroll
     for (int mat = 0; mat < MATS; ++mat)
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) acc[mat][cb] += *(const f32x4*)&red[mat][cb][wt][lane][0];
   }
   if (p.k_split > 1) {
-    if (wg == 0) {
+    if (wg == 0 && !loader) {
       const size_t mat_stride = (size_t)p.m_pad * p.n;
       float* out = p.part + (size_t)ks * MATS * mat_stride;
 #pragma unroll
@@ -459,7 +482,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvParams p) {
   // activation buffers are free after the last barrier) so that each thread
   // finishes whole (sequence, 4-column) groups of both flows.
   float* res = reinterpret_cast<float*>(smem);  // [mat][m][kRowsPerWg columns]
-  if (wg == 0) {
+  if (wg == 0 && !loader) {
 #pragma unroll
     for (int mat = 0; mat < MATS; ++mat)
 #pragma unroll

@@ -698,6 +698,8 @@ dfa_status dfa_decode_stack(const dfa_stack_desc* d, const dfa_stack_layer* laye
       if (!layers[l].k_cache || !layers[l].v_cache) return fail(DFA_ERR_NULL, "every layer needs its caches");
       if (d->rms_norm && (!layers[l].norm_attn || !layers[l].norm_mlp))
         return fail(DFA_ERR_NULL, "every layer needs its norm weights");
+      if (d->rms_norm && (!aligned16(layers[l].norm_attn) || !aligned16(layers[l].norm_mlp)))
+        return fail(DFA_ERR_ALIGNMENT, "norm weights must be 16-byte aligned");
     }
     if (!workspace || ws_bytes < sp.total) return fail(DFA_ERR_WORKSPACE, "workspace smaller than dfa_decode_stack_workspace_size()");
     if (!aligned16(workspace)) return fail(DFA_ERR_ALIGNMENT, "workspace must be 16-byte aligned");

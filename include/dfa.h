@@ -361,8 +361,8 @@ DFA_API dfa_status dfa_decode_layer(const dfa_layer_desc* desc, const dfa_layer_
  * pages do not name (this library's choices):
  *  - rms_norm = 1: pre-norm RMSNorm before the attention block and before the
  *    MLP block, y = x / sqrt(mean(x^2) + rms_eps) * w, one weight vector per
- *    block and layer, shared by both flows; the residuals add the un-normed x
- *    and h;
+ *    block and layer (16-byte aligned), shared by both flows; the residuals
+ *    add the un-normed x and h;
  *  - rope: rotary embeddings of both flows' queries and of the primary's key
  *    at position ctx_lens[b] (before the query coupling and the cache
  *    append): dimension pairs of each head, (i, i + head_dim/2) for

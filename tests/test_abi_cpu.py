@@ -320,6 +320,16 @@ def test_stack_validation():
         _lib._check(_lib.lib().dfa_decode_stack(ctypes.byref(dfa.StackDesc(**ok)), arr, None, None, FAKE, FAKE, FAKE,
                                                 FAKE, FAKE, FAKE, FAKE, 1 << 30, None))
     assert _lib.STATUS[e.value.status] == "DFA_ERR_NULL"
+    # norm weights are read in 16-byte pieces: a misaligned one is refused before any launch
+    for lay in arr:
+        for name in ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down", "a", "b", "c"):
+            setattr(lay.w, name, FAKE)
+        lay.norm_attn, lay.norm_mlp, lay.k_cache, lay.v_cache = FAKE, FAKE, FAKE, FAKE
+    arr[1].norm_mlp = FAKE + 4
+    with pytest.raises(dfa.DfaError) as e:
+        _lib._check(_lib.lib().dfa_decode_stack(ctypes.byref(dfa.StackDesc(**ok)), arr, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                                FAKE, FAKE, FAKE, FAKE, 1 << 30, None))
+    assert _lib.STATUS[e.value.status] == "DFA_ERR_ALIGNMENT"
 
 
 def _call_noalloc(d, **ptrs):

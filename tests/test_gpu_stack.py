@@ -26,6 +26,10 @@ SMALL = W.C5.replace(batch=5, hidden=256, num_q_heads=4, num_kv_heads=2, head_di
                      shuffle_blocks=True, capacity=0)
 WIDE = W.C5.replace(batch=8, hidden=1024, num_q_heads=8, num_kv_heads=2, head_dim=128, mlp=2048, ctx=300,
                     block_size=16, shuffle_blocks=True, capacity=0)
+# 12288 MLP rows: the SwiGLU GEMV runs unsplit, its epilogue in the GEMV kernel (smaller MLPs split k and
+# finish in the reduction); 40 sequences: GEMV slices of 32 and 8
+TALL = W.C5.replace(batch=40, hidden=256, num_q_heads=4, num_kv_heads=2, head_dim=64, mlp=12288, ctx=40, block_size=16,
+                    shuffle_blocks=True, capacity=0)
 ROPE = {"none": dfa.DFA_ROPE_NONE, "half": dfa.DFA_ROPE_HALF, "interleaved": dfa.DFA_ROPE_INTERLEAVED}
 
 
@@ -90,11 +94,13 @@ def oracle(sc):
 
 
 CASES = [("half", True, SMALL, 3), ("interleaved", True, SMALL, 3), ("half", False, SMALL, 2),
-         ("none", True, SMALL, 2), ("half", True, WIDE, 2), ("interleaved", False, WIDE, 2)]
+         ("none", True, SMALL, 2), ("half", True, WIDE, 2), ("interleaved", False, WIDE, 2),
+         ("half", True, TALL, 2)]
 
 
 @pytest.mark.parametrize("rope,rms,layer,layers", CASES,
-                         ids=[f"{r}-{'rms' if n else 'plain'}-d{c.head_dim}-L{l}" for r, n, c, l in CASES])
+                         ids=[f"{r}-{'rms' if n else 'plain'}-d{c.head_dim}-b{c.batch}-m{c.mlp}-L{l}"
+                              for r, n, c, l in CASES])
 def test_stack_matches_oracle(rope, rms, layer, layers):
     sc = W.make_stack_case(W.StackConfig("t", layer, layers=layers, rope=rope, rms=rms), 71)
     say(f"case stack rope {rope} rms {rms} layers {layers} head_dim {layer.head_dim}")

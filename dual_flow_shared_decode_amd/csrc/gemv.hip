@@ -29,15 +29,16 @@
 // range, so one launch can cover stacked matrices (the layer's [Wq; Wk; Wv]).
 // The k-range is streamed in 128-column stages. The math waves keep three
 // stages of weights in flight in registers (two for paired 128-row tiles)
-// and only wait for their own loads; the loader waves keep three stages of
-// raw activations in flight and, per stage, convert the next stage's
-// activations to hi/lo bf16 in LDS (double-buffered; per column block, row
-// r's 8-column groups are stored in slot group ^ r so that both the
-// conversion's writes and the MFMA operand reads are free of bank
-// conflicts). One barrier per stage hands the buffers over. Loads complete in
-// issue order within a wave, so a wave that fetched both would wait for its
-// weights before it could convert activations; split this way the GEMVs of
-// the layer shapes run 4-8% faster. With one k-range the epilogue runs
+// and only wait for their own loads; the loader waves keep two stages of raw
+// activations in flight and, per stage, convert the next stage's activations
+// to hi/lo bf16 in LDS (double-buffered; per column block, row r's 8-column
+// groups are stored in slot group ^ r so that both the conversion's writes
+// and the MFMA operand reads are free of bank conflicts), at raised wave
+// priority since the conversion gates the stage. One barrier per stage hands
+// the buffers over. Loads complete in issue order within a wave, so a wave
+// that fetched both would wait for its weights before it could convert
+// activations; split this way the GEMVs of the layer shapes run 8-12%
+// faster. With one k-range the epilogue runs
 // in the same kernel; otherwise partial sums go to the workspace
 // [k-split][matrix][row][n] and gemv_finalize adds them in a fixed order and
 // applies the epilogue (so the primary flow's results never depend on the

@@ -142,6 +142,23 @@ def layer_bytes(cfg):
     return w + kv_read + kv_write + act
 
 
+def copy_calibration(args, rec):
+    """For counter runs (--copy-calibration MIB): one plain device copy of that size after the timed
+    work, so that the counters' readings of a known byte count give their scale."""
+    if not args.copy_calibration:
+        return
+    import torch
+
+    n = args.copy_calibration << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    rec["copy_calibration_bytes"] = n
+    del src, dst
+
+
 def bench_layer(args):
     """One dfa_decode_layer step of the full-layer workload (batch 32, hidden 4096, 32/8 heads of 128,
     SwiGLU MLP 14336, 4096 cached positions)."""
@@ -194,15 +211,17 @@ def bench_layer(args):
     nbytes = layer_bytes(cfg)
     gbps = nbytes / (ms * 1e-3) / 1e9
     log(f"layer step {ms * 1e3:.1f} us, {nbytes / 1e6:.0f} MB -> {gbps:.0f} GB/s")
-    print(json.dumps({"metric": "dual-flow decode layer step: tokens/s (both flows) + achieved HBM GB/s vs peak",
-                      "value": 2 * cfg.batch / (ms * 1e-3), "unit": "tokens/s (both flows)", "n_gpus": 1,
-                      "steps": args.steps, "warmup": warmup, "ms_per_step": ms, "higher_is_better": True,
-                      "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-                      "config": {"workload": "c5: one dual-flow decode layer step, batch 32, hidden 4096, 32/8 heads "
-                                             "of 128, SwiGLU MLP 14336, 4096 cached positions",
-                                 "batch": cfg.batch},
-                      "achieved_gbps": gbps, "hbm_peak_gbps": HBM_PEAK_GBPS, "frac_of_peak": gbps / HBM_PEAK_GBPS,
-                      "algorithmic_bytes_per_step": nbytes}), flush=True)
+    rec = {"metric": "dual-flow decode layer step: tokens/s (both flows) + achieved HBM GB/s vs peak",
+           "value": 2 * cfg.batch / (ms * 1e-3), "unit": "tokens/s (both flows)", "n_gpus": 1,
+           "steps": args.steps, "warmup": warmup, "ms_per_step": ms, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "c5: one dual-flow decode layer step, batch 32, hidden 4096, 32/8 heads "
+                                  "of 128, SwiGLU MLP 14336, 4096 cached positions",
+                      "batch": cfg.batch},
+           "achieved_gbps": gbps, "hbm_peak_gbps": HBM_PEAK_GBPS, "frac_of_peak": gbps / HBM_PEAK_GBPS,
+           "algorithmic_bytes_per_step": nbytes}
+    copy_calibration(args, rec)
+    print(json.dumps(rec), flush=True)
 
 
 GEMV_SHAPES = (  # the dense layer's weight streams at hidden 4096, 32/8 heads of 128, SwiGLU 14336
@@ -290,14 +309,7 @@ def bench_gemv(args):
                                   "SwiGLU pair 2 x 14336 x 4096, down 4096 x 14336", "batch": batch,
                       "num_flows": flows},
            "frac_of_peak": gbps / HBM_PEAK_GBPS, "shapes": shapes}
-    if args.copy_calibration:
-        n = args.copy_calibration << 20
-        src = torch.ones(n, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        rec["copy_calibration_bytes"] = n
+    copy_calibration(args, rec)
     print(json.dumps(rec), flush=True)
 
 
@@ -836,15 +848,7 @@ def main():
     if t2 and t1:
         rec["traffic_two_flows_over_one_flow"] = t2 / t1
 
-    if args.copy_calibration:
-        n = args.copy_calibration << 20
-        src = torch.ones(n, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        rec["copy_calibration_bytes"] = n
-        del src, dst
+    copy_calibration(args, rec)
     if not args.no_extras:
         if "ms_one_flow" in m:
             rec["ms_per_step_one_flow"] = m["ms_one_flow"]
